@@ -1,0 +1,157 @@
+"""CPU oracle for the MXFP4 MoE expert layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP
+library: ``oracle.c`` is compiled by gcc on its own and loaded with ctypes,
+and ``brute.py`` is an independent numpy re-statement used to cross-check it.
+
+Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
+  e2m1/e4m3/e8m0 decode ....... pinned (code tables, torch float8_e4m3fn)
+  quantize_mxfp4/mxfp8 ........ pinned (round trip, midpoints, saturation,
+                                  brute-force nearest search, torch RNE)
+  route ....................... pinned (brute-force sort, softmax identity)
+  forward ..................... pinned (closed forms, scale identities,
+                                  brute.py on tiny shapes)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Mapping, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (plain IEEE fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                        "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [i32]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [i32]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [i32]
+        L.oracle_quantize_mxfp4.restype = i32
+        L.oracle_quantize_mxfp4.argtypes = [vp, i64, i64, vp, vp]
+        L.oracle_quantize_mxfp8.restype = i32
+        L.oracle_quantize_mxfp8.argtypes = [vp, i64, i64, vp, vp]
+        L.oracle_route.restype = i32
+        L.oracle_route.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_forward.restype = i32
+        L.oracle_forward.argtypes = [vp, vp, i64, i64, i64, i64, i32,
+                                     vp, vp, vp, vp, i32, vp, i64, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e8m0_value(code: int) -> float:
+    return lib().oracle_e8m0_value(int(code))
+
+
+def quantize_mxfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """float32 [rows, cols] -> (packed uint8 [rows, cols/2], scales uint8 [rows, cols/32])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    packed = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    rc = lib().oracle_quantize_mxfp4(_p(w), rows, cols, _p(packed), _p(scales))
+    if rc:
+        raise ValueError(f"oracle_quantize_mxfp4 failed ({rc})")
+    return packed, scales
+
+
+def quantize_mxfp8(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """fp64 [rows, cols] -> (E4M3 codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    rows, cols = v.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    rc = lib().oracle_quantize_mxfp8(_p(v), rows, cols, _p(codes), _p(scales))
+    if rc:
+        raise ValueError(f"oracle_quantize_mxfp8 failed ({rc})")
+    return codes, scales
+
+
+def route(logits: np.ndarray, k: int) -> dict:
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sorted_ = np.empty(T * k, np.int32)
+    pos = np.empty(T * k, np.int32)
+    rc = lib().oracle_route(_p(logits), T, E, k, _p(ids), _p(w), _p(counts), _p(offsets),
+                            _p(sorted_), _p(pos))
+    if rc:
+        raise ValueError(f"oracle_route failed ({rc})")
+    return {"ids": ids, "w": w, "counts": counts, "offsets": offsets,
+            "sorted": sorted_, "pos": pos}
+
+
+def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
+            experts: Mapping[int, Sequence[np.ndarray]], tokens: Sequence[int] | None = None,
+            act_mxfp8: bool = False) -> np.ndarray:
+    """Layer output (fp64) for ``tokens`` (default: all).
+
+    ``experts[e] = (gu_packed [2I,H/2], gu_scales [2I,H/32], dn_packed [H,I/2],
+    dn_scales [H,I/32])`` for every expert the listed tokens are routed to.
+    """
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    assert x_bf16.shape == (T, H)
+    toks = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    ptr_t = ctypes.c_void_p * E
+    keep = []
+    arrays = [ptr_t(), ptr_t(), ptr_t(), ptr_t()]
+    for e, mats in experts.items():
+        for i, m in enumerate(mats):
+            m = np.ascontiguousarray(m, dtype=np.uint8)
+            keep.append(m)
+            arrays[i][e] = m.ctypes.data
+    out = np.zeros((len(toks), H), np.float64)
+    rc = lib().oracle_forward(_p(x_bf16), _p(logits), T, E, H, I, k,
+                              ctypes.addressof(arrays[0]), ctypes.addressof(arrays[1]),
+                              ctypes.addressof(arrays[2]), ctypes.addressof(arrays[3]),
+                              1 if act_mxfp8 else 0, _p(toks), len(toks), _p(out))
+    if rc == -2:
+        raise KeyError("oracle_forward: a routed expert's weights were not given")
+    if rc:
+        raise ValueError(f"oracle_forward failed ({rc})")
+    return out
