@@ -1,0 +1,158 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 MoE expert layer.
+ *
+ * The operation (bjdmk.com.cn news page, section on the road to 1000
+ * tokens/s; tilert.ai blog, section on the second leap; HyperAI transcript,
+ * section on real-world case studies): the MoE expert layer of a
+ * trillion-parameter model whose expert weights, and only those, are stored
+ * as MXFP4 (4-bit E2M1 elements, one E8M0 power-of-two scale per 32
+ * consecutive elements along the reduction dimension), run at the token
+ * counts of a speculative-decode verify step (8 draft tokens + 1) or of a
+ * prefill chunk.  Each token is routed to its top_k experts; each expert
+ * computes SiLU(gate) * up and then the down projection; the expert outputs
+ * are summed with the routing weights:
+ *
+ *   ids[t,:]  = the top_k experts by router logit (ties -> lower index),
+ *               ordered by (logit desc, index asc)
+ *   w[t,j]    = exp(l[t,ids[t,j]] - l[t,ids[t,0]]) / sum_i exp(l[t,ids[t,i]] - l[t,ids[t,0]])
+ *   h         = SiLU(Wg[e] x_t) * (Wu[e] x_t),    SiLU(g) = g / (1 + exp(-g))
+ *   out[t,:]  = sum_j w[t,j] * Wd[e_j] h_j
+ *
+ * The pages give no router or FFN formula; this is the standard softmax
+ * top-k MoE with a SiLU-gated FFN, the plainest reading of "experts" they
+ * describe.  Accumulation is fp32; the intermediate h is bf16 (bf16
+ * activations) or MXFP8 (prefill); out is bf16 rounded to nearest even.
+ *
+ * Data layout (all row-major, contiguous, caller-owned device memory):
+ *   x              [T, H]        bf16 bit patterns
+ *   router_logits  [T, E]        fp32 (any router bias already added)
+ *   W_gate_up      [E, 2I, H/2]  uint8: two E2M1 codes per byte, element k of
+ *                                a row in byte k/2, even k in the LOW nibble;
+ *                                rows 0..I-1 are gate, rows I..2I-1 are up
+ *   W_down         [E, H, I/2]   uint8, same packing
+ *   scales->gate_up [E, 2I, H/32] uint8 E8M0 (value 2^(u-127), 0xFF = NaN)
+ *   scales->down    [E, H, I/32]  uint8 E8M0
+ *   out            [T, H]        bf16, fully overwritten
+ * Every device pointer must be 16-byte aligned.  H and I must be multiples
+ * of 128.
+ *
+ * Ownership: the caller owns every tensor and keeps it alive until the work
+ * enqueued on `stream` has completed.  The library keeps no caller pointer.
+ * It owns one workspace per device (routing arrays, h, per-assignment
+ * outputs, queue counters), allocated by moe_mxfp4_init; the forward calls
+ * never allocate.
+ *
+ * Errors: arguments are validated synchronously before anything is
+ * enqueued; a failed check returns a negative status, enqueues nothing and
+ * leaves `out` untouched.  num_tokens == 0 is a valid no-op.  A failed HIP
+ * call returns MOE_E_HIP; moe_mxfp4_status_string then also reports the
+ * HIP error text.  Nothing aborts and no C++ exception crosses this ABI.
+ * NaN inputs propagate and are not checked.
+ *
+ * Concurrency: one workspace per device, shared by every call on that
+ * device; calls whose work overlaps on one device (e.g. on two streams)
+ * race.  Calls on different devices are independent.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_E_NULL (-1)      /* a required pointer is NULL */
+#define MOE_E_SHAPE (-2)     /* a size is out of range or not a multiple it must be */
+#define MOE_E_ALIGN (-3)     /* a device pointer is not 16-byte aligned */
+#define MOE_E_TOPK (-4)      /* top_k outside 1..min(E, max_top_k) */
+#define MOE_E_TOKENS (-5)    /* num_tokens above the max_tokens given to init */
+#define MOE_E_NOT_INIT (-6)  /* moe_mxfp4_init was not called for the current device */
+#define MOE_E_HIP (-7)       /* a HIP runtime call or kernel launch failed */
+#define MOE_E_OPTION (-8)    /* an option value is not recognised */
+
+/* activation formats fed to the expert GEMMs */
+#define MOE_ACT_BF16 0       /* x and h in bf16 (verify token counts) */
+#define MOE_ACT_MXFP8 1      /* x and h encoded to MXFP8 E4M3 + E8M0 per 32 (prefill) */
+
+/* GEMM path selection (moe_mxfp4_options.gemm_path) */
+#define MOE_PATH_AUTO 0      /* per expert: GEMV for few tokens, MFMA for many */
+#define MOE_PATH_GEMV 1      /* force the VALU GEMV path for every expert */
+#define MOE_PATH_MFMA 2      /* force the bf16-MFMA path for every expert */
+
+/* The two E8M0 scale tensors (device pointers). */
+typedef struct moe_mxfp4_scales {
+    const uint8_t* gate_up; /* [E, 2I, H/32] */
+    const uint8_t* down;    /* [E, H, I/32]  */
+} moe_mxfp4_scales;
+
+/* Options of moe_mxfp4_forward_ex.  Zero-initialised = moe_mxfp4_forward.
+ * The optional outputs are device buffers the call fills (NULL to skip):
+ * the routing result and, with MOE_ACT_MXFP8, the MXFP8 encoding of x. */
+typedef struct moe_mxfp4_options {
+    int32_t act_format;  /* MOE_ACT_BF16 or MOE_ACT_MXFP8 */
+    int32_t gemm_path;   /* MOE_PATH_* */
+    int32_t* ids;        /* [T, top_k] expert per slot, slot order (logit desc, index asc) */
+    float* weights;      /* [T, top_k] renormalised softmax weights */
+    int32_t* counts;     /* [E] slots per expert */
+    int32_t* offsets;    /* [E+1] exclusive prefix sum of counts */
+    int32_t* sorted;     /* [T*top_k] slots t*top_k+j grouped by expert, ascending inside one */
+    uint8_t* x_codes;    /* [T, H] E4M3 codes of x (MOE_ACT_MXFP8 only) */
+    uint8_t* x_scales;   /* [T, H/32] E8M0 scales of x (MOE_ACT_MXFP8 only) */
+    /* Optional hipEvent_t handles recorded on `stream` at the stage
+     * boundaries: [0] before routing, [1] after routing, [2] after the
+     * gate_up GEMM, [3] after the down GEMM, [4] after the combine.  Only
+     * the first num_events (<= 5) are recorded; used to time the kernels. */
+    void* const* events;
+    int32_t num_events;
+} moe_mxfp4_options;
+
+/* Allocate the workspace on the current device for layers with at most
+ * max_tokens tokens, exactly num_experts experts of hidden size `hidden`
+ * and intermediate size `inter`, and top_k <= max_top_k.  Calling it again
+ * on the same device replaces the previous workspace.  Sizes: max_tokens in
+ * 1..2^20, num_experts in 1..1024, hidden and inter multiples of 128 in
+ * 128..16384, max_top_k in 1..min(32, num_experts).
+ * Returns MOE_OK, MOE_E_SHAPE, MOE_E_TOPK or MOE_E_HIP (allocation failed). */
+int moe_mxfp4_init(int64_t max_tokens, int64_t num_experts, int64_t hidden,
+                   int64_t inter, int32_t max_top_k);
+
+/* Release the workspaces of every device (after synchronising them). */
+void moe_mxfp4_finalize(void);
+
+/* The layer with bf16 activations, enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream).  x, router_logits and out hold num_tokens rows.
+ * Returns without synchronising. */
+int moe_mxfp4_forward(const void* x, const float* router_logits, int64_t num_tokens,
+                      int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
+                      const moe_mxfp4_scales* scales, void* out, void* stream);
+
+/* moe_mxfp4_forward with options (activation format, path, debug outputs).
+ * opt == NULL is the same as moe_mxfp4_forward. */
+int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_tokens,
+                         int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
+                         const moe_mxfp4_scales* scales, void* out, void* stream,
+                         const moe_mxfp4_options* opt);
+
+/* Encode a float32 matrix w [rows, cols] to MXFP4 along cols (the block
+ * rule of the weights: scale 2^(floor(log2 amax) - 2) with the exponent
+ * clamped to [-127, 127], amax == 0 -> scale code 0, elements rounded to the
+ * nearest E2M1 value with ties to the even code and saturating at 6; a block
+ * with a non-finite element gets scale 0xFF and element codes 0).
+ * packed [rows, cols/2], scales [rows, cols/32], all on the current device,
+ * enqueued on `stream`.  cols must be a multiple of 32, w 16-byte aligned,
+ * and packed 16-byte aligned when cols is a multiple of 32 (always). */
+int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                       uint8_t* scales, void* stream);
+
+/* Static text of a status code; for MOE_E_HIP, the text of the last HIP
+ * error seen by the calling thread. */
+const char* moe_mxfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,197 @@
+"""ctypes binding of libmoe_mxfp4.so, with the C ABI's own names.
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch device tensors (torch provides memory and streams); each
+is checked for dtype, shape and contiguity here so that the pointer handed
+to the library means what include/moe_mxfp4.h says it means.  There is no
+fallback: if the library is not built this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mxfp4.so")
+
+MOE_OK = 0
+MOE_E_NULL = -1
+MOE_E_SHAPE = -2
+MOE_E_ALIGN = -3
+MOE_E_TOPK = -4
+MOE_E_TOKENS = -5
+MOE_E_NOT_INIT = -6
+MOE_E_HIP = -7
+MOE_E_OPTION = -8
+
+MOE_ACT_BF16 = 0
+MOE_ACT_MXFP8 = 1
+MOE_PATH_AUTO = 0
+MOE_PATH_GEMV = 1
+MOE_PATH_MFMA = 2
+
+EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
+            "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {moe_mxfp4_status_string(status)}")
+
+
+class moe_mxfp4_scales(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
+
+
+class moe_mxfp4_options(ctypes.Structure):
+    _fields_ = [("act_format", ctypes.c_int32), ("gemm_path", ctypes.c_int32),
+                ("ids", ctypes.c_void_p), ("weights", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("sorted", ctypes.c_void_p), ("x_codes", ctypes.c_void_p),
+                ("x_scales", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("num_events", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m mxfp4_moe_expert_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        L.moe_mxfp4_init.restype = ctypes.c_int
+        L.moe_mxfp4_init.argtypes = [i64, i64, i64, i64, i32]
+        L.moe_mxfp4_finalize.restype = None
+        L.moe_mxfp4_finalize.argtypes = []
+        fwd = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(moe_mxfp4_scales), vp, vp]
+        L.moe_mxfp4_forward.restype = ctypes.c_int
+        L.moe_mxfp4_forward.argtypes = fwd
+        L.moe_mxfp4_forward_ex.restype = ctypes.c_int
+        L.moe_mxfp4_forward_ex.argtypes = fwd + [ctypes.POINTER(moe_mxfp4_options)]
+        L.moe_mxfp4_quantize.restype = ctypes.c_int
+        L.moe_mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.moe_mxfp4_status_string.restype = ctypes.c_char_p
+        L.moe_mxfp4_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def moe_mxfp4_status_string(status: int) -> str:
+    return lib().moe_mxfp4_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+    return rc
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def moe_mxfp4_init(max_tokens: int, num_experts: int, hidden: int, inter: int,
+                   max_top_k: int, check: bool = True) -> int:
+    rc = lib().moe_mxfp4_init(max_tokens, num_experts, hidden, inter, max_top_k)
+    return _check(rc, "moe_mxfp4_init") if check else rc
+
+
+def moe_mxfp4_finalize() -> None:
+    lib().moe_mxfp4_finalize()
+
+
+def _expect(t, dtype, shape, name):
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales, out,
+                         stream=None, act_format: int = MOE_ACT_BF16,
+                         gemm_path: int = MOE_PATH_AUTO, ids=None, weights=None,
+                         counts=None, offsets=None, sorted=None, x_codes=None,
+                         x_scales=None, events=None, check: bool = True,
+                         validate: bool = True) -> int:
+    """Enqueue one layer on ``stream`` (default: torch's current stream).
+
+    x [T,H] bfloat16, router_logits [T,E] float32, W_gate_up [E,2I,H/2] uint8,
+    W_down [E,H,I/2] uint8, scales = (gate_up [E,2I,H/32], down [E,H,I/32])
+    uint8, out [T,H] bfloat16.  ``validate=False`` skips the Python-side
+    shape checks so the library's own validation can be exercised.
+    ``events``: up to 5 torch.cuda.Event (timing enabled) recorded by the
+    library at its stage boundaries.
+    """
+    import torch
+    if validate:
+        T, H = x.shape
+        E = router_logits.shape[1]
+        I2 = W_gate_up.shape[1]
+        _expect(x, torch.bfloat16, (T, H), "x")
+        _expect(router_logits, torch.float32, (T, E), "router_logits")
+        _expect(W_gate_up, torch.uint8, (E, I2, H // 2), "W_gate_up")
+        _expect(W_down, torch.uint8, (E, H, I2 // 4), "W_down")
+        _expect(scales[0], torch.uint8, (E, I2, H // 32), "scales[0]")
+        _expect(scales[1], torch.uint8, (E, H, I2 // 64), "scales[1]")
+        _expect(out, torch.bfloat16, (T, H), "out")
+    sc = moe_mxfp4_scales(_ptr(scales[0]), _ptr(scales[1])) if scales is not None else None
+    ev_arr, n_ev = None, 0
+    if events:
+        handles = []
+        for e in events:
+            if not e.cuda_event:  # torch creates the event lazily at its first record
+                e.record()
+            handles.append(e.cuda_event)
+        n_ev = len(handles)
+        ev_arr = (ctypes.c_void_p * n_ev)(*handles)
+    opt = moe_mxfp4_options(act_format, gemm_path, _ptr(ids), _ptr(weights), _ptr(counts),
+                            _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
+                            ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
+                            n_ev)
+    T = x.shape[0] if x is not None else 0
+    rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
+                                    _ptr(W_down), ctypes.byref(sc) if sc is not None else None,
+                                    _ptr(out), _stream(stream), ctypes.byref(opt))
+    return _check(rc, "moe_mxfp4_forward_ex") if check else rc
+
+
+def moe_mxfp4_forward(x, router_logits, top_k: int, W_gate_up, W_down, scales, out,
+                      stream=None, check: bool = True) -> int:
+    """The layer with bf16 activations (see moe_mxfp4_forward_ex for shapes)."""
+    import torch
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I2 = W_gate_up.shape[1]
+    _expect(x, torch.bfloat16, (T, H), "x")
+    _expect(router_logits, torch.float32, (T, E), "router_logits")
+    _expect(out, torch.bfloat16, (T, H), "out")
+    sc = moe_mxfp4_scales(_ptr(scales[0]), _ptr(scales[1]))
+    rc = lib().moe_mxfp4_forward(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
+                                 _ptr(W_down), ctypes.byref(sc), _ptr(out), _stream(stream))
+    return _check(rc, "moe_mxfp4_forward") if check else rc
+
+
+def moe_mxfp4_quantize(w, packed, scales, stream=None, check: bool = True) -> int:
+    """Encode float32 w [rows, cols] to MXFP4 into packed [rows, cols/2] and
+    scales [rows, cols/32] (uint8 device tensors)."""
+    import torch
+    rows, cols = w.shape
+    _expect(w, torch.float32, (rows, cols), "w")
+    _expect(packed, torch.uint8, (rows, cols // 2), "packed")
+    _expect(scales, torch.uint8, (rows, cols // 32), "scales")
+    rc = lib().moe_mxfp4_quantize(_ptr(w), rows, cols, _ptr(packed), _ptr(scales), _stream(stream))
+    return _check(rc, "moe_mxfp4_quantize") if check else rc

@@ -1,0 +1,261 @@
+// moe_abi.hip -- the C ABI (include/moe_mxfp4.h): validation, the per-device
+// workspace, and the launch sequence of one MoE expert layer.
+//
+// Launch sequence of a forward on `stream` (no host synchronisation):
+//   route (top-k + stable sort by expert + active-expert lists)
+//   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine.
+// Every expert that received no token is absent from the active lists and
+// costs no weight bytes: the layer reads only the experts its tokens use,
+// the property the pages build the 4-bit expert format around (bjdmk.com.cn
+// news page, co-design section).
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/moe_mxfp4.h"
+#include "moe_internal.h"
+
+namespace {
+
+using moe::Workspace;
+
+constexpr int kMaxDevices = 64;
+Workspace* g_ws[kMaxDevices] = {};
+int g_num_ws = 0;  // number of live workspaces (0: nothing initialised)
+std::mutex g_mu;
+thread_local char g_hip_msg[256] = "";
+
+int hip_fail(hipError_t err, const char* what) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s (%d)", what, hipGetErrorString(err), (int)err);
+    return MOE_E_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Lay the workspace out in one allocation (256-byte aligned sub-buffers).
+size_t layout(Workspace* ws, char* base) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off = round_up(off + bytes, 256);
+        return p;
+    };
+    const size_t S = (size_t)ws->max_tokens * ws->kmax;
+    ws->ids = (int32_t*)take(S * 4);
+    ws->wts = (float*)take(S * 4);
+    ws->counts = (int32_t*)take(ws->E * 4);
+    ws->offsets = (int32_t*)take((ws->E + 1) * 4);
+    ws->sorted = (int32_t*)take(S * 4);
+    ws->pos = (int32_t*)take(S * 4);
+    ws->gemv_list = (int32_t*)take(ws->E * 4);
+    ws->mfma_list = (int32_t*)take(ws->E * 4);
+    ws->meta = (int32_t*)take(moe::kMetaWords * 4);
+    ws->h = (uint16_t*)take(S * ws->I * 2);
+    ws->y = (float*)take(S * ws->H * 4);
+    return off;
+}
+
+void free_ws(Workspace* ws) {
+    if (!ws) return;
+    if (ws->base) {
+        int cur = 0;
+        hipGetDevice(&cur);
+        hipSetDevice(ws->device);
+        hipDeviceSynchronize();
+        hipFree(ws->base);
+        hipSetDevice(cur);
+    }
+    delete ws;
+}
+
+// Workspace of the current device, or null (without any HIP call when no
+// device has been initialised).
+Workspace* current_ws() {
+    if (g_num_ws == 0) return nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    return g_ws[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mxfp4_init(int64_t max_tokens, int64_t num_experts, int64_t hidden, int64_t inter,
+                   int32_t max_top_k) {
+    if (max_tokens < 1 || max_tokens > (1 << 20)) return MOE_E_SHAPE;
+    if (num_experts < 1 || num_experts > moe::kMaxExperts) return MOE_E_SHAPE;
+    if (hidden < 128 || hidden > 16384 || hidden % 128) return MOE_E_SHAPE;
+    if (inter < 128 || inter > 16384 || inter % 128) return MOE_E_SHAPE;
+    if (max_top_k < 1 || max_top_k > moe::kMaxTopK || max_top_k > num_experts) return MOE_E_TOPK;
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice, "device index");
+    Workspace* ws = new Workspace();
+    ws->device = dev;
+    ws->max_tokens = max_tokens;
+    ws->E = num_experts;
+    ws->H = hidden;
+    ws->I = inter;
+    ws->kmax = max_top_k;
+    ws->bytes = layout(ws, nullptr);
+    err = hipMalloc(&ws->base, ws->bytes);
+    if (err != hipSuccess) {
+        ws->base = nullptr;
+        delete ws;
+        return hip_fail(err, "hipMalloc(workspace)");
+    }
+    layout(ws, (char*)ws->base);
+    err = hipMemset(ws->base, 0, ws->bytes);
+    if (err != hipSuccess) {
+        free_ws(ws);
+        return hip_fail(err, "hipMemset(workspace)");
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_ws[dev]) {
+        free_ws(g_ws[dev]);
+        g_num_ws--;
+    }
+    g_ws[dev] = ws;
+    g_num_ws++;
+    return MOE_OK;
+}
+
+void moe_mxfp4_finalize(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (int d = 0; d < kMaxDevices; d++) {
+        if (g_ws[d]) {
+            free_ws(g_ws[d]);
+            g_ws[d] = nullptr;
+        }
+    }
+    g_num_ws = 0;
+}
+
+int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_tokens,
+                         int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
+                         const moe_mxfp4_scales* scales, void* out, void* stream,
+                         const moe_mxfp4_options* opt) {
+    moe_mxfp4_options o;
+    memset(&o, 0, sizeof(o));
+    if (opt) o = *opt;
+    // context-free checks first
+    if (num_tokens < 0) return MOE_E_SHAPE;
+    if (o.act_format != MOE_ACT_BF16) return MOE_E_OPTION;  // MXFP8 path not built yet
+    if (o.gemm_path != MOE_PATH_AUTO && o.gemm_path != MOE_PATH_GEMV) return MOE_E_OPTION;
+    if (o.num_events < 0 || o.num_events > 5 || (o.num_events > 0 && !o.events))
+        return MOE_E_OPTION;
+    if (num_tokens == 0) return MOE_OK;
+    if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
+    if (!scales->gate_up || !scales->down) return MOE_E_NULL;
+    if (top_k < 1) return MOE_E_TOPK;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(W_gate_up) ||
+        !aligned16(W_down) || !aligned16(scales->gate_up) || !aligned16(scales->down) ||
+        !aligned16(out))
+        return MOE_E_ALIGN;
+    Workspace* ws = current_ws();
+    if (!ws) return MOE_E_NOT_INIT;
+    if (num_tokens > ws->max_tokens) return MOE_E_TOKENS;
+    if (top_k > ws->kmax || top_k > ws->E) return MOE_E_TOPK;
+
+    hipStream_t st = (hipStream_t)stream;
+    auto mark = [&](int i) -> hipError_t {
+        if (i < o.num_events && o.events[i]) return hipEventRecord((hipEvent_t)o.events[i], st);
+        return hipSuccess;
+    };
+    const int T = (int)num_tokens, k = top_k;
+    const int E = (int)ws->E, H = (int)ws->H, I = (int)ws->I;
+    const int S = T * k;
+    const int max_active = S < E ? S : E;
+    hipError_t err;
+
+    if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30,
+                            o.gemm_path == MOE_PATH_AUTO ? 1 : o.gemm_path, st);
+    if (err != hipSuccess) return hip_fail(err, "route");
+    if ((err = mark(1)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+
+    moe::GemmArgs a;
+    a.x = (const uint16_t*)x;
+    a.wgu = W_gate_up;
+    a.sgu = scales->gate_up;
+    a.wdn = W_down;
+    a.sdn = scales->down;
+    a.counts = ws->counts;
+    a.offsets = ws->offsets;
+    a.sorted = ws->sorted;
+    a.list = ws->gemv_list;
+    a.meta = ws->meta;
+    a.list_meta = moe::kMetaNumGemv;
+    a.h = ws->h;
+    a.y = ws->y;
+    a.T = T;
+    a.H = H;
+    a.I = I;
+    a.k = k;
+    err = moe::launch_gemv_gate_up(a, max_active, st);
+    if (err != hipSuccess) return hip_fail(err, "gate_up");
+    if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = moe::launch_gemv_down(a, max_active, st);
+    if (err != hipSuccess) return hip_fail(err, "down");
+    if ((err = mark(3)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = moe::launch_combine(ws->y, ws->wts, ws->pos, T, H, k, (uint16_t*)out, st);
+    if (err != hipSuccess) return hip_fail(err, "combine");
+    if ((err = mark(4)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+
+    // optional copies of the routing result
+    struct {
+        void* dst;
+        const void* src;
+        size_t bytes;
+    } copies[] = {
+        {o.ids, ws->ids, (size_t)S * 4},         {o.weights, ws->wts, (size_t)S * 4},
+        {o.counts, ws->counts, (size_t)E * 4},   {o.offsets, ws->offsets, (size_t)(E + 1) * 4},
+        {o.sorted, ws->sorted, (size_t)S * 4},
+    };
+    for (auto& c : copies) {
+        if (!c.dst) continue;
+        err = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, st);
+        if (err != hipSuccess) return hip_fail(err, "hipMemcpyAsync(debug output)");
+    }
+    return MOE_OK;
+}
+
+int moe_mxfp4_forward(const void* x, const float* router_logits, int64_t num_tokens,
+                      int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
+                      const moe_mxfp4_scales* scales, void* out, void* stream) {
+    return moe_mxfp4_forward_ex(x, router_logits, num_tokens, top_k, W_gate_up, W_down, scales,
+                                out, stream, nullptr);
+}
+
+int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                       uint8_t* scales, void* stream) {
+    if (rows < 0 || cols < 0 || cols % 32) return MOE_E_SHAPE;
+    if (rows == 0 || cols == 0) return MOE_OK;
+    if (!w || !packed || !scales) return MOE_E_NULL;
+    if (!aligned16(w) || !aligned16(packed)) return MOE_E_ALIGN;
+    hipError_t err = moe::launch_quantize_mxfp4(w, rows, cols, packed, scales, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "quantize");
+    return MOE_OK;
+}
+
+const char* moe_mxfp4_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_E_NULL: return "a required pointer is NULL";
+        case MOE_E_SHAPE: return "a size is out of range or not a required multiple";
+        case MOE_E_ALIGN: return "a device pointer is not 16-byte aligned";
+        case MOE_E_TOPK: return "top_k out of range";
+        case MOE_E_TOKENS: return "num_tokens exceeds max_tokens of moe_mxfp4_init";
+        case MOE_E_NOT_INIT: return "moe_mxfp4_init was not called for the current device";
+        case MOE_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+        case MOE_E_OPTION: return "an option value is not recognised";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// moe_internal.h -- internal declarations shared by the library's HIP sources.
+// Not installed and not part of the C ABI (include/moe_mxfp4.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- tuning
+constexpr int kWave = 64;
+constexpr int kGemvThreads = 256;       // 4 waves
+constexpr int kGemvLanesPerRow = 16;    // one DPP row of lanes shares a matrix row
+constexpr int kGemvSlots = kGemvThreads / kGemvLanesPerRow;  // row slots per workgroup
+constexpr int kGemvMaxTok = 4;          // tokens held per GEMV pass
+constexpr int kGemvUnroll = 4;          // blocks per lane per loop step
+// row units per work item: a unit is a (gate, up) row pair for gate_up and
+// two adjacent rows for down
+constexpr int kGateUpUnits = 32;
+constexpr int kDownUnits = 64;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+
+// meta[] words in the workspace
+enum Meta : int {
+    kMetaNumGemv = 0,   // active experts on the GEMV path
+    kMetaNumMfma = 1,   // active experts on the MFMA path
+    kMetaWords = 16,
+};
+
+// One device's workspace, owned by the library.
+struct Workspace {
+    int device = -1;
+    int64_t max_tokens = 0, E = 0, H = 0, I = 0;
+    int kmax = 0;
+    void* base = nullptr;       // single allocation holding everything below
+    size_t bytes = 0;
+    int32_t* ids = nullptr;     // [Tmax*kmax]
+    float* wts = nullptr;       // [Tmax*kmax]
+    int32_t* counts = nullptr;  // [E]
+    int32_t* offsets = nullptr; // [E+1]
+    int32_t* sorted = nullptr;  // [Tmax*kmax]
+    int32_t* pos = nullptr;     // [Tmax*kmax]
+    int32_t* gemv_list = nullptr;  // [E] active experts routed to the GEMV path
+    int32_t* mfma_list = nullptr;  // [E] active experts routed to the MFMA path
+    int32_t* meta = nullptr;       // [kMetaWords]
+    uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
+    float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order
+};
+
+// Arguments common to the expert GEMM kernels.
+struct GemmArgs {
+    const uint16_t* x;          // [T, H] bf16
+    const uint8_t* wgu;         // [E, 2I, H/2]
+    const uint8_t* sgu;         // [E, 2I, H/32]
+    const uint8_t* wdn;         // [E, H, I/2]
+    const uint8_t* sdn;         // [E, H, I/32]
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* list;        // active experts for this path
+    const int32_t* meta;
+    int list_meta;              // which meta word holds the list length
+    uint16_t* h;
+    float* y;
+    int T, H, I, k;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch.
+hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
+                        int gemv_max_tokens, int path, hipStream_t stream);
+hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t stream);
+hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream);
+hipError_t launch_combine(const float* y, const float* wts, const int32_t* sorted_pos,
+                          int T, int H, int k, uint16_t* out, hipStream_t stream);
+hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                                 uint8_t* scales, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+* routing (ids, counts, offsets, sorted order) bit-exact; weights within 1e-6
+* MXFP4 encoding of the weights bit-exact
+* layer output: max |out - ref| <= 2e-2 * rms(ref) (bf16 activations and h,
+  fp32 accumulation, bf16 output) -- on every token for the small workloads,
+  on sampled tokens for the full-size ones
+* determinism, unread empty experts, and the ABI's synchronous errors
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_common import bf16_tensor_to_f64, oracle_experts, parity_ratio, say
+from workloads import Config, get_config, make_logits, make_weight_fp32, make_x_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mxfp4_moe_expert_02_amd as M
+    return M
+
+
+_layers = {}
+
+
+def get_layer(cfg: Config, logits=None):
+    from mxfp4_moe_expert_02_amd.layer import build_layer
+    key = (cfg, None if logits is None else logits.tobytes())
+    if key not in _layers:
+        say(f"building layer {cfg.name} seed {cfg.seed}")
+        _layers[key] = build_layer(cfg, logits=logits)
+    return _layers[key]
+
+
+def run(M, layer, path=0, debug=False):
+    import torch
+    c = layer.cfg
+    M.moe_mxfp4_init(c.T, c.E, c.H, c.I, c.k)
+    dbg = {}
+    if debug:
+        S = c.T * c.k
+        dbg = dict(ids=torch.empty((c.T, c.k), dtype=torch.int32, device="cuda"),
+                   weights=torch.empty((c.T, c.k), dtype=torch.float32, device="cuda"),
+                   counts=torch.empty(c.E, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(c.E + 1, dtype=torch.int32, device="cuda"),
+                   sorted=torch.empty(S, dtype=torch.int32, device="cuda"))
+    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path}")
+    M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, layer.wgu, layer.wdn, layer.scales,
+                           layer.out, gemm_path=path, **dbg)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in dbg.items()}
+
+
+def test_loads_in_tree_library(torch_dev, M):
+    import os
+    lib = M.lib()
+    assert os.path.dirname(lib._name) == os.path.dirname(M.__file__)
+
+
+# ---------------------------------------------------------------- encoding
+
+def _gpu_quantize(M, w):
+    import torch
+    wt = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    p = torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty((w.shape[0], w.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    M.moe_mxfp4_quantize(wt, p, s)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), s.cpu().numpy()
+
+
+def test_quantize_edge_blocks_bit_exact(torch_dev, M, oracle_lib):
+    say("quantize edge blocks")
+    rng = np.random.default_rng(0)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0
+    w[0, 32:64] = -0.0
+    w[1, :32] = np.float32(1e-40)            # subnormal amax
+    w[1, 32:64] = np.float32(3.0e38)         # near fp32 max
+    w[2, :32] = np.linspace(-8, 8, 32).astype(np.float32)
+    w[3, :32] = np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4, np.float32)  # ties
+    w[3, 32:64] = -w[3, :32]
+    w[4, :32] = 2.0 ** -5                     # exact power of two
+    w[4, 32:64] = np.nextafter(np.float32(2.0 ** -5), np.float32(0))
+    w[5, :32] = np.float32(2.0 ** -130)       # scale clamps at 2^-127
+    w[6, :32] = np.nan
+    w[6, 40] = np.inf
+    p, s = _gpu_quantize(M, w)
+    po, so = oracle_lib.quantize_mxfp4(w)
+    assert np.array_equal(s, so)
+    assert np.array_equal(p, po)
+
+
+def test_quantize_tiny_workload_bit_exact(torch_dev, M, oracle_lib):
+    cfg = get_config("c1")
+    layer = get_layer(cfg)
+    for e in range(cfg.E):
+        gp, gs = oracle_lib.quantize_mxfp4(make_weight_fp32(cfg, "gate_up", e))
+        dp, ds = oracle_lib.quantize_mxfp4(make_weight_fp32(cfg, "down", e))
+        assert np.array_equal(layer.wgu[e].cpu().numpy(), gp)
+        assert np.array_equal(layer.sgu[e].cpu().numpy(), gs)
+        assert np.array_equal(layer.wdn[e].cpu().numpy(), dp)
+        assert np.array_equal(layer.sdn[e].cpu().numpy(), ds)
+
+
+def test_quantize_verify_workload_sample_bit_exact(torch_dev, M, oracle_lib):
+    cfg = get_config("c2")
+    layer = get_layer(cfg)
+    for e in (0, cfg.E - 1):
+        gp, gs = oracle_lib.quantize_mxfp4(make_weight_fp32(cfg, "gate_up", e))
+        assert np.array_equal(layer.wgu[e].cpu().numpy(), gp)
+        assert np.array_equal(layer.sgu[e].cpu().numpy(), gs)
+        dp, ds = oracle_lib.quantize_mxfp4(make_weight_fp32(cfg, "down", e))
+        assert np.array_equal(layer.wdn[e].cpu().numpy(), dp)
+        assert np.array_equal(layer.sdn[e].cpu().numpy(), ds)
+
+
+# ---------------------------------------------------------------- routing
+
+def _check_route(dbg, ref, k):
+    assert np.array_equal(dbg["ids"], ref["ids"])
+    assert np.array_equal(dbg["counts"], ref["counts"])
+    assert np.array_equal(dbg["offsets"], ref["offsets"])
+    assert np.array_equal(dbg["sorted"], ref["sorted"])
+    assert np.abs(dbg["weights"] - ref["w"]).max() <= 1e-6
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4"])
+def test_route_bit_exact(torch_dev, M, oracle_lib, key):
+    cfg = get_config(key)
+    layer = get_layer(cfg)
+    dbg = run(M, layer, debug=True)
+    _check_route(dbg, oracle_lib.route(make_logits(cfg), cfg.k), cfg.k)
+
+
+def test_route_ties_bit_exact(torch_dev, M, oracle_lib):
+    cfg = Config("ties", "ties_t16_e40_h128_i128_k6", 16, 40, 128, 128, 6, "normal", "bf16", 7)
+    rng = np.random.default_rng(5)
+    logits = rng.integers(-2, 3, size=(cfg.T, cfg.E)).astype(np.float32)  # many exact ties
+    logits[0, :] = 0.0
+    logits[1, ::2] = -0.0
+    logits[2, :] = -np.inf
+    logits[2, 39] = 1.0
+    logits[3, 33:] = 1e30
+    layer = get_layer(cfg, logits=logits)
+    dbg = run(M, layer, debug=True)
+    ref = oracle_lib.route(logits, cfg.k)
+    assert np.array_equal(dbg["ids"], ref["ids"])
+    assert np.array_equal(dbg["sorted"], ref["sorted"])
+    assert np.array_equal(dbg["offsets"], ref["offsets"])
+    fin = np.isfinite(ref["w"])
+    assert np.abs(dbg["weights"][fin] - ref["w"][fin]).max() <= 1e-6
+
+
+# ---------------------------------------------------------------- layer output
+
+def _parity(M, oracle_lib, cfg, layer, tokens, path=0, logits=None):
+    run(M, layer, path=path)
+    lg = make_logits(cfg) if logits is None else logits
+    ids = oracle_lib.route(lg, cfg.k)["ids"]
+    ex = oracle_experts(oracle_lib, cfg, ids[tokens].ravel())
+    ref = oracle_lib.forward(make_x_bf16(cfg), lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens)
+    got = bf16_tensor_to_f64(layer.out)[tokens]
+    ratio = parity_ratio(got, ref)
+    say(f"parity {cfg.name} tokens={list(tokens)} max|d|/rms = {ratio:.3e}")
+    assert np.isfinite(got).all()
+    assert ratio <= TOL
+    return ratio
+
+
+def test_forward_tiny_all_tokens(torch_dev, M, oracle_lib):
+    cfg = get_config("c1")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(cfg.T)))
+
+
+def test_forward_verify_sampled(torch_dev, M, oracle_lib):
+    cfg = get_config("c2")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 4, 8])
+
+
+def test_forward_batched_verify_sampled(torch_dev, M, oracle_lib):
+    cfg = get_config("c3")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71])
+
+
+def test_forward_zipf_verify_sampled(torch_dev, M, oracle_lib):
+    cfg = get_config("c4")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 143, 287])
+
+
+def test_forward_one_hot_expert_many_tokens(torch_dev, M, oracle_lib):
+    """Every token picks expert 3 first: one expert with 13 tokens (several
+    GEMV passes), ragged tail of 1 token."""
+    cfg = Config("hot", "hot_t13_e8_h384_i256_k3", 13, 8, 384, 256, 3, "normal", "bf16", 11)
+    logits = make_logits(cfg)
+    logits[:, 3] += 100.0
+    _parity(M, oracle_lib, cfg, get_layer(cfg, logits=logits), list(range(cfg.T)), logits=logits)
+
+
+@pytest.mark.parametrize("T,k", [(1, 1), (1, 8), (2, 5)])
+def test_forward_small_edges(torch_dev, M, oracle_lib, T, k):
+    cfg = Config("edge", f"edge_t{T}_e8_h256_i128_k{k}", T, 8, 256, 128, k, "normal", "bf16", 21 + T)
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(T)))
+
+
+def test_forward_deterministic(torch_dev, M):
+    cfg = get_config("c2")
+    layer = get_layer(cfg)
+    run(M, layer)
+    a = layer.out.clone()
+    run(M, layer)
+    assert torch_dev.equal(a.view(torch_dev.int16), layer.out.view(torch_dev.int16))
+
+
+def test_untouched_experts_are_not_read(torch_dev, M):
+    """NaN scales (0xFF) on every expert no token chooses: output unchanged."""
+    import torch
+    cfg = Config("pois", "poison_t9_e16_h256_i128_k2", 9, 16, 256, 128, 2, "normal", "bf16", 31)
+    logits = make_logits(cfg)
+    logits[:, 10:] -= 100.0
+    layer = get_layer(cfg, logits=logits)
+    run(M, layer)
+    base = layer.out.clone()
+    sgu, sdn = layer.sgu.clone(), layer.sdn.clone()
+    layer.sgu[10:] = 255
+    layer.sdn[10:] = 255
+    run(M, layer)
+    assert torch.isfinite(layer.out.float()).all()
+    assert torch.equal(base.view(torch.int16), layer.out.view(torch.int16))
+    layer.sgu.copy_(sgu)
+    layer.sdn.copy_(sdn)
+
+
+def test_synchronous_errors_leave_out_untouched(torch_dev, M):
+    import torch
+    cfg = get_config("c1")
+    layer = get_layer(cfg)
+    M.moe_mxfp4_init(cfg.T, cfg.E, cfg.H, cfg.I, cfg.k)
+    layer.out.fill_(1.5)
+    torch.cuda.synchronize()
+    rc = M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.E + 1, layer.wgu, layer.wdn,
+                                layer.scales, layer.out, check=False)
+    assert rc == M.MOE_E_TOPK
+    big = torch.zeros((cfg.T + 1, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.zeros((cfg.T + 1, cfg.E), dtype=torch.float32, device="cuda")
+    rc = M.moe_mxfp4_forward_ex(big, lg, cfg.k, layer.wgu, layer.wdn, layer.scales, big,
+                                check=False)
+    assert rc == M.MOE_E_TOKENS
+    torch.cuda.synchronize()
+    assert (layer.out.float() == 1.5).all()
