@@ -9,8 +9,9 @@ weights ~ N(0,0.02) encoded to MXFP4 on the GPU).
 One step = one full layer (route -> gate_up + SiLU*up -> down -> combine) on
 inputs already resident in HBM.  Prints ONE JSON line:
   value  = touched-expert weight bytes (packed E2M1 + E8M0) / mean layer time, GB/s
-  roofline = the dominant kernel (gate_up) against the 8 TB/s HBM peak, timed
-             live with HIP events recorded by the library between its kernels
+  roofline = the dominant kernel (gate_up: 2/3 of the bytes) against the
+             8 TB/s HBM peak, timed live with HIP events the library records
+             between its kernels
   cpu_baseline = the fp64 CPU oracle on the host cores, same workload
 """
 from __future__ import annotations
@@ -29,7 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "MoE layer µs + achieved HBM GB/s (% peak) at 9-token verify step, 1 GPU"
-STAGES = ["route", "gate_up", "down", "combine"]
+STAGES = ["route", "gate_up", "down_combine"]
 
 
 def parse():
@@ -41,6 +42,9 @@ def parse():
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
+    p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="also run one probe copy of this many bytes (counter calibration)")
     return p.parse_args()
 
 
@@ -51,6 +55,26 @@ def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:
     gu = n * (2 * I * H // 2 + 2 * I * H // 32)
     dn = n * (H * I // 2 + H * I // 32)
     return gu, dn
+
+
+def probe_bandwidth(M, torch, nbytes: int = 4 << 30, reps: int = 20) -> float:
+    """Achievable HBM read bandwidth: a plain 128-bit streaming read of
+    ``nbytes`` (far above the 256 MiB Infinity Cache), GB/s."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(M.moe_probe_sink_words(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        M.moe_probe_stream_read(buf, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        M.moe_probe_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    return gbs
 
 
 def cpu_baseline(cfg, gbytes_total: float) -> dict:
@@ -119,20 +143,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # stage events: 5 per step, recorded by the library on `stream` between its kernels
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
-          for _ in range(args.steps)]
+    # timed region: K back-to-back layers, bracketed by synchronisation
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        step(events=ev[i])
+    for _ in range(args.steps):
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # per-kernel times: the same K steps again with the library recording HIP
+    # events on `stream` at its kernel boundaries
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(STAGES)}
+    dn_ms = stage_ms["down_combine"]
 
     # cold steps: a 512 MiB write between steps evicts the 256 MiB Infinity Cache and L2
     cold = None
@@ -151,6 +182,14 @@ def main():
         del flush
         cold = float(np.median(times))
 
+    probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        M.moe_probe_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
     us = ms_per_step * 1e3
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     gu_ms = stage_ms["gate_up"]
@@ -165,6 +204,8 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "us_per_layer": round(us, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "hbm_probe_GBps": round(probe_gbs, 1) if probe_gbs else None,
+        "pct_of_probe": round(100 * gbs / probe_gbs, 2) if probe_gbs else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -174,9 +215,13 @@ def main():
                        max_tokens_per_expert=int(counts_np.max()),
                        touched_weight_bytes=int(total_bytes), gemm_path=args.path),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "roofline": {"bound": "hbm", "kernel": "gate_up (fused gate+up MXFP4 GEMV + SiLU*up)",
+        "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
+                       "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "gemv_gate_up_kernel (fused gate+up MXFP4 GEMV + SiLU*up)",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
     }
     if cold is not None:

@@ -103,8 +103,8 @@ typedef struct moe_mxfp4_options {
     uint8_t* x_scales;   /* [T, H/32] E8M0 scales of x (MOE_ACT_MXFP8 only) */
     /* Optional hipEvent_t handles recorded on `stream` at the stage
      * boundaries: [0] before routing, [1] after routing, [2] after the
-     * gate_up GEMM, [3] after the down GEMM, [4] after the combine.  Only
-     * the first num_events (<= 5) are recorded; used to time the kernels. */
+     * gate_up GEMM, [3] after the down GEMM and the combine.  Only the
+     * first num_events (<= 4) are recorded; used to time the kernels. */
     void* const* events;
     int32_t num_events;
 } moe_mxfp4_options;

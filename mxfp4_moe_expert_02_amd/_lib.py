@@ -32,7 +32,8 @@ MOE_PATH_GEMV = 1
 MOE_PATH_MFMA = 2
 
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
-            "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string")
+            "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
+            "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,12 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.moe_mxfp4_status_string.restype = ctypes.c_char_p
         L.moe_mxfp4_status_string.argtypes = [ctypes.c_int]
+        L.moe_probe_stream_read.restype = ctypes.c_int
+        L.moe_probe_stream_read.argtypes = [vp, i64, vp, vp]
+        L.moe_probe_sink_words.restype = i64
+        L.moe_probe_sink_words.argtypes = []
+        L.moe_probe_copy.restype = ctypes.c_int
+        L.moe_probe_copy.argtypes = [vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -195,3 +202,23 @@ def moe_mxfp4_quantize(w, packed, scales, stream=None, check: bool = True) -> in
     _expect(scales, torch.uint8, (rows, cols // 32), "scales")
     rc = lib().moe_mxfp4_quantize(_ptr(w), rows, cols, _ptr(packed), _ptr(scales), _stream(stream))
     return _check(rc, "moe_mxfp4_quantize") if check else rc
+
+
+def moe_probe_sink_words() -> int:
+    return lib().moe_probe_sink_words()
+
+
+def moe_probe_stream_read(src, sink, stream=None, check: bool = True) -> int:
+    """Stream-read every byte of the device tensor ``src`` (128-bit loads)."""
+    rc = lib().moe_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                     _stream(stream))
+    return _check(rc, "moe_probe_stream_read") if check else rc
+
+
+def moe_probe_copy(src, dst, stream=None, check: bool = True) -> int:
+    """Copy the device tensor ``src`` into ``dst`` (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("moe_probe_copy: size mismatch")
+    rc = lib().moe_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))
+    return _check(rc, "moe_probe_copy") if check else rc

@@ -1,0 +1,57 @@
+// device_common.h -- small device helpers shared by the expert GEMM kernels.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (expert weights are read exactly once)
+__device__ inline uint4 load_stream16(const uint8_t* p) {
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// E8M0 code -> 2^(s-127) as fp32 (2^-127 is an fp32 subnormal; 0xFF -> NaN)
+__device__ inline float e8m0_to_f32(uint32_t s) {
+    float f = ldexpf(1.0f, (int)s - 127);
+    return s == 255u ? __builtin_nanf("") : f;
+}
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// out[t, n0 .. n0+width) = sum_j w[t,j] * y[pos[t,j], ...] summed in slot
+// order j = 0..k-1 in fp32, rounded to bf16.  y is read with agent-coherent
+// loads because other workgroups of the running kernel wrote it.
+__device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width) {
+    for (int c = threadIdx.x; c < width; c += blockDim.x) {
+        const int n = n0 + c;
+        float acc = 0.f;
+        for (int j = 0; j < a.k; j++) {
+            const float w = a.wts[(int64_t)t * a.k + j];
+            const int p = a.pos[(int64_t)t * a.k + j];
+            const float v = __hip_atomic_load(a.y + (int64_t)p * a.H + n, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            acc = fmaf(w, v, acc);
+        }
+        a.out[(int64_t)t * a.H + n] = f32_to_bf16_rne(acc);
+    }
+}
+
+}  // namespace moe

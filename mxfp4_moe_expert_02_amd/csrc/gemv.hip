@@ -23,21 +23,10 @@
 //     (row_ror 8, 4, 2, 1), leaving the sum in every lane.
 // gate_up items also apply SiLU(gate) * up and store h in bf16; down items
 // store the per-assignment outputs y in fp32.
-#include "moe_internal.h"
+#include "device_common.h"
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load (the weights are read exactly once)
-__device__ inline uint4 load_stream16(const uint8_t* p) {
-    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ inline bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
 // sum over the 16 lanes of a DPP row, result in all 16 lanes
 __device__ inline float row16_sum(float v) {
@@ -50,21 +39,6 @@ __device__ inline float row16_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                0x121, 0xf, 0xf, false));
     return v;
-}
-
-// E8M0 code -> 2^(s-127) as fp32 (2^-127 is an fp32 subnormal; 0xFF -> NaN)
-__device__ inline float e8m0_to_f32(uint32_t s) {
-    float f = ldexpf(1.0f, (int)s - 127);
-    return s == 255u ? __builtin_nanf("") : f;
-}
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
 }
 
 // LDS position (in 16-byte units) of quarter q of block b of a token row
@@ -82,39 +56,65 @@ __device__ inline void stage_rows(uint4* __restrict__ xs, int M, int K, RowFn ro
     }
 }
 
-// Dot products of R matrix rows with MT staged tokens, for this lane's
-// blocks of the rows.  rows[r] points at the packed row, srows[r] at its
-// scale row.  Returns per-lane partial sums in acc (not yet reduced).
-template <int MT, int R>
-__device__ inline void rows_dot(const uint8_t* const (&rows)[R], const uint8_t* const (&srows)[R],
-                                int nblk, const uint4* __restrict__ xs, int units_per_tok,
-                                int lane16, float (&acc)[R][MT]) {
-#pragma unroll
-    for (int r = 0; r < R; r++)
-#pragma unroll
-        for (int t = 0; t < MT; t++) acc[r][t] = 0.f;
+// ---------------------------------------------------------------------------
+// Software-pipelined row-pair GEMV core.
+//
+// A lane walks a flat sequence of steps; step s covers, for one unit (two
+// matrix rows), kGemvUnroll of the lane's blocks in each row.  The loads of
+// step s+1 are issued before step s is computed (two register buffers), so
+// every lane keeps 128-256 bytes of weights in flight, and the first step is
+// issued before the activation tile is staged.  A unit's 16 lanes reduce
+// with DPP when its last step is done and hand the sums to `epi`.
+// ---------------------------------------------------------------------------
 
-    for (int b0 = lane16; b0 < nblk; b0 += kGemvLanesPerRow * kGemvUnroll) {
-        uint4 w[kGemvUnroll][R];
-        uint32_t s[kGemvUnroll][R];
+template <int R>
+struct StepBuf {
+    uint4 w[kGemvUnroll][R];
+    uint32_t s[kGemvUnroll][R];
+};
+
+template <int MT, int R, typename RowsFn>
+struct RowGemv {
+    RowsFn rows_of;      // rows_of(unit, rows[R], srows[R])
+    int unit0, unit_step, n_units, n_iter, nblk, lane16;
+
+    __device__ int steps() const { return n_units * n_iter; }
+
+    __device__ void load(int s, StepBuf<R>& b) const {
+        const int u = unit0 + (s / n_iter) * unit_step, it = s % n_iter;
+        const uint8_t* rows[R];
+        const uint8_t* srows[R];
+        rows_of(u, rows, srows);
 #pragma unroll
-        for (int u = 0; u < kGemvUnroll; u++) {
-            int b = b0 + u * kGemvLanesPerRow;
+        for (int j = 0; j < kGemvUnroll; j++) {
+            const int blk = lane16 + kGemvLanesPerRow * (kGemvUnroll * it + j);
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                if (b < nblk) {
-                    w[u][r] = load_stream16(rows[r] + (int64_t)b * 16);
-                    s[u][r] = srows[r][b];
+                if (blk < nblk) {
+                    b.w[j][r] = load_stream16(rows[r] + (int64_t)blk * 16);
+                    b.s[j][r] = srows[r][blk];
                 } else {
-                    w[u][r] = make_uint4(0, 0, 0, 0);
-                    s[u][r] = 127;
+                    b.w[j][r] = make_uint4(0, 0, 0, 0);
+                    b.s[j][r] = 127;
                 }
             }
         }
+    }
+
+    // accumulate step s (whose loads are in b) into acc
+    __device__ void compute(int s, const StepBuf<R>& b, const uint4* __restrict__ xs,
+                            int units_per_tok, float (&acc)[R][MT]) const {
+        const int it = s % n_iter;
+        if (it == 0) {
 #pragma unroll
-        for (int u = 0; u < kGemvUnroll; u++) {
-            int b = b0 + u * kGemvLanesPerRow;
-            if (b >= nblk) break;
+            for (int r = 0; r < R; r++)
+#pragma unroll
+                for (int t = 0; t < MT; t++) acc[r][t] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kGemvUnroll; j++) {
+            const int blk = lane16 + kGemvLanesPerRow * (kGemvUnroll * it + j);
+            if (blk >= nblk) break;
             float part[R][MT];
 #pragma unroll
             for (int r = 0; r < R; r++)
@@ -124,142 +124,213 @@ __device__ inline void rows_dot(const uint8_t* const (&rows)[R], const uint8_t* 
             for (int q = 0; q < 4; q++) {
                 uint4 xv[MT];
 #pragma unroll
-                for (int t = 0; t < MT; t++) xv[t] = xs[t * units_per_tok + xs_unit(b, q)];
+                for (int t = 0; t < MT; t++) xv[t] = xs[t * units_per_tok + xs_unit(blk, q)];
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    uint32_t word = (q == 0) ? w[u][r].x : (q == 1) ? w[u][r].y
-                                  : (q == 2) ? w[u][r].z : w[u][r].w;
-                    // byte j of the word holds elements 2j (low nibble), 2j+1
-                    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0);
-                    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1);
-                    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2);
-                    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3);
+                    const uint32_t word = (q == 0) ? b.w[j][r].x : (q == 1) ? b.w[j][r].y
+                                        : (q == 2) ? b.w[j][r].z : b.w[j][r].w;
+                    // byte i of the word holds elements 2i (low nibble) and 2i+1
+                    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0);
+                    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1);
+                    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2);
+                    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3);
 #pragma unroll
                     for (int t = 0; t < MT; t++) {
-                        float a = part[r][t];
-                        a = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(xv[t].x), a, false);
-                        a = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(xv[t].y), a, false);
-                        a = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(xv[t].z), a, false);
-                        a = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(xv[t].w), a, false);
-                        part[r][t] = a;
+                        float v = part[r][t];
+                        v = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(xv[t].x), v, false);
+                        v = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(xv[t].y), v, false);
+                        v = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(xv[t].z), v, false);
+                        v = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(xv[t].w), v, false);
+                        part[r][t] = v;
                     }
                 }
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                float sc = e8m0_to_f32(s[u][r]);
+                const float sc = e8m0_to_f32(b.s[j][r]);
 #pragma unroll
                 for (int t = 0; t < MT; t++) acc[r][t] = fmaf(part[r][t], sc, acc[r][t]);
             }
         }
     }
-}
+};
 
-// Work item decode: blockIdx.x = slot * tiles + tile, slot indexes the
-// path's active-expert list.  Returns false when the slot is unused.
-__device__ inline bool item_of(const GemmArgs& a, int tiles, int& e, int& tile, int& M, int& off) {
-    int slot = blockIdx.x / tiles;
-    tile = blockIdx.x % tiles;
-    if (slot >= a.meta[a.list_meta]) return false;
-    e = a.list[slot];
-    M = a.counts[e];
-    off = a.offsets[e];
-    return true;
-}
-
-template <int MT>
-__device__ void gate_up_pass(const GemmArgs& a, int e, int tile, int off, int M,
-                             const uint4* xs) {
-    const int lane16 = threadIdx.x % kGemvLanesPerRow;
-    const int slot = threadIdx.x / kGemvLanesPerRow;
-    const int K = a.H, nblk = K / 32, units = K / 8;
-    const uint8_t* W = a.wgu + (int64_t)e * (2 * a.I) * (K / 2);
-    const uint8_t* S = a.sgu + (int64_t)e * (2 * a.I) * nblk;
-    const int n0 = tile * kGateUpUnits;
-    for (int unit = slot; unit < kGateUpUnits; unit += kGemvSlots) {
-        int n = n0 + unit;
-        if (n >= a.I) break;
-        const uint8_t* rows[2] = {W + (int64_t)n * (K / 2), W + (int64_t)(a.I + n) * (K / 2)};
-        const uint8_t* srows[2] = {S + (int64_t)n * nblk, S + (int64_t)(a.I + n) * nblk};
-        float acc[2][MT];
-        rows_dot<MT, 2>(rows, srows, nblk, xs, units, lane16, acc);
+// Run a RowGemv over its steps: first loads, then stage() (which must end
+// with a workgroup barrier), then the pipelined loop.  epi(unit, sums)
+// receives the reduced sums (valid in every lane of the 16) after each unit.
+template <int MT, int R, typename RowsFn, typename StageFn, typename EpiFn>
+__device__ void run_row_gemv(const RowGemv<MT, R, RowsFn>& g, const uint4* xs, int units_per_tok,
+                             StageFn stage, EpiFn epi) {
+    const int S = g.steps();
+    StepBuf<R> A, B;
+    float acc[R][MT];
+    if (S > 0) g.load(0, A);
+    stage();
+    auto finish = [&](int s) {
+        if (s % g.n_iter == g.n_iter - 1) {
+            float sums[R][MT];
 #pragma unroll
-        for (int t = 0; t < MT; t++) {
-            float g = row16_sum(acc[0][t]);
-            float u = row16_sum(acc[1][t]);
-            if (lane16 == t && t < M)
-                a.h[(int64_t)(off + t) * a.I + n] = f32_to_bf16_rne(silu_mul(g, u));
+            for (int r = 0; r < R; r++)
+#pragma unroll
+                for (int t = 0; t < MT; t++) sums[r][t] = row16_sum(acc[r][t]);
+            epi(g.unit0 + (s / g.n_iter) * g.unit_step, sums);
         }
-    }
-}
-
-template <int MT>
-__device__ void down_pass(const GemmArgs& a, int e, int tile, int off, int M, const uint4* xs) {
-    const int lane16 = threadIdx.x % kGemvLanesPerRow;
-    const int slot = threadIdx.x / kGemvLanesPerRow;
-    const int K = a.I, nblk = K / 32, units = K / 8;
-    const uint8_t* W = a.wdn + (int64_t)e * a.H * (K / 2);
-    const uint8_t* S = a.sdn + (int64_t)e * a.H * nblk;
-    const int n0 = tile * kDownUnits * 2;
-    for (int unit = slot; unit < kDownUnits; unit += kGemvSlots) {
-        int n = n0 + 2 * unit;
-        if (n >= a.H) break;
-        const uint8_t* rows[2] = {W + (int64_t)n * (K / 2), W + (int64_t)(n + 1) * (K / 2)};
-        const uint8_t* srows[2] = {S + (int64_t)n * nblk, S + (int64_t)(n + 1) * nblk};
-        float acc[2][MT];
-        rows_dot<MT, 2>(rows, srows, nblk, xs, units, lane16, acc);
-#pragma unroll
-        for (int t = 0; t < MT; t++) {
-            float y0 = row16_sum(acc[0][t]);
-            float y1 = row16_sum(acc[1][t]);
-            if (lane16 == t && t < M)
-                *reinterpret_cast<float2*>(a.y + (int64_t)(off + t) * a.H + n) =
-                    make_float2(y0, y1);
+    };
+    for (int s = 0; s < S; s += 2) {
+        if (s + 1 < S) g.load(s + 1, B);
+        g.compute(s, A, xs, units_per_tok, acc);
+        finish(s);
+        if (s + 1 < S) {
+            if (s + 2 < S) g.load(s + 2, A);
+            g.compute(s + 1, B, xs, units_per_tok, acc);
+            finish(s + 1);
         }
     }
 }
 
 extern __shared__ uint4 dyn_lds[];
 
-__global__ void __launch_bounds__(kGemvThreads)
-gemv_gate_up_kernel(GemmArgs a) {
-    const int tiles = (a.I + kGateUpUnits - 1) / kGateUpUnits;
-    int e, tile, M, off;
-    if (!item_of(a, tiles, e, tile, M, off)) return;
+// One gate_up pass over up to MT tokens (rows off .. off+m of the sorted
+// assignments): units are (gate row n, up row I+n) pairs of this tile.
+template <int MT>
+__device__ void gate_up_pass(const GemmArgs& a, int e, int tile, int off, int m, int tok0) {
+    const int lane16 = threadIdx.x % kGemvLanesPerRow;
+    const int slot = threadIdx.x / kGemvLanesPerRow;
+    const int K = a.H, nblk = K / 32, units = K / 8;
+    const uint8_t* W = a.wgu + (int64_t)e * (2 * a.I) * (K / 2);
+    const uint8_t* S = a.sgu + (int64_t)e * (2 * a.I) * nblk;
+    const int n0 = tile * kGateUpUnits;
+    const int nu = min(kGateUpUnits, a.I - n0);
+    auto rows_of = [&](int u, const uint8_t* (&rows)[2], const uint8_t* (&srows)[2]) {
+        const int n = n0 + u;
+        rows[0] = W + (int64_t)n * (K / 2);
+        rows[1] = W + (int64_t)(a.I + n) * (K / 2);
+        srows[0] = S + (int64_t)n * nblk;
+        srows[1] = S + (int64_t)(a.I + n) * nblk;
+    };
+    RowGemv<MT, 2, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
+                                        slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
+                                        (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
+                                            (kGemvLanesPerRow * kGemvUnroll),
+                                        nblk, lane16};
     uint4* xs = dyn_lds;
-    for (int t0 = 0; t0 < M; t0 += kGemvMaxTok) {
-        int m = min(kGemvMaxTok, M - t0);
-        __syncthreads();
-        stage_rows(xs, m, a.H, [&](int t) {
-            int token = a.sorted[off + t0 + t] / a.k;
-            return a.x + (int64_t)token * a.H;
+    auto stage = [&]() {
+        stage_rows(xs, m, K, [&](int t) {
+            const int token = a.sorted[off + t] / a.k;
+            return a.x + (int64_t)token * K;
         });
         __syncthreads();
+    };
+    auto epi = [&](int u, float (&sums)[2][MT]) {
+        const int n = n0 + u;
+#pragma unroll
+        for (int t = 0; t < MT; t++)
+            if (lane16 == t && t < m)
+                a.h[(int64_t)(off + t) * a.I + n] = f32_to_bf16_rne(silu_mul(sums[0][t], sums[1][t]));
+    };
+    run_row_gemv(g, xs, units, stage, epi);
+    (void)tok0;
+}
+
+// One down pass: units are two adjacent output rows (n, n+1) of this tile.
+template <int MT>
+__device__ void down_pass(const GemmArgs& a, int e, int tile, int off, int m) {
+    const int lane16 = threadIdx.x % kGemvLanesPerRow;
+    const int slot = threadIdx.x / kGemvLanesPerRow;
+    const int K = a.I, nblk = K / 32, units = K / 8;
+    const uint8_t* W = a.wdn + (int64_t)e * a.H * (K / 2);
+    const uint8_t* S = a.sdn + (int64_t)e * a.H * nblk;
+    const int n0 = tile * kColTile;
+    const int nu = min(kDownUnits, (a.H - n0) / 2);
+    auto rows_of = [&](int u, const uint8_t* (&rows)[2], const uint8_t* (&srows)[2]) {
+        const int n = n0 + 2 * u;
+        rows[0] = W + (int64_t)n * (K / 2);
+        rows[1] = W + (int64_t)(n + 1) * (K / 2);
+        srows[0] = S + (int64_t)n * nblk;
+        srows[1] = S + (int64_t)(n + 1) * nblk;
+    };
+    RowGemv<MT, 2, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
+                                        slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
+                                        (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
+                                            (kGemvLanesPerRow * kGemvUnroll),
+                                        nblk, lane16};
+    uint4* xs = dyn_lds;
+    auto stage = [&]() {
+        stage_rows(xs, m, K, [&](int t) { return a.h + (int64_t)(off + t) * K; });
+        __syncthreads();
+    };
+    auto epi = [&](int u, float (&sums)[2][MT]) {
+        const int n = n0 + 2 * u;
+#pragma unroll
+        for (int t = 0; t < MT; t++)
+            if (lane16 == t && t < m) {
+                // agent-coherent store: the combining block may run on another XCD
+                const uint64_t bits = (uint64_t)__float_as_uint(sums[0][t]) |
+                                      ((uint64_t)__float_as_uint(sums[1][t]) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(a.y + (int64_t)(off + t) * a.H + n),
+                                   bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+    };
+    run_row_gemv(g, xs, units, stage, epi);
+}
+
+// gate_up: blockIdx.x = slot * tg + tile over an upper bound of active
+// experts; a tile is 32 gate rows with their 32 up rows.  Blocks past the
+// routed experts exit at once.
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_gate_up_kernel(GemmArgs a) {
+    const int tg = (a.I + kGateUpUnits - 1) / kGateUpUnits;
+    const int slot = blockIdx.x / tg, tile = blockIdx.x % tg;
+    if (slot >= uniform(a.meta[a.list_meta])) return;
+    const int e = uniform(a.list[slot]);
+    const int M = uniform(a.counts[e]), off = uniform(a.offsets[e]);
+    for (int t0 = 0; t0 < M; t0 += kGemvMaxTok) {
+        const int m = min(kGemvMaxTok, M - t0);
+        __syncthreads();  // the previous pass is done with the staged tile
         switch (m) {
-            case 1: gate_up_pass<1>(a, e, tile, off + t0, m, xs); break;
-            case 2: gate_up_pass<2>(a, e, tile, off + t0, m, xs); break;
-            case 3: gate_up_pass<3>(a, e, tile, off + t0, m, xs); break;
-            default: gate_up_pass<4>(a, e, tile, off + t0, m, xs); break;
+            case 1: gate_up_pass<1>(a, e, tile, off + t0, m, t0); break;
+            case 2: gate_up_pass<2>(a, e, tile, off + t0, m, t0); break;
+            case 3: gate_up_pass<3>(a, e, tile, off + t0, m, t0); break;
+            default: gate_up_pass<4>(a, e, tile, off + t0, m, t0); break;
         }
     }
 }
 
-__global__ void __launch_bounds__(kGemvThreads)
+// down: blockIdx.x = slot * td + tile; a tile is kColTile output columns.
+// After writing its rows of y, a block counts the tile done for each of its
+// tokens; the block whose count completes a token's k experts combines that
+// token's tile.  Nothing waits: the last finisher does the work.  y moves
+// between blocks through agent-coherent atomic stores and loads, ordered
+// by waiting for this block's stores to complete before the counter update;
+// no L2 writeback or invalidate is needed.
+__global__ void __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(3)))
 gemv_down_kernel(GemmArgs a) {
-    const int tiles = (a.H + 2 * kDownUnits - 1) / (2 * kDownUnits);
-    int e, tile, M, off;
-    if (!item_of(a, tiles, e, tile, M, off)) return;
-    uint4* xs = dyn_lds;
+    __shared__ int s_combine[kGemvMaxTok];
+    const int td = a.col_tiles;
+    const int slot = blockIdx.x / td, tile = blockIdx.x % td;
+    if (slot >= uniform(a.meta[a.list_meta])) return;
+    const int e = uniform(a.list[slot]);
+    const int M = uniform(a.counts[e]), off = uniform(a.offsets[e]);
     for (int t0 = 0; t0 < M; t0 += kGemvMaxTok) {
-        int m = min(kGemvMaxTok, M - t0);
-        __syncthreads();
-        stage_rows(xs, m, a.I, [&](int t) { return a.h + (int64_t)(off + t0 + t) * a.I; });
+        const int m = min(kGemvMaxTok, M - t0);
         __syncthreads();
         switch (m) {
-            case 1: down_pass<1>(a, e, tile, off + t0, m, xs); break;
-            case 2: down_pass<2>(a, e, tile, off + t0, m, xs); break;
-            case 3: down_pass<3>(a, e, tile, off + t0, m, xs); break;
-            default: down_pass<4>(a, e, tile, off + t0, m, xs); break;
+            case 1: down_pass<1>(a, e, tile, off + t0, m); break;
+            case 2: down_pass<2>(a, e, tile, off + t0, m); break;
+            case 3: down_pass<3>(a, e, tile, off + t0, m); break;
+            default: down_pass<4>(a, e, tile, off + t0, m); break;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's y stores done
+        __syncthreads();
+        if (threadIdx.x < m) {
+            const int token = a.sorted[off + t0 + threadIdx.x] / a.k;
+            const int old = atomicAdd(&a.tile_done[token * td + tile], 1);
+            s_combine[threadIdx.x] = (old == a.k - 1) ? token : -1;
+        }
+        __syncthreads();
+        for (int i = 0; i < m; i++) {
+            const int token = uniform(s_combine[i]);
+            if (token >= 0) combine_tile(a, token, tile * kColTile, kColTile);
         }
     }
 }
@@ -267,16 +338,15 @@ gemv_down_kernel(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t stream) {
-    int tiles = (a.I + kGateUpUnits - 1) / kGateUpUnits;
-    size_t lds = (size_t)kGemvMaxTok * a.H * 2;
-    gemv_gate_up_kernel<<<max_active * tiles, kGemvThreads, lds, stream>>>(a);
+    const int tg = (a.I + kGateUpUnits - 1) / kGateUpUnits;
+    const size_t lds = (size_t)kGemvMaxTok * a.H * 2;
+    gemv_gate_up_kernel<<<max_active * tg, kGemvThreads, lds, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream) {
-    int tiles = (a.H + 2 * kDownUnits - 1) / (2 * kDownUnits);
-    size_t lds = (size_t)kGemvMaxTok * a.I * 2;
-    gemv_down_kernel<<<max_active * tiles, kGemvThreads, lds, stream>>>(a);
+    const size_t lds = (size_t)kGemvMaxTok * a.I * 2;
+    gemv_down_kernel<<<max_active * a.col_tiles, kGemvThreads, lds, stream>>>(a);
     return hipGetLastError();
 }
 

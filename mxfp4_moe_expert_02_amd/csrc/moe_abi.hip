@@ -52,7 +52,10 @@ size_t layout(Workspace* ws, char* base) {
     ws->pos = (int32_t*)take(S * 4);
     ws->gemv_list = (int32_t*)take(ws->E * 4);
     ws->mfma_list = (int32_t*)take(ws->E * 4);
+    ws->mfma_items = (int2*)take((ws->E + S / moe::kMfmaTok + 1) * sizeof(int2));
     ws->meta = (int32_t*)take(moe::kMetaWords * 4);
+    ws->col_tiles = (int)(ws->H / moe::kColTile);
+    ws->tile_done = (int32_t*)take((size_t)ws->max_tokens * (ws->H / moe::kMfmaDownRows) * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
     return off;
@@ -146,8 +149,10 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     // context-free checks first
     if (num_tokens < 0) return MOE_E_SHAPE;
     if (o.act_format != MOE_ACT_BF16) return MOE_E_OPTION;  // MXFP8 path not built yet
-    if (o.gemm_path != MOE_PATH_AUTO && o.gemm_path != MOE_PATH_GEMV) return MOE_E_OPTION;
-    if (o.num_events < 0 || o.num_events > 5 || (o.num_events > 0 && !o.events))
+    if (o.gemm_path != MOE_PATH_AUTO && o.gemm_path != MOE_PATH_GEMV &&
+        o.gemm_path != MOE_PATH_MFMA)
+        return MOE_E_OPTION;
+    if (o.num_events < 0 || o.num_events > 4 || (o.num_events > 0 && !o.events))
         return MOE_E_OPTION;
     if (num_tokens == 0) return MOE_OK;
     if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
@@ -174,8 +179,9 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     hipError_t err;
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30,
-                            o.gemm_path == MOE_PATH_AUTO ? 1 : o.gemm_path, st);
+    // AUTO takes the matrix-core path for every expert
+    const int path = o.gemm_path == MOE_PATH_AUTO ? MOE_PATH_MFMA : o.gemm_path;
+    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, st);
     if (err != hipSuccess) return hip_fail(err, "route");
     if ((err = mark(1)) != hipSuccess) return hip_fail(err, "hipEventRecord");
 
@@ -197,15 +203,29 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.H = H;
     a.I = I;
     a.k = k;
-    err = moe::launch_gemv_gate_up(a, max_active, st);
-    if (err != hipSuccess) return hip_fail(err, "gate_up");
-    if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    err = moe::launch_gemv_down(a, max_active, st);
-    if (err != hipSuccess) return hip_fail(err, "down");
+    a.tile_done = ws->tile_done;
+    a.items = ws->mfma_items;
+    a.wts = ws->wts;
+    a.pos = ws->pos;
+    a.out = (uint16_t*)out;
+    a.col_tiles = ws->col_tiles;
+    if (path == MOE_PATH_GEMV) {
+        err = moe::launch_gemv_gate_up(a, max_active, st);
+        if (err != hipSuccess) return hip_fail(err, "gate_up");
+        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        err = moe::launch_gemv_down(a, max_active, st);
+        if (err != hipSuccess) return hip_fail(err, "down");
+    } else {
+        a.list = ws->mfma_list;
+        a.list_meta = moe::kMetaNumMfma;
+        const int max_items = max_active + S / moe::kMfmaTok + 1;
+        err = moe::launch_mfma_gate_up(a, max_items, st);
+        if (err != hipSuccess) return hip_fail(err, "gate_up");
+        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        err = moe::launch_mfma_down(a, max_items, st);
+        if (err != hipSuccess) return hip_fail(err, "down");
+    }
     if ((err = mark(3)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    err = moe::launch_combine(ws->y, ws->wts, ws->pos, T, H, k, (uint16_t*)out, st);
-    if (err != hipSuccess) return hip_fail(err, "combine");
-    if ((err = mark(4)) != hipSuccess) return hip_fail(err, "hipEventRecord");
 
     // optional copies of the routing result
     struct {

@@ -25,8 +25,22 @@ constexpr int kMaxExperts = 1024;
 enum Meta : int {
     kMetaNumGemv = 0,   // active experts on the GEMV path
     kMetaNumMfma = 1,   // active experts on the MFMA path
+    kMetaNumMfmaItems = 2,  // (expert, token group) items of the MFMA path
     kMetaWords = 16,
 };
+
+// columns of the output covered by one down-projection tile of the GEMV
+// path; also the width of its combine tile
+constexpr int kColTile = 2 * kDownUnits;
+
+// MFMA path: an item is one expert and up to kMfmaTok of its tokens; a
+// gate_up tile is kMfmaRows gate rows with their up rows, a down tile is
+// kMfmaDownRows output rows (also its combine tile width); the 4 waves of a
+// workgroup split K.
+constexpr int kMfmaTok = 16;
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaDownRows = 32;
+constexpr int kMfmaThreads = 256;
 
 // One device's workspace, owned by the library.
 struct Workspace {
@@ -43,7 +57,10 @@ struct Workspace {
     int32_t* pos = nullptr;     // [Tmax*kmax]
     int32_t* gemv_list = nullptr;  // [E] active experts routed to the GEMV path
     int32_t* mfma_list = nullptr;  // [E] active experts routed to the MFMA path
+    int2* mfma_items = nullptr;    // [E + Tmax*kmax/kMfmaTok] (slot, first token) of MFMA items
     int32_t* meta = nullptr;       // [kMetaWords]
+    int32_t* tile_done = nullptr;  // [Tmax * H/kMfmaDownRows] finished down tiles per (token, column tile)
+    int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
     float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order
 };
@@ -64,16 +81,28 @@ struct GemmArgs {
     uint16_t* h;
     float* y;
     int T, H, I, k;
+    // combine state
+    int32_t* tile_done;         // [T * tiles] experts done per (token, column tile)
+    const int2* items;          // MFMA path: (slot, first token) per item
+    const float* wts;           // [T*k] routing weights
+    const int32_t* pos;         // [T*k] slot -> row of y
+    uint16_t* out;              // [T, H] bf16
+    int col_tiles;
 };
 
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch.
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
                         int gemv_max_tokens, int path, hipStream_t stream);
+// GEMV path: gate_up (+ SiLU * up -> h), then down (-> y) whose last
+// finisher per (token, column tile) also combines that tile of the output.
+// max_active bounds the number of routed experts (grids are sized by it).
 hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t stream);
 hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream);
-hipError_t launch_combine(const float* y, const float* wts, const int32_t* sorted_pos,
-                          int T, int H, int k, uint16_t* out, hipStream_t stream);
+// MFMA path: same contract, items from the route's MFMA item list;
+// max_items bounds their number.
+hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                                  uint8_t* scales, hipStream_t stream);
 

@@ -1,14 +1,6 @@
-// combine_quant.hip -- the weighted combine of expert outputs and the MXFP4
-// weight encoder, gfx950.
+// quant.hip -- MXFP4 weight encoder, gfx950.
 //
-// combine: out[t] = sum_j w[t,j] * y[pos[t,j]], summed in slot order j =
-// 0..k-1 in fp32 and rounded to bf16 (nearest even).  A gather, not a
-// scatter: no atomics, so the result is bit-reproducible.  This realises the
-// weighted sum of the k experts' outputs that top-k MoE routing implies
-// (bjdmk.com.cn news page, co-design section: each expert sees only part of
-// the tokens).
-//
-// quantize: MXFP4 encoding of float32 weights along the rows, one thread per
+// MXFP4 encoding of float32 weights along the rows, one thread per
 // block of 32 (OCP MX block: 32 E2M1 elements + one E8M0 scale), the format
 // the pages give the expert weights (bjdmk.com.cn page, 4 bits per
 // parameter).  The element rounding is written as a count of crossed
@@ -17,40 +9,6 @@
 
 namespace moe {
 namespace {
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-constexpr int kCombineThreads = 256;
-
-// grid (ceil(H / (4*256)), T); each thread owns 4 consecutive columns
-__global__ void __launch_bounds__(kCombineThreads)
-combine_kernel(const float* __restrict__ y, const float* __restrict__ wts,
-               const int32_t* __restrict__ pos, int H, int k, uint16_t* __restrict__ out) {
-    const int t = blockIdx.y;
-    const int n = (blockIdx.x * kCombineThreads + threadIdx.x) * 4;
-    if (n >= H) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; j++) {
-        float w = wts[(int64_t)t * k + j];
-        int p = pos[(int64_t)t * k + j];
-        float4 v = *reinterpret_cast<const float4*>(y + (int64_t)p * H + n);
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
-    }
-    ushort4 o;
-    o.x = f32_to_bf16_rne(acc.x);
-    o.y = f32_to_bf16_rne(acc.y);
-    o.z = f32_to_bf16_rne(acc.z);
-    o.w = f32_to_bf16_rne(acc.w);
-    *reinterpret_cast<ushort4*>(out + (int64_t)t * H + n) = o;
-}
 
 // floor(log2(a)) of a finite a > 0 given as float bits
 __device__ inline int floor_log2_f32(uint32_t bits) {
@@ -114,13 +72,6 @@ quantize_mxfp4_kernel(const float* __restrict__ w, int64_t nblocks, int64_t bloc
 }
 
 }  // namespace
-
-hipError_t launch_combine(const float* y, const float* wts, const int32_t* pos, int T, int H,
-                          int k, uint16_t* out, hipStream_t stream) {
-    dim3 grid((H / 4 + kCombineThreads - 1) / kCombineThreads, T);
-    combine_kernel<<<grid, kCombineThreads, 0, stream>>>(y, wts, pos, H, k, out);
-    return hipGetLastError();
-}
 
 hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                                  uint8_t* scales, hipStream_t stream) {

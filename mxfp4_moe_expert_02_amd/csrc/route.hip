@@ -8,14 +8,18 @@
 // (token, slot) assignments by expert, so that each expert's tokens are
 // contiguous and every expert that got no token produces no work at all.
 //
-// Two kernels:
-//   route_topk_kernel  one wave per token: k rounds of a wave-wide arg-max
-//                      over (logit desc, index asc), then the weights.
-//   route_sort_kernel  one workgroup: per-range histograms in LDS, a scan
-//                      over ranges and experts, a stable scatter, and the
-//                      lists of active experts (heaviest first) per path.
-// All of it is integer or compare-only except the weights, so ids, counts,
-// offsets and the sorted order are bit-exact and deterministic.
+// Top-k is computed by rank counting: the rank of expert e for token t is
+// the number of experts that beat it (larger logit, or equal logit and lower
+// index); ranks 0..k-1 are the chosen slots.  Every (t, e) pair is ranked
+// independently, so there is no serial reduction chain.  The sort builds
+// per-range histograms in LDS, scans them, and scatters each range in slot
+// order, which makes the order inside an expert ascending and the whole
+// result deterministic.  Selection, counts, offsets and order are integer or
+// compare-only, hence bit-exact; only the weights use exp.
+//
+// Small layers (T*E <= kFusedPairs) route in one workgroup (one launch);
+// larger ones use a grid for top-k and one workgroup for the sort.  Both
+// also reset the per-(token, column tile) combine counters.
 #include <float.h>
 #include <limits.h>
 
@@ -24,193 +28,225 @@
 namespace moe {
 namespace {
 
-constexpr int kTopkWavesPerBlock = 4;
-constexpr int kMaxPerLane = kMaxExperts / kWave;  // 16 logits per lane
-
-struct Cand {
-    float v;
-    int i;
-};
+constexpr int kRouteThreads = 1024;
+constexpr int kFusedPairs = 12288;    // T*E routed by the single-workgroup kernel
+constexpr int kTopkThreads = 256;
+constexpr int kSortLdsInts = 12288;   // per-range histograms
 
 // a beats b: larger logit, or equal logit and lower expert index
 __device__ inline bool beats(float av, int ai, float bv, int bi) {
     return av > bv || (av == bv && ai < bi);
 }
 
-__global__ void __launch_bounds__(kTopkWavesPerBlock * kWave)
-route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                  int32_t* __restrict__ ids, float* __restrict__ wts) {
+// Inclusive prefix sum over a wave64 with DPP row shifts and row broadcasts.
+__device__ inline int wave_incl_scan(int v) {
     const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kTopkWavesPerBlock + threadIdx.x / kWave;
-    if (t >= T) return;
-    const float* row = logits + (int64_t)t * E;
+    int t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += t;
+    t = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    v += t;
+    (void)lane;
+    return v;
+}
 
-    float v[kMaxPerLane];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) {
-        int e = lane + i * kWave;
-        v[i] = (e < E) ? row[e] : -INFINITY;
-        if (e >= E) taken |= 1u << i;
+// Rank-count top-k of the tokens [t0, t0+nt) whose logits sit in LDS
+// (lg[i*E + e] for token t0+i).  sel_id/sel_l [nt*k] are LDS scratch.
+// Writes ids and weights of those tokens.  Uses every thread of the block.
+__device__ void topk_tokens(const float* lg, int nt, int t0, int E, int k, int* sel_id,
+                            float* sel_l, int32_t* ids, float* wts) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    for (int i = tid; i < nt * k; i += nthr) {
+        sel_id[i] = i % k;  // defined even if NaN logits leave a rank unfilled
+        sel_l[i] = -INFINITY;
     }
-    float my_logit = -INFINITY;
-    int my_id = 0;
-    float top = 0.f;
-    for (int r = 0; r < k; r++) {
-        // best untaken candidate of this lane
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; i++) {
-            int e = lane + i * kWave;
-            if (!(taken & (1u << i)) && beats(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
-        // wave-wide arg-max by butterfly; every lane ends with the winner
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-            float ov = __shfl_xor(bv, m, kWave);
-            int oi = __shfl_xor(bi, m, kWave);
-            if (beats(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (r == 0) top = bv;
-        // the owner marks it taken
-        if (bi % kWave == lane) taken |= 1u << (bi / kWave);
-        if (lane == r) {
-            my_logit = bv;
-            my_id = bi;
+    __syncthreads();
+    for (int p = tid; p < nt * E; p += nthr) {
+        const int i = p / E, e = p % E;
+        const float* row = lg + i * E;
+        const float v = row[e];
+        int rank = 0;
+        for (int f = 0; f < E; f++) rank += beats(row[f], f, v, e) ? 1 : 0;
+        if (rank < k) {
+            sel_id[i * k + rank] = e;
+            sel_l[i * k + rank] = v;
         }
     }
-    // renormalised softmax over the k chosen logits
-    float p = (lane < k) ? __expf(my_logit - top) : 0.f;
-    float s = p;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) s += __shfl_xor(s, m, kWave);
-    if (lane < k) {
-        ids[(int64_t)t * k + lane] = my_id;
-        wts[(int64_t)t * k + lane] = p / s;
+    __syncthreads();
+    for (int p = tid; p < nt * k; p += nthr) {
+        const int i = p / k, j = p % k;
+        const float top = sel_l[i * k];
+        float s = 0.f;
+        for (int q = 0; q < k; q++) s += __expf(sel_l[i * k + q] - top);
+        const int64_t o = (int64_t)(t0 + i) * k + j;
+        ids[o] = sel_id[p];
+        wts[o] = __expf(sel_l[p] - top) / s;
     }
 }
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortLdsInts = 16384;  // 64 KiB of per-range histograms
-
-__global__ void __launch_bounds__(kSortThreads)
-route_sort_kernel(const int32_t* __restrict__ ids, int S, int E, int32_t* __restrict__ counts,
-                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
-                  int32_t* __restrict__ pos, int32_t* __restrict__ gemv_list,
-                  int32_t* __restrict__ mfma_list, int32_t* __restrict__ meta,
-                  int gemv_max_tokens, int path) {
-    __shared__ int32_t hist[kSortLdsInts];
-    __shared__ int32_t s_cnt[kMaxExperts];
-    __shared__ int32_t s_off[kMaxExperts + 1];
-    __shared__ int32_t s_ngemv, s_nmfma;
-    const int tid = threadIdx.x;
-
-    // number of ranges R (power of two): R*E ints fit in LDS, R <= threads, R <= S
+// Stable counting sort of the S slots by expert (ids[s] = expert of slot
+// s, in LDS or global memory), the active-expert lists, and the reset of
+// the combine counters.  One workgroup.
+__device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Workspace& ws,
+                           int gemv_max_tokens, int path, int* hist, int* s_cnt, int* s_off) {
+    __shared__ int s_n[3];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    // R ranges (power of two) of L consecutive slots: R ~ sqrt(S), R*E fits in LDS
     int R = 1;
-    while (R * 2 <= kSortThreads && R * 2 * E <= kSortLdsInts && R * 2 <= S) R *= 2;
-    const int L = (S + R - 1) / R;  // slots per range
+    while (R * 2 <= nthr && R * 2 * E <= kSortLdsInts && R * R * 4 <= S) R *= 2;
+    const int L = (S + R - 1) / R;
 
-    for (int i = tid; i < R * E; i += kSortThreads) hist[i] = 0;
-    if (tid == 0) {
-        s_ngemv = 0;
-        s_nmfma = 0;
-    }
+    for (int i = tid; i < R * E; i += nthr) hist[i] = 0;
+    if (tid < 3) s_n[tid] = 0;
+    // reset the combine counters of the down kernels (sized for the finest tile)
+    for (int i = tid; i < T * (int)(ws.H / kMfmaDownRows); i += nthr) ws.tile_done[i] = 0;
     __syncthreads();
-    // 1. per-range histogram (each range owned by one thread: no atomics)
-    if (tid < R) {
-        int s0 = tid * L, s1 = min(S, s0 + L);
+    if (tid < R) {  // 1. per-range histogram
+        const int s0 = tid * L, s1 = min(S, s0 + L);
         for (int s = s0; s < s1; s++) hist[tid * E + ids[s]]++;
     }
     __syncthreads();
-    // 2. per expert: exclusive scan over ranges
-    for (int e = tid; e < E; e += kSortThreads) {
+    for (int e = tid; e < E; e += nthr) {  // 2. per expert: exclusive scan over ranges
         int run = 0;
         for (int r = 0; r < R; r++) {
-            int c = hist[r * E + e];
+            const int c = hist[r * E + e];
             hist[r * E + e] = run;
             run += c;
         }
         s_cnt[e] = run;
-        counts[e] = run;
+        ws.counts[e] = run;
     }
     __syncthreads();
-    // 3. exclusive scan over experts (E <= 1024: one wave, chunks of 64)
-    if (tid < kWave) {
+    if (tid < kWave) {  // 3. exclusive scan over experts, one wave, 64 at a time
         int carry = 0;
         for (int base = 0; base < E; base += kWave) {
-            int e = base + tid;
-            int c = (e < E) ? s_cnt[e] : 0;
-            int incl = c;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                int o = __shfl_up(incl, d, kWave);
-                if (tid >= d) incl += o;
-            }
+            const int e = base + tid;
+            const int c = (e < E) ? s_cnt[e] : 0;
+            const int incl = wave_incl_scan(c);
             if (e < E) s_off[e] = carry + incl - c;
-            carry += __shfl(incl, kWave - 1, kWave);
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (tid == 0) s_off[E] = carry;
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += kSortThreads) offsets[e] = s_off[e];
-    // 4. stable scatter: each range walks its slots in order
-    if (tid < R) {
-        int s0 = tid * L, s1 = min(S, s0 + L);
+    for (int e = tid; e <= E; e += nthr) ws.offsets[e] = s_off[e];
+    if (tid < R) {  // 4. stable scatter: each range walks its slots in order
+        const int s0 = tid * L, s1 = min(S, s0 + L);
         for (int s = s0; s < s1; s++) {
-            int e = ids[s];
-            int p = s_off[e] + hist[tid * E + e]++;
-            sorted[p] = s;
-            pos[s] = p;
+            const int e = ids[s];
+            const int p = s_off[e] + hist[tid * E + e]++;
+            ws.sorted[p] = s;
+            ws.pos[s] = p;
         }
     }
-    // 5. active experts, heaviest first (ties: lower index first), split by path
-    for (int e = tid; e < E; e += kSortThreads) {
-        int c = s_cnt[e];
-        if (c == 0) continue;
-        bool to_gemv = (path == 1) || (path == 0 && c <= gemv_max_tokens);
-        int rank = 0;
+    // 5. active-expert lists.  GEMV path: ascending expert index (every
+    //    GEMV item costs about the same), compacted with a wave scan.
+    //    MFMA path: heaviest first (ties: lower index first) so the longest
+    //    items start earliest.
+    if (tid < kWave) {
+        int carry = 0;
+        for (int base = 0; base < E; base += kWave) {
+            const int e = base + tid;
+            const int c = (e < E) ? s_cnt[e] : 0;
+            const bool g = c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens));
+            const int incl = wave_incl_scan(g ? 1 : 0);
+            if (g) ws.gemv_list[carry + incl - 1] = e;
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        if (tid == 0) s_n[0] = carry;
+    }
+    for (int e = tid; e < E; e += nthr) {
+        const int c = s_cnt[e];
+        const bool m = c > 0 && !((path == 1) || (path == 0 && c <= gemv_max_tokens));
+        if (!m) continue;
+        int rank = 0, base = 0;  // base: items of the experts ranked before e
         for (int f = 0; f < E; f++) {
-            int cf = s_cnt[f];
-            if (cf == 0) continue;
-            bool f_gemv = (path == 1) || (path == 0 && cf <= gemv_max_tokens);
-            if (f_gemv != to_gemv) continue;
-            if (cf > c || (cf == c && f < e)) rank++;
+            const int cf = s_cnt[f];
+            const bool mf = cf > 0 && !((path == 1) || (path == 0 && cf <= gemv_max_tokens));
+            if (mf && (cf > c || (cf == c && f < e))) {
+                rank++;
+                base += (cf + kMfmaTok - 1) / kMfmaTok;
+            }
         }
-        if (to_gemv) {
-            gemv_list[rank] = e;
-            atomicAdd(&s_ngemv, 1);
-        } else {
-            mfma_list[rank] = e;
-            atomicAdd(&s_nmfma, 1);
-        }
+        ws.mfma_list[rank] = e;
+        const int groups = (c + kMfmaTok - 1) / kMfmaTok;
+        for (int g = 0; g < groups; g++) ws.mfma_items[base + g] = make_int2(rank, g * kMfmaTok);
+        atomicAdd(&s_n[1], 1);
+        atomicAdd(&s_n[2], groups);
     }
     __syncthreads();
     if (tid == 0) {
-        meta[kMetaNumGemv] = s_ngemv;
-        meta[kMetaNumMfma] = s_nmfma;
+        ws.meta[kMetaNumGemv] = s_n[0];
+        ws.meta[kMetaNumMfma] = s_n[1];
+        ws.meta[kMetaNumMfmaItems] = s_n[2];
     }
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_fused_kernel(const float* __restrict__ logits, int T, int E, int k, Workspace ws,
+                   int gemv_max_tokens, int path) {
+    __shared__ float lg[kFusedPairs];
+    __shared__ int sel_id[kRouteThreads];
+    __shared__ float sel_l[kRouteThreads];
+    __shared__ int hist[kSortLdsInts];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts + 1];
+    for (int i = threadIdx.x; i < T * E; i += blockDim.x) lg[i] = logits[i];
+    __syncthreads();
+    topk_tokens(lg, T, 0, E, k, sel_id, sel_l, ws.ids, ws.wts);
+    __syncthreads();
+    // the ids of all T*k slots are still in LDS (sel_id), read them there
+    sort_slots(sel_id, T * k, E, T, ws, gemv_max_tokens, path, hist, s_cnt, s_off);
+}
+
+// grid over token groups: each block ranks tokens [t0, t0 + nt)
+__global__ void __launch_bounds__(kTopkThreads)
+route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int tokens_per_block,
+                  int32_t* __restrict__ ids, float* __restrict__ wts) {
+    extern __shared__ float dyn[];
+    const int t0 = blockIdx.x * tokens_per_block;
+    const int nt = min(tokens_per_block, T - t0);
+    float* lg = dyn;
+    int* sel_id = reinterpret_cast<int*>(dyn + tokens_per_block * E);
+    float* sel_l = dyn + tokens_per_block * E + tokens_per_block * k;
+    for (int i = threadIdx.x; i < nt * E; i += blockDim.x) lg[i] = logits[(int64_t)t0 * E + i];
+    __syncthreads();
+    topk_tokens(lg, nt, t0, E, k, sel_id, sel_l, ids, wts);
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_sort_kernel(int T, int E, int k, Workspace ws, int gemv_max_tokens, int path) {
+    __shared__ int hist[kSortLdsInts];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts + 1];
+    sort_slots(ws.ids, T * k, E, T, ws, gemv_max_tokens, path, hist, s_cnt, s_off);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
                         int gemv_max_tokens, int path, hipStream_t stream) {
-    int blocks = (T + kTopkWavesPerBlock - 1) / kTopkWavesPerBlock;
-    route_topk_kernel<<<blocks, kTopkWavesPerBlock * kWave, 0, stream>>>(logits, T, E, k, ws.ids,
-                                                                          ws.wts);
+    if ((int64_t)T * E <= kFusedPairs && T * k <= kRouteThreads) {
+        route_fused_kernel<<<1, kRouteThreads, 0, stream>>>(logits, T, E, k, ws,
+                                                            gemv_max_tokens, path);
+        return hipGetLastError();
+    }
+    const int tpb = E >= kTopkThreads ? 1 : kTopkThreads / E;
+    const int blocks = (T + tpb - 1) / tpb;
+    const size_t lds = (size_t)tpb * (E + 2 * k) * 4;
+    route_topk_kernel<<<blocks, kTopkThreads, lds, stream>>>(logits, T, E, k, tpb, ws.ids,
+                                                             ws.wts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_sort_kernel<<<1, kSortThreads, 0, stream>>>(ws.ids, T * k, E, ws.counts, ws.offsets,
-                                                      ws.sorted, ws.pos, ws.gemv_list,
-                                                      ws.mfma_list, ws.meta, gemv_max_tokens,
-                                                      path);
+    route_sort_kernel<<<1, kRouteThreads, 0, stream>>>(T, E, k, ws, gemv_max_tokens, path);
     return hipGetLastError();
 }
 

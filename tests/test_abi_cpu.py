@@ -10,7 +10,8 @@ import pytest
 
 from tests.conftest import ROOT, gpu_available
 
-HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,14 +23,18 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_mxfp4_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward", "moe_mxfp4_forward_ex",
-        "moe_mxfp4_quantize", "moe_mxfp4_status_string"])
+        "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_probe_stream_read",
+        "moe_probe_sink_words", "moe_probe_copy"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -38,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (moe_mxfp4_\w+)", out))
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
     assert set(declared_functions()) <= exported
     assert set(L.EXPORTED) == set(declared_functions())
 

@@ -56,6 +56,8 @@ def run(M, layer, path=0, debug=False):
                    counts=torch.empty(c.E, dtype=torch.int32, device="cuda"),
                    offsets=torch.empty(c.E + 1, dtype=torch.int32, device="cuda"),
                    sorted=torch.empty(S, dtype=torch.int32, device="cuda"))
+    layer.out.fill_(float("nan"))  # every element must be written by this call
+    torch.cuda.synchronize()
     say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path}")
     M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, layer.wgu, layer.wdn, layer.scales,
                            layer.out, gemm_path=path, **dbg)
@@ -172,71 +174,98 @@ def _parity(M, oracle_lib, cfg, layer, tokens, path=0, logits=None):
     ids = oracle_lib.route(lg, cfg.k)["ids"]
     ex = oracle_experts(oracle_lib, cfg, ids[tokens].ravel())
     ref = oracle_lib.forward(make_x_bf16(cfg), lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens)
-    got = bf16_tensor_to_f64(layer.out)[tokens]
+    full = bf16_tensor_to_f64(layer.out)
+    assert np.isfinite(full).all()  # every (token, column) was written
+    got = full[tokens]
     ratio = parity_ratio(got, ref)
     say(f"parity {cfg.name} tokens={list(tokens)} max|d|/rms = {ratio:.3e}")
-    assert np.isfinite(got).all()
     assert ratio <= TOL
     return ratio
 
 
-def test_forward_tiny_all_tokens(torch_dev, M, oracle_lib):
+PATHS = [pytest.param(1, id="gemv"), pytest.param(2, id="mfma")]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_tiny_all_tokens(torch_dev, M, oracle_lib, path):
     cfg = get_config("c1")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(cfg.T)))
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(cfg.T)), path=path)
 
 
-def test_forward_verify_sampled(torch_dev, M, oracle_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_verify_sampled(torch_dev, M, oracle_lib, path):
     cfg = get_config("c2")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 4, 8])
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 4, 8], path=path)
 
 
-def test_forward_batched_verify_sampled(torch_dev, M, oracle_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_batched_verify_sampled(torch_dev, M, oracle_lib, path):
     cfg = get_config("c3")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71])
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71], path=path)
 
 
-def test_forward_zipf_verify_sampled(torch_dev, M, oracle_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_zipf_verify_sampled(torch_dev, M, oracle_lib, path):
     cfg = get_config("c4")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 143, 287])
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 143, 287], path=path)
 
 
-def test_forward_one_hot_expert_many_tokens(torch_dev, M, oracle_lib):
-    """Every token picks expert 3 first: one expert with 13 tokens (several
-    GEMV passes), ragged tail of 1 token."""
-    cfg = Config("hot", "hot_t13_e8_h384_i256_k3", 13, 8, 384, 256, 3, "normal", "bf16", 11)
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_one_hot_expert_many_tokens(torch_dev, M, oracle_lib, path):
+    """Every token picks expert 3 first: one expert with 37 tokens (several
+    GEMV passes, three MFMA token groups with a ragged last one)."""
+    cfg = Config("hot", "hot_t37_e8_h384_i256_k3", 37, 8, 384, 256, 3, "normal", "bf16", 11)
     logits = make_logits(cfg)
     logits[:, 3] += 100.0
-    _parity(M, oracle_lib, cfg, get_layer(cfg, logits=logits), list(range(cfg.T)), logits=logits)
+    _parity(M, oracle_lib, cfg, get_layer(cfg, logits=logits), list(range(cfg.T)), path=path,
+            logits=logits)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T,k", [(1, 1), (1, 8), (2, 5)])
-def test_forward_small_edges(torch_dev, M, oracle_lib, T, k):
+def test_forward_small_edges(torch_dev, M, oracle_lib, T, k, path):
     cfg = Config("edge", f"edge_t{T}_e8_h256_i128_k{k}", T, 8, 256, 128, k, "normal", "bf16", 21 + T)
-    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(T)))
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(T)), path=path)
 
 
-def test_forward_deterministic(torch_dev, M):
+def test_forward_paths_agree(torch_dev, M):
+    """The VALU and matrix-core paths compute the same layer: their bf16
+    outputs differ only by accumulation order (within the parity bar)."""
+    import torch
     cfg = get_config("c2")
     layer = get_layer(cfg)
-    run(M, layer)
+    run(M, layer, path=1)
+    a = layer.out.float().clone()
+    run(M, layer, path=2)
+    b = layer.out.float()
+    rms = torch.sqrt(torch.mean(a * a))
+    assert float((a - b).abs().max() / rms) <= TOL
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_deterministic(torch_dev, M, path):
+    cfg = get_config("c2")
+    layer = get_layer(cfg)
+    run(M, layer, path=path)
     a = layer.out.clone()
-    run(M, layer)
+    run(M, layer, path=path)
     assert torch_dev.equal(a.view(torch_dev.int16), layer.out.view(torch_dev.int16))
 
 
-def test_untouched_experts_are_not_read(torch_dev, M):
+@pytest.mark.parametrize("path", PATHS)
+def test_untouched_experts_are_not_read(torch_dev, M, path):
     """NaN scales (0xFF) on every expert no token chooses: output unchanged."""
     import torch
     cfg = Config("pois", "poison_t9_e16_h256_i128_k2", 9, 16, 256, 128, 2, "normal", "bf16", 31)
     logits = make_logits(cfg)
     logits[:, 10:] -= 100.0
     layer = get_layer(cfg, logits=logits)
-    run(M, layer)
+    run(M, layer, path=path)
     base = layer.out.clone()
     sgu, sdn = layer.sgu.clone(), layer.sdn.clone()
     layer.sgu[10:] = 255
     layer.sdn[10:] = 255
-    run(M, layer)
+    run(M, layer, path=path)
     assert torch.isfinite(layer.out.float()).all()
     assert torch.equal(base.view(torch.int16), layer.out.view(torch.int16))
     layer.sgu.copy_(sgu)
