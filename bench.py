@@ -39,7 +39,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="c2", help="workload key c1..c4 (default: c2, 9-token verify)")
-    p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA")
+    p.add_argument("--path", type=int, default=0,
+                   help="1: VALU GEMV over row-major weights; 2 (default): bf16 MFMA over "
+                        "the tile layout (weights prepacked once before timing)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
@@ -126,17 +128,20 @@ def main():
     M.moe_mxfp4_init(cfg.T, cfg.E, cfg.H, cfg.I, cfg.k)
     stream = torch.cuda.current_stream()
 
+    path = args.path or M.MOE_PATH_MFMA
+    layout = M.MOE_LAYOUT_TILES if path == M.MOE_PATH_MFMA else M.MOE_LAYOUT_ROWS
+    wgu, wdn, scales = layer.weights(layout)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, layer.wgu, layer.wdn, layer.scales,
-                           layer.out, gemm_path=args.path, counts=counts)
+    M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
+                           gemm_path=path, weight_layout=layout, counts=counts)
     torch.cuda.synchronize()
     counts_np = counts.cpu().numpy()
     gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
     total_bytes = gu_bytes + dn_bytes
 
     def step(events=None):
-        M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, layer.wgu, layer.wdn,
-                               layer.scales, layer.out, gemm_path=args.path, events=events)
+        M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
+                               gemm_path=path, weight_layout=layout, events=events)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -213,12 +218,15 @@ def main():
         "data": "synthetic",
         "config": dict(cfg.describe(), touched_experts=int((counts_np > 0).sum()),
                        max_tokens_per_expert=int(counts_np.max()),
-                       touched_weight_bytes=int(total_bytes), gemm_path=args.path),
+                       touched_weight_bytes=int(total_bytes),
+                       gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
+                       weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows"),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm",
-                     "kernel": "gemv_gate_up_kernel (fused gate+up MXFP4 GEMV + SiLU*up)",
+                     "kernel": ("mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else
+                                "gemv_gate_up_kernel") + " (fused gate+up MXFP4 GEMM + SiLU*up)",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,

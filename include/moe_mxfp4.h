@@ -78,9 +78,13 @@ extern "C" {
 #define MOE_ACT_MXFP8 1      /* x and h encoded to MXFP8 E4M3 + E8M0 per 32 (prefill) */
 
 /* GEMM path selection (moe_mxfp4_options.gemm_path) */
-#define MOE_PATH_AUTO 0      /* per expert: GEMV for few tokens, MFMA for many */
-#define MOE_PATH_GEMV 1      /* force the VALU GEMV path for every expert */
-#define MOE_PATH_MFMA 2      /* force the bf16-MFMA path for every expert */
+#define MOE_PATH_AUTO 0      /* the path that reads the given weight layout */
+#define MOE_PATH_GEMV 1      /* VALU GEMV with DPP reductions (row-major weights) */
+#define MOE_PATH_MFMA 2      /* bf16 matrix cores (weights in the MFMA tile layout) */
+
+/* Weight layouts (moe_mxfp4_options.weight_layout) */
+#define MOE_LAYOUT_ROWS 0    /* row-major packed codes + scales, as described above */
+#define MOE_LAYOUT_TILES 1   /* the MFMA tile layout written by moe_mxfp4_prepack */
 
 /* The two E8M0 scale tensors (device pointers). */
 typedef struct moe_mxfp4_scales {
@@ -107,6 +111,10 @@ typedef struct moe_mxfp4_options {
      * first num_events (<= 4) are recorded; used to time the kernels. */
     void* const* events;
     int32_t num_events;
+    /* MOE_LAYOUT_ROWS (0, the default) or MOE_LAYOUT_TILES: the layout of
+     * W_gate_up, W_down and the scales.  ROWS runs the GEMV path, TILES the
+     * MFMA path; asking for the other path returns MOE_E_OPTION. */
+    int32_t weight_layout;
 } moe_mxfp4_options;
 
 /* Allocate the workspace on the current device for layers with at most
@@ -146,6 +154,23 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
  * and packed 16-byte aligned when cols is a multiple of 32 (always). */
 int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                        uint8_t* scales, void* stream);
+
+/* Rearrange num_matrices MXFP4 matrices [rows, cols] (packed [.., rows,
+ * cols/2], scales [.., rows, cols/32], row-major as above) into the MFMA
+ * tile layout that forward_ex reads with weight_layout = MOE_LAYOUT_TILES.
+ * Same byte counts: tiles holds rows*cols/2 and tile_scales rows*cols/32
+ * bytes per matrix.  Layout: each 64-row quad (four 16-row groups) and
+ * 128-column chunk (four MX blocks) becomes 4 KB of codes ordered
+ * [group][lane][16 bytes] (lane = r + 16 g: block g of row r) followed, in
+ * tile_scales, by 256 scale bytes ordered [lane][group].  gate_up_pairs != 0
+ * (for W_gate_up, rows = 2I) makes quad q hold gate rows 32q..32q+31 as
+ * groups 0, 1 and up rows I+32q..I+32q+31 as groups 2, 3; otherwise quad q
+ * holds rows 64q..64q+63.  rows % 64 == 0, cols % 128 == 0; packed and tiles
+ * 16-byte aligned, tile_scales 4-byte aligned.  A one-time step at weight
+ * load (not part of a forward call).  Enqueued on `stream`. */
+int moe_mxfp4_prepack(const uint8_t* packed, const uint8_t* scales, int64_t num_matrices,
+                      int64_t rows, int64_t cols, int32_t gate_up_pairs, uint8_t* tiles,
+                      uint8_t* tile_scales, void* stream);
 
 /* Static text of a status code; for MOE_E_HIP, the text of the last HIP
  * error seen by the calling thread. */

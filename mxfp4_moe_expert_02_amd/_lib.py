@@ -30,9 +30,12 @@ MOE_ACT_MXFP8 = 1
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_MFMA = 2
+MOE_LAYOUT_ROWS = 0
+MOE_LAYOUT_TILES = 1
 
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
+            "moe_mxfp4_prepack",
             "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy")
 
 
@@ -52,7 +55,7 @@ class moe_mxfp4_options(ctypes.Structure):
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("sorted", ctypes.c_void_p), ("x_codes", ctypes.c_void_p),
                 ("x_scales", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
-                ("num_events", ctypes.c_int32)]
+                ("num_events", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -79,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.moe_mxfp4_status_string.restype = ctypes.c_char_p
         L.moe_mxfp4_status_string.argtypes = [ctypes.c_int]
+        L.moe_mxfp4_prepack.restype = ctypes.c_int
+        L.moe_mxfp4_prepack.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
         L.moe_probe_stream_read.restype = ctypes.c_int
         L.moe_probe_stream_read.argtypes = [vp, i64, vp, vp]
         L.moe_probe_sink_words.restype = i64
@@ -132,8 +137,8 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                          stream=None, act_format: int = MOE_ACT_BF16,
                          gemm_path: int = MOE_PATH_AUTO, ids=None, weights=None,
                          counts=None, offsets=None, sorted=None, x_codes=None,
-                         x_scales=None, events=None, check: bool = True,
-                         validate: bool = True) -> int:
+                         x_scales=None, events=None, weight_layout: int = MOE_LAYOUT_ROWS,
+                         check: bool = True, validate: bool = True) -> int:
     """Enqueue one layer on ``stream`` (default: torch's current stream).
 
     x [T,H] bfloat16, router_logits [T,E] float32, W_gate_up [E,2I,H/2] uint8,
@@ -147,13 +152,15 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     if validate:
         T, H = x.shape
         E = router_logits.shape[1]
-        I2 = W_gate_up.shape[1]
         _expect(x, torch.bfloat16, (T, H), "x")
         _expect(router_logits, torch.float32, (T, E), "router_logits")
-        _expect(W_gate_up, torch.uint8, (E, I2, H // 2), "W_gate_up")
-        _expect(W_down, torch.uint8, (E, H, I2 // 4), "W_down")
-        _expect(scales[0], torch.uint8, (E, I2, H // 32), "scales[0]")
-        _expect(scales[1], torch.uint8, (E, H, I2 // 64), "scales[1]")
+        I2 = W_gate_up.numel() * 2 // (E * H)  # 2I from the byte count (both layouts)
+        for t, n, name in ((W_gate_up, E * I2 * H // 2, "W_gate_up"), (W_down, E * H * I2 // 4, "W_down"),
+                           (scales[0], E * I2 * H // 32, "scales[0]"),
+                           (scales[1], E * H * I2 // 64, "scales[1]")):
+            if t.dtype != torch.uint8 or t.numel() != n or not t.is_contiguous():
+                raise ValueError(f"{name}: expected {n} contiguous uint8 bytes, got "
+                                 f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
         _expect(out, torch.bfloat16, (T, H), "out")
     sc = moe_mxfp4_scales(_ptr(scales[0]), _ptr(scales[1])) if scales is not None else None
     ev_arr, n_ev = None, 0
@@ -168,7 +175,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     opt = moe_mxfp4_options(act_format, gemm_path, _ptr(ids), _ptr(weights), _ptr(counts),
                             _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
                             ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
-                            n_ev)
+                            n_ev, weight_layout)
     T = x.shape[0] if x is not None else 0
     rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,
@@ -190,6 +197,22 @@ def moe_mxfp4_forward(x, router_logits, top_k: int, W_gate_up, W_down, scales, o
     rc = lib().moe_mxfp4_forward(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                  _ptr(W_down), ctypes.byref(sc), _ptr(out), _stream(stream))
     return _check(rc, "moe_mxfp4_forward") if check else rc
+
+
+def moe_mxfp4_prepack(packed, scales, tiles, tile_scales, gate_up_pairs: bool,
+                      stream=None, check: bool = True) -> int:
+    """Rearrange row-major MXFP4 matrices packed [N, rows, cols/2] + scales
+    [N, rows, cols/32] into the MFMA tile layout (same byte sizes)."""
+    import torch
+    N, rows, half = packed.shape
+    cols = half * 2
+    _expect(scales, torch.uint8, (N, rows, cols // 32), "scales")
+    if tiles.numel() != packed.numel() or tile_scales.numel() != scales.numel():
+        raise ValueError("moe_mxfp4_prepack: output sizes must equal input sizes")
+    rc = lib().moe_mxfp4_prepack(_ptr(packed), _ptr(scales), N, rows, cols,
+                                 1 if gate_up_pairs else 0, _ptr(tiles), _ptr(tile_scales),
+                                 _stream(stream))
+    return _check(rc, "moe_mxfp4_prepack") if check else rc
 
 
 def moe_mxfp4_quantize(w, packed, scales, stream=None, check: bool = True) -> int:

@@ -149,6 +149,11 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     // context-free checks first
     if (num_tokens < 0) return MOE_E_SHAPE;
     if (o.act_format != MOE_ACT_BF16) return MOE_E_OPTION;  // MXFP8 path not built yet
+    if (o.weight_layout != MOE_LAYOUT_ROWS && o.weight_layout != MOE_LAYOUT_TILES)
+        return MOE_E_OPTION;
+    // the GEMV path reads row-major weights, the MFMA path the tile layout
+    if (o.gemm_path == MOE_PATH_GEMV && o.weight_layout != MOE_LAYOUT_ROWS) return MOE_E_OPTION;
+    if (o.gemm_path == MOE_PATH_MFMA && o.weight_layout != MOE_LAYOUT_TILES) return MOE_E_OPTION;
     if (o.gemm_path != MOE_PATH_AUTO && o.gemm_path != MOE_PATH_GEMV &&
         o.gemm_path != MOE_PATH_MFMA)
         return MOE_E_OPTION;
@@ -179,8 +184,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     hipError_t err;
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    // AUTO takes the matrix-core path for every expert
-    const int path = o.gemm_path == MOE_PATH_AUTO ? MOE_PATH_MFMA : o.gemm_path;
+    const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
     err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, st);
     if (err != hipSuccess) return hip_fail(err, "route");
     if ((err = mark(1)) != hipSuccess) return hip_fail(err, "hipEventRecord");

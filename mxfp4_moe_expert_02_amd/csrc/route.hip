@@ -147,40 +147,35 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
             ws.pos[s] = p;
         }
     }
-    // 5. active-expert lists.  GEMV path: ascending expert index (every
-    //    GEMV item costs about the same), compacted with a wave scan.
-    //    MFMA path: heaviest first (ties: lower index first) so the longest
-    //    items start earliest.
+    // 5. active-expert lists in ascending expert index, compacted with wave
+    //    scans: the GEMV list, and the MFMA list with its items (expert
+    //    slot, first token) of up to kMfmaTok tokens each.
     if (tid < kWave) {
-        int carry = 0;
+        int n_g = 0, n_m = 0, n_items = 0;
         for (int base = 0; base < E; base += kWave) {
             const int e = base + tid;
             const int c = (e < E) ? s_cnt[e] : 0;
             const bool g = c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens));
-            const int incl = wave_incl_scan(g ? 1 : 0);
-            if (g) ws.gemv_list[carry + incl - 1] = e;
-            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-        }
-        if (tid == 0) s_n[0] = carry;
-    }
-    for (int e = tid; e < E; e += nthr) {
-        const int c = s_cnt[e];
-        const bool m = c > 0 && !((path == 1) || (path == 0 && c <= gemv_max_tokens));
-        if (!m) continue;
-        int rank = 0, base = 0;  // base: items of the experts ranked before e
-        for (int f = 0; f < E; f++) {
-            const int cf = s_cnt[f];
-            const bool mf = cf > 0 && !((path == 1) || (path == 0 && cf <= gemv_max_tokens));
-            if (mf && (cf > c || (cf == c && f < e))) {
-                rank++;
-                base += (cf + kMfmaTok - 1) / kMfmaTok;
+            const bool m = c > 0 && !g;
+            const int groups = m ? (c + kMfmaTok - 1) / kMfmaTok : 0;
+            const int ig = wave_incl_scan(g ? 1 : 0);
+            const int im = wave_incl_scan(m ? 1 : 0);
+            const int ii = wave_incl_scan(groups);
+            if (g) ws.gemv_list[n_g + ig - 1] = e;
+            if (m) {
+                const int slot = n_m + im - 1, first = n_items + ii - groups;
+                ws.mfma_list[slot] = e;
+                for (int q = 0; q < groups; q++) ws.mfma_items[first + q] = make_int2(slot, q * kMfmaTok);
             }
+            n_g += __builtin_amdgcn_readlane(ig, kWave - 1);
+            n_m += __builtin_amdgcn_readlane(im, kWave - 1);
+            n_items += __builtin_amdgcn_readlane(ii, kWave - 1);
         }
-        ws.mfma_list[rank] = e;
-        const int groups = (c + kMfmaTok - 1) / kMfmaTok;
-        for (int g = 0; g < groups; g++) ws.mfma_items[base + g] = make_int2(rank, g * kMfmaTok);
-        atomicAdd(&s_n[1], 1);
-        atomicAdd(&s_n[2], groups);
+        if (tid == 0) {
+            s_n[0] = n_g;
+            s_n[1] = n_m;
+            s_n[2] = n_items;
+        }
     }
     __syncthreads();
     if (tid == 0) {

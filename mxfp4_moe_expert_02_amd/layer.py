@@ -26,10 +26,25 @@ class DeviceLayer:
     wdn: "torch.Tensor"      # [E, H, I/2] uint8
     sdn: "torch.Tensor"      # [E, H, I/32] uint8
     out: "torch.Tensor"      # [T, H] bfloat16
+    # the same weights in the MFMA tile layout (moe_mxfp4_prepack), or None
+    wgu_t: "torch.Tensor" = None
+    sgu_t: "torch.Tensor" = None
+    wdn_t: "torch.Tensor" = None
+    sdn_t: "torch.Tensor" = None
 
     @property
     def scales(self):
         return (self.sgu, self.sdn)
+
+    @property
+    def tile_scales(self):
+        return (self.sgu_t, self.sdn_t)
+
+    def weights(self, layout: int):
+        """(W_gate_up, W_down, scales) in the given layout."""
+        if layout == _lib.MOE_LAYOUT_TILES:
+            return self.wgu_t, self.wdn_t, self.tile_scales
+        return self.wgu, self.wdn, self.scales
 
     def expert_bytes(self) -> int:
         """Packed + scale bytes of one expert (both matrices)."""
@@ -38,7 +53,8 @@ class DeviceLayer:
 
 
 def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
-                x_bf16: np.ndarray | None = None, logits: np.ndarray | None = None) -> DeviceLayer:
+                x_bf16: np.ndarray | None = None, logits: np.ndarray | None = None,
+                tiles: bool = True) -> DeviceLayer:
     import torch
     dev = torch.device(device)
     T, E, H, I = cfg.T, cfg.E, cfg.H, cfg.I
@@ -59,5 +75,11 @@ def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
             _lib.moe_mxfp4_quantize(staging, wp[e], sp[e])
         del staging
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    layer = DeviceLayer(cfg, x, lt, wgu, sgu, wdn, sdn, out)
+    if tiles:
+        layer.wgu_t, layer.sgu_t = torch.empty_like(wgu), torch.empty_like(sgu)
+        layer.wdn_t, layer.sdn_t = torch.empty_like(wdn), torch.empty_like(sdn)
+        _lib.moe_mxfp4_prepack(wgu, sgu, layer.wgu_t, layer.sgu_t, gate_up_pairs=True)
+        _lib.moe_mxfp4_prepack(wdn, sdn, layer.wdn_t, layer.sdn_t, gate_up_pairs=False)
     torch.cuda.synchronize(dev)
-    return DeviceLayer(cfg, x, lt, wgu, sgu, wdn, sdn, out)
+    return layer

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward", "moe_mxfp4_forward_ex",
-        "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_probe_stream_read",
+        "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_mxfp4_prepack",
+        "moe_probe_stream_read",
         "moe_probe_sink_words", "moe_probe_copy"])
 
 
@@ -93,6 +94,14 @@ def test_forward_validation_without_gpu(L):
     assert _fwd(L, out=0x7002) == L.MOE_E_ALIGN
     assert _fwd(L, opt=L.moe_mxfp4_options(7, 0)) == L.MOE_E_OPTION
     assert _fwd(L, opt=L.moe_mxfp4_options(0, 9)) == L.MOE_E_OPTION
+    tiles_gemv = L.moe_mxfp4_options(0, L.MOE_PATH_GEMV)
+    tiles_gemv.weight_layout = L.MOE_LAYOUT_TILES
+    assert _fwd(L, opt=tiles_gemv) == L.MOE_E_OPTION      # GEMV reads row-major weights
+    rows_mfma = L.moe_mxfp4_options(0, L.MOE_PATH_MFMA)
+    assert _fwd(L, opt=rows_mfma) == L.MOE_E_OPTION       # MFMA reads the tile layout
+    bad_layout = L.moe_mxfp4_options(0, 0)
+    bad_layout.weight_layout = 5
+    assert _fwd(L, opt=bad_layout) == L.MOE_E_OPTION
     assert L.lib().moe_mxfp4_forward(0x1000, 0x2000, 9, 2, 0x3000, 0x4000, None, 0x7000,
                                      None) == L.MOE_E_NULL
 
@@ -104,6 +113,15 @@ def test_quantize_validation(L):
     assert q(0, 4, 64, 0x2000, 0x3000, None) == L.MOE_E_NULL
     assert q(0x1004, 4, 64, 0x2000, 0x3000, None) == L.MOE_E_ALIGN
     assert q(0x1000, 0, 64, 0x2000, 0x3000, None) == L.MOE_OK
+
+
+def test_prepack_validation(L):
+    p = L.lib().moe_mxfp4_prepack
+    assert p(0x1000, 0x2000, 2, 96, 256, 0, 0x3000, 0x4000, None) == L.MOE_E_SHAPE   # rows % 64
+    assert p(0x1000, 0x2000, 2, 128, 192, 0, 0x3000, 0x4000, None) == L.MOE_E_SHAPE  # cols % 128
+    assert p(0, 0x2000, 2, 128, 256, 0, 0x3000, 0x4000, None) == L.MOE_E_NULL
+    assert p(0x1008, 0x2000, 2, 128, 256, 0, 0x3000, 0x4000, None) == L.MOE_E_ALIGN
+    assert p(0x1000, 0x2000, 0, 128, 256, 0, 0x3000, 0x4000, None) == L.MOE_OK
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

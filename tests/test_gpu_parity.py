@@ -59,8 +59,10 @@ def run(M, layer, path=0, debug=False):
     layer.out.fill_(float("nan"))  # every element must be written by this call
     torch.cuda.synchronize()
     say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path}")
-    M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, layer.wgu, layer.wdn, layer.scales,
-                           layer.out, gemm_path=path, **dbg)
+    layout = M.MOE_LAYOUT_TILES if path == M.MOE_PATH_MFMA else M.MOE_LAYOUT_ROWS
+    wgu, wdn, scales = layer.weights(layout)
+    M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, wgu, wdn, scales, layer.out,
+                           gemm_path=path, weight_layout=layout, **dbg)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in dbg.items()}
 
@@ -127,6 +129,40 @@ def test_quantize_verify_workload_sample_bit_exact(torch_dev, M, oracle_lib):
         dp, ds = oracle_lib.quantize_mxfp4(make_weight_fp32(cfg, "down", e))
         assert np.array_equal(layer.wdn[e].cpu().numpy(), dp)
         assert np.array_equal(layer.sdn[e].cpu().numpy(), ds)
+
+
+def _tiles_reference(packed, scales, pairs):
+    """The MFMA tile layout written out with numpy indexing (host-side data
+    movement only): [quad][chunk][group][lane = r + 16 g][16 B] and scales
+    [quad][chunk][lane][group]."""
+    rows, half = packed.shape
+    cols = half * 2
+    Q, C = rows // 64, cols // 128
+    q, rg, r = np.meshgrid(np.arange(Q), np.arange(4), np.arange(16), indexing="ij")
+    if pairs:
+        row = np.where(rg < 2, 0, rows // 2) + 32 * q + 16 * (rg % 2) + r
+    else:
+        row = 64 * q + 16 * rg + r
+    blocks = packed.reshape(rows, cols // 32, 16)
+    t = np.empty((Q, C, 4, 64, 16), np.uint8)
+    ts = np.empty((Q, C, 64, 4), np.uint8)
+    for c in range(C):
+        for g in range(4):
+            t[:, c, :, g * 16:(g + 1) * 16, :] = blocks[row, 4 * c + g, :]
+            ts[:, c, g * 16:(g + 1) * 16, :] = scales[row, 4 * c + g].transpose(0, 2, 1)
+    return t.reshape(-1), ts.reshape(-1)
+
+
+@pytest.mark.parametrize("key", ["c1", "c2"])
+def test_prepack_tile_layout_bit_exact(torch_dev, M, key):
+    cfg = get_config(key)
+    layer = get_layer(cfg)
+    for e in (0, cfg.E - 1):
+        for wp, sp, wt, st, pairs in ((layer.wgu, layer.sgu, layer.wgu_t, layer.sgu_t, True),
+                                       (layer.wdn, layer.sdn, layer.wdn_t, layer.sdn_t, False)):
+            t, ts = _tiles_reference(wp[e].cpu().numpy(), sp[e].cpu().numpy(), pairs)
+            assert np.array_equal(wt[e].cpu().numpy().reshape(-1), t)
+            assert np.array_equal(st[e].cpu().numpy().reshape(-1), ts)
 
 
 # ---------------------------------------------------------------- routing
