@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the layer replayed from a captured HIP graph")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run one probe copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -159,6 +161,29 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
 
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(stream)
+        with torch.cuda.stream(s_cap):
+            step()  # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s_cap):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+
     # per-kernel times: the same K steps again with the library recording HIP
     # events on `stream` at its kernel boundaries
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
@@ -232,6 +257,8 @@ def main():
                      "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
     }
+    if graph_ms is not None:
+        result["graph_us_per_layer"] = round(graph_ms * 1e3, 2)
     if cold is not None:
         result["cold_us_per_layer"] = round(cold * 1e3, 2)
         result["cold_GBps"] = round(total_bytes / (cold * 1e-3) / 1e9, 2)

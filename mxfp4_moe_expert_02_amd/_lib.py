@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_mxfp4.so")
+# MOE_MXFP4_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("MOE_MXFP4_LIB") or os.path.join(HERE, "libmoe_mxfp4.so")
 
 MOE_OK = 0
 MOE_E_NULL = -1

@@ -30,29 +30,35 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, bdir: str, extra: list) -> str:
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str | None = None, defines: dict | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every .hip source and link the shared library (default: the
+    in-tree libmoe_mxfp4.so).  ``defines`` adds -D tuning constants."""
+    bdir = build_dir or BUILD
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
+    extra = [f"-D{k}={v}" for k, v in (defines or {}).items()]
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, bdir, extra), srcs))
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

@@ -36,8 +36,15 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_MFMA_CHUNKS_PER_STEP
+#define MOE_MFMA_CHUNKS_PER_STEP 2
+#endif
+#ifndef MOE_MFMA_WAVES_PER_EU
+#define MOE_MFMA_WAVES_PER_EU 2
+#endif
+
 constexpr int kWaves = kMfmaThreads / kWave;  // 4, split K
-constexpr int kChunksPerStep = 2;             // 128-column chunks per prefetch step
+constexpr int kChunksPerStep = MOE_MFMA_CHUNKS_PER_STEP;  // 128-column chunks per prefetch step
 constexpr int kGroups = 4;                    // 16-row groups per quad
 
 // E8M0 code as the fp32 scale operand of v_cvt_scalef32_* (the code in the
@@ -67,11 +74,14 @@ struct XStep {
 };
 
 // One wave: chunks [c_begin, c_end) of one quad against up to 16 tokens.
-// tiles/tscales point at the quad's chunk 0; xrow is this lane's token row
-// (bf16) or null for a zero column.
-__device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, const uint16_t* xrow,
+// tiles/tscales point at the quad's chunk 0; row_of() gives this lane's
+// token row (bf16) or null for a zero column, and is called only after the
+// first weight loads are in flight (it usually waits on an index load).
+template <typename RowFn>
+__device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowFn row_of,
                                  int c_begin, int c_end, f32x4_t (&acc)[kGroups]) {
     const int lane = threadIdx.x % kWave, g = lane / 16;
+    const uint16_t* xrow = nullptr;
 #pragma unroll
     for (int rg = 0; rg < kGroups; rg++) acc[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto load_w = [&](int c0, WStep& b) {
@@ -115,6 +125,7 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, c
     XStep xa;
     int c = c_begin;
     if (c < c_end) load_w(c, wa);
+    xrow = row_of();
     while (c < c_end) {
         const int n1 = c + kChunksPerStep;
         if (n1 < c_end) load_w(n1, wb);  // prefetch the next step's weights
@@ -156,30 +167,28 @@ __device__ inline void wave_chunk_range(int chunks, int& c_begin, int& c_end) {
 // gate_up: blockIdx.x = item * quads + quad; quad q = gate rows 32q..32q+31
 // (groups 0, 1) with up rows I+32q..I+32q+31 (groups 2, 3).
 __global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
 mfma_gate_up_kernel(GemmArgs a) {
     __shared__ f32x4_t red[(kWaves - 1) * kGroups * kWave];
     const int quads = a.I / 32;
     const int item = blockIdx.x / quads, quad = blockIdx.x % quads;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
-    const int2 it2 = a.items[item];
-    const int slot = uniform(it2.x), tok0 = uniform(it2.y);
-    const int e = uniform(a.list[slot]);
-    const int M = uniform(a.counts[e]), off = uniform(a.offsets[e]);
-    const int m = min(kMfmaTok, M - tok0);
+    const int4 it = a.items[item];
+    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int K = a.H, chunks = K / 128;
     const int64_t quad_id = (int64_t)e * quads + quad;
     const uint8_t* tiles = a.wgu + quad_id * chunks * 4096;
     const uint8_t* tsc = a.sgu + quad_id * chunks * 256;
-    const uint16_t* xrow = nullptr;
-    if (c < m) xrow = a.x + (int64_t)(a.sorted[off + tok0 + c] / a.k) * K;
     int cb, ce;
     wave_chunk_range(chunks, cb, ce);
     f32x4_t acc[kGroups];
-    mfma_quad(tiles, tsc, xrow, cb, ce, acc);
+    mfma_quad(tiles, tsc, [&]() -> const uint16_t* {
+        return c < m ? a.x + (int64_t)(a.sorted[row0 + c] / a.k) * K : nullptr;
+    }, cb, ce, acc);
     reduce_waves(acc, red);
     if (threadIdx.x < kWave && c < m) {
-        uint16_t* hrow = a.h + (int64_t)(off + tok0 + c) * a.I + 32 * quad + 4 * g;
+        uint16_t* hrow = a.h + (int64_t)(row0 + c) * a.I + 32 * quad + 4 * g;
 #pragma unroll
         for (int rg = 0; rg < 2; rg++) {
             ushort4 o;
@@ -192,33 +201,47 @@ mfma_gate_up_kernel(GemmArgs a) {
     }
 }
 
-// down: K = I is short, so no split-K: each wave of the block takes its own
-// quad (output rows 64q..64q+63) over the whole K; blockIdx.x = item *
-// ceil(quads / 4) + quad group.  A quad is also the combine tile: the wave
-// that completes a token's k experts on it combines it (the last finisher,
-// as in gemv.hip); everything after the weights is wave-local.
+// down: a workgroup takes two quads (output rows 64q..64q+63), each split
+// in two K halves over two waves; blockIdx.x = item * ceil(quads / 2) +
+// pair.  A quad is also the combine tile: the wave holding the summed
+// accumulator counts the tile done for its tokens, and the one that
+// completes a token's k experts combines it (the last finisher, as in
+// gemv.hip).  y moves through agent-coherent stores and loads.
 __global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
 mfma_down_kernel(GemmArgs a) {
-    const int quads = a.H / 64, qgroups = (quads + kWaves - 1) / kWaves;
-    const int item = blockIdx.x / qgroups;
-    const int quad = (blockIdx.x % qgroups) * kWaves + (int)(threadIdx.x / kWave);
-    if (item >= uniform(a.meta[kMetaNumMfmaItems]) || quad >= quads) return;
-    const int2 it2 = a.items[item];
-    const int slot = uniform(it2.x), tok0 = uniform(it2.y);
-    const int e = uniform(a.list[slot]);
-    const int M = uniform(a.counts[e]), off = uniform(a.offsets[e]);
-    const int m = min(kMfmaTok, M - tok0);
+    __shared__ f32x4_t red[2 * kGroups * kWave];
+    const int quads = a.H / 64, pairs = (quads + 1) / 2;
+    const int item = blockIdx.x / pairs;
+    const int w = threadIdx.x / kWave, half = w & 1;
+    const int quad = (blockIdx.x % pairs) * 2 + (w >> 1);
+    if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
+    const int4 it = a.items[item];
+    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int K = a.I, chunks = K / 128;
-    const int64_t quad_id = (int64_t)e * quads + quad;
-    const uint8_t* tiles = a.wdn + quad_id * chunks * 4096;
-    const uint8_t* tsc = a.sdn + quad_id * chunks * 256;
-    const uint16_t* xrow = (c < m) ? a.h + (int64_t)(off + tok0 + c) * K : nullptr;
+    const bool live = quad < quads;
     f32x4_t acc[kGroups];
-    mfma_quad(tiles, tsc, xrow, 0, chunks, acc);
+    if (live) {
+        const int64_t quad_id = (int64_t)e * quads + quad;
+        const uint8_t* tiles = a.wdn + quad_id * chunks * 4096;
+        const uint8_t* tsc = a.sdn + quad_id * chunks * 256;
+        const int hc = (chunks + 1) / 2;
+        mfma_quad(tiles, tsc, [&]() -> const uint16_t* {
+            return c < m ? a.h + (int64_t)(row0 + c) * K : nullptr;
+        }, half ? hc : 0, half ? chunks : hc, acc);
+        if (half) {
+#pragma unroll
+            for (int rg = 0; rg < kGroups; rg++) red[((w >> 1) * kGroups + rg) * kWave + lane] = acc[rg];
+        }
+    }
+    __syncthreads();
+    if (!live || half) return;
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++) acc[rg] += red[((w >> 1) * kGroups + rg) * kWave + lane];
     const int n0 = 64 * quad;
     if (c < m) {
-        float* dst = a.y + (int64_t)(off + tok0 + c) * a.H + n0 + 4 * g;
+        float* dst = a.y + (int64_t)(row0 + c) * a.H + n0 + 4 * g;
 #pragma unroll
         for (int rg = 0; rg < kGroups; rg++) {
             // agent-coherent stores: the combining wave may run on another XCD
@@ -237,7 +260,7 @@ mfma_down_kernel(GemmArgs a) {
     int token = -1;
     bool last = false;
     if (lane < m) {
-        token = a.sorted[off + tok0 + lane] / a.k;
+        token = a.sorted[row0 + lane] / a.k;
         last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
     }
     uint64_t todo = __ballot(last);
@@ -248,10 +271,10 @@ mfma_down_kernel(GemmArgs a) {
         // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
         float v = 0.f;
         for (int j = 0; j < a.k; j++) {
-            const float w = a.wts[(int64_t)t * a.k + j];
+            const float wt = a.wts[(int64_t)t * a.k + j];
             const int p = a.pos[(int64_t)t * a.k + j];
-            v = fmaf(w, __hip_atomic_load(a.y + (int64_t)p * a.H + n0 + lane, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT), v);
+            v = fmaf(wt, __hip_atomic_load(a.y + (int64_t)p * a.H + n0 + lane, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT), v);
         }
         a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(v);
     }
@@ -266,8 +289,8 @@ hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 }
 
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream) {
-    const int qgroups = (a.H / 64 + kWaves - 1) / kWaves;
-    mfma_down_kernel<<<max_items * qgroups, kMfmaThreads, 0, stream>>>(a);
+    const int pairs = (a.H / 64 + 1) / 2;
+    mfma_down_kernel<<<max_items * pairs, kMfmaThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

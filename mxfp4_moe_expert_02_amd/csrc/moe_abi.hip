@@ -52,7 +52,7 @@ size_t layout(Workspace* ws, char* base) {
     ws->pos = (int32_t*)take(S * 4);
     ws->gemv_list = (int32_t*)take(ws->E * 4);
     ws->mfma_list = (int32_t*)take(ws->E * 4);
-    ws->mfma_items = (int2*)take((ws->E + S / moe::kMfmaTok + 1) * sizeof(int2));
+    ws->mfma_items = (int4*)take((ws->E + S / moe::kMfmaTok + 1) * sizeof(int4));
     ws->meta = (int32_t*)take(moe::kMetaWords * 4);
     ws->col_tiles = (int)(ws->H / moe::kColTile);
     ws->tile_done = (int32_t*)take((size_t)ws->max_tokens * (ws->H / moe::kMfmaDownRows) * 4);

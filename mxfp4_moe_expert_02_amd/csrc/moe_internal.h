@@ -57,7 +57,7 @@ struct Workspace {
     int32_t* pos = nullptr;     // [Tmax*kmax]
     int32_t* gemv_list = nullptr;  // [E] active experts routed to the GEMV path
     int32_t* mfma_list = nullptr;  // [E] active experts routed to the MFMA path
-    int2* mfma_items = nullptr;    // [E + Tmax*kmax/kMfmaTok] (slot, first token) of MFMA items
+    int4* mfma_items = nullptr;    // [E + Tmax*kmax/kMfmaTok] MFMA items: (expert, first sorted row, tokens, 0)
     int32_t* meta = nullptr;       // [kMetaWords]
     int32_t* tile_done = nullptr;  // [Tmax * H/kMfmaDownRows] finished down tiles per (token, column tile)
     int col_tiles = 0;             // H / kColTile
@@ -83,7 +83,7 @@ struct GemmArgs {
     int T, H, I, k;
     // combine state
     int32_t* tile_done;         // [T * tiles] experts done per (token, column tile)
-    const int2* items;          // MFMA path: (slot, first token) per item
+    const int4* items;          // MFMA path: (expert, first sorted row, tokens, 0) per item
     const float* wts;           // [T*k] routing weights
     const int32_t* pos;         // [T*k] slot -> row of y
     uint16_t* out;              // [T, H] bf16

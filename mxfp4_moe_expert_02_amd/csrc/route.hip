@@ -148,8 +148,8 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
         }
     }
     // 5. active-expert lists in ascending expert index, compacted with wave
-    //    scans: the GEMV list, and the MFMA list with its items (expert
-    //    slot, first token) of up to kMfmaTok tokens each.
+    //    scans: the GEMV list, and the MFMA list with its items of up to
+    //    kMfmaTok tokens each: (expert, first row in sorted order, tokens).
     if (tid < kWave) {
         int n_g = 0, n_m = 0, n_items = 0;
         for (int base = 0; base < E; base += kWave) {
@@ -165,7 +165,9 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
             if (m) {
                 const int slot = n_m + im - 1, first = n_items + ii - groups;
                 ws.mfma_list[slot] = e;
-                for (int q = 0; q < groups; q++) ws.mfma_items[first + q] = make_int2(slot, q * kMfmaTok);
+                for (int q = 0; q < groups; q++)
+                    ws.mfma_items[first + q] =
+                        make_int4(e, s_off[e] + q * kMfmaTok, min(kMfmaTok, c - q * kMfmaTok), 0);
             }
             n_g += __builtin_amdgcn_readlane(ig, kWave - 1);
             n_m += __builtin_amdgcn_readlane(im, kWave - 1);
