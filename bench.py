@@ -61,6 +61,36 @@ def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:
     return gu, dn
 
 
+KERNEL_SOURCES = ["mxfp4_moe_expert_02_amd/csrc/mfma.hip", "mxfp4_moe_expert_02_amd/csrc/gemv.hip",
+                  "mxfp4_moe_expert_02_amd/csrc/device_common.h",
+                  "mxfp4_moe_expert_02_amd/csrc/moe_internal.h"]
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.txt
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated by a copy of known size),
+    or None if none was taken with the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = sources_sha256()
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and not line.startswith("#"):
+            w, k, sha, nbytes = parts
+            if w == workload and k == kernel and sha == digest:
+                return int(nbytes)
+    return None
+
+
 def probe_bandwidth(M, torch, nbytes: int = 4 << 30, reps: int = 20) -> float:
     """Achievable HBM read bandwidth: a plain 128-bit streaming read of
     ``nbytes`` (far above the 256 MiB Infinity Cache), GB/s."""
@@ -213,6 +243,7 @@ def main():
         cold = float(np.median(times))
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
+    kname = "mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else "gemv_gate_up_kernel"
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -250,10 +281,10 @@ def main():
         "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else
-                                "gemv_gate_up_kernel") + " (fused gate+up MXFP4 GEMM + SiLU*up)",
+                     "kernel": kname + " (fused gate+up MXFP4 GEMM + SiLU*up)",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, kname),
                      "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
     }
