@@ -94,16 +94,19 @@ static int nearest_code(double mag, const double* table, int max_code) {
 
 /* One MX block: scale X = 2^(floor(log2 amax) - emax_elem), the exponent
  * clamped to [-127, 127] so it fits E8M0; elements = nearest(v / X).
- * amax == 0 gives scale code 0 and all elements +0.  A non-finite amax gives
- * scale code 0xFF (NaN) and element codes 0. */
+ * amax == 0 gives scale code 0 and all elements +0.  A block holding any
+ * non-finite element (NaN or infinity, wherever it sits) gives scale code
+ * 0xFF (NaN) and element codes 0. */
 static void encode_block(const double* v, int n, int emax_elem, const double* table,
                          int max_code, int sign_bit, uint8_t* codes, uint8_t* scale) {
     double amax = 0.0;
+    int finite = 1;
     for (int i = 0; i < n; i++) {
         double a = fabs(v[i]);
-        if (!(a <= amax)) amax = a; /* also picks up NaN */
+        if (!isfinite(a)) finite = 0; /* NaN or infinity anywhere in the block */
+        else if (a > amax) amax = a;
     }
-    if (!isfinite(amax)) {
+    if (!finite) {
         *scale = 255;
         for (int i = 0; i < n; i++) codes[i] = 0;
         return;

@@ -202,3 +202,25 @@ def test_mxfp8_midpoint_ties_even(oracle_lib):
     assert scales[0, 0] == 127
     assert codes[0, 1] == 0x38 and codes[0, 2] == 0x3A and codes[0, 3] == 0xB8
     assert codes[0, 4] == 0x76
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
+@pytest.mark.parametrize("where", [0, 3, 17, 31])
+def test_non_finite_element_anywhere_makes_the_block_nan(oracle_lib, bad, where):
+    """A block holding a NaN or an infinity at any position encodes as scale
+    0xFF with element codes 0, whatever finite values follow it; the other
+    blocks of the row are encoded as if it were not there."""
+    rng = np.random.default_rng(where)
+    row = rng.standard_normal(96)
+    alone = row.copy()
+    row[32 + where] = bad
+    p4, s4 = oracle_lib.quantize_mxfp4(row[None, :].astype(np.float32))
+    a4, t4 = oracle_lib.quantize_mxfp4(alone[None, :].astype(np.float32))
+    assert s4[0, 1] == 255 and not p4[0, 16:32].any()
+    assert s4[0, 0] == t4[0, 0] and s4[0, 2] == t4[0, 2]
+    assert np.array_equal(p4[0, :16], a4[0, :16]) and np.array_equal(p4[0, 32:], a4[0, 32:])
+    c8, s8 = oracle_lib.quantize_mxfp8(row[None, :])
+    b8, t8 = oracle_lib.quantize_mxfp8(alone[None, :])
+    assert s8[0, 1] == 255 and not c8[0, 32:64].any()
+    assert s8[0, 0] == t8[0, 0] and s8[0, 2] == t8[0, 2]
+    assert np.array_equal(c8[0, :32], b8[0, :32]) and np.array_equal(c8[0, 64:], b8[0, 64:])
