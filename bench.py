@@ -12,7 +12,13 @@ inputs already resident in HBM.  Prints ONE JSON line:
   roofline = the dominant kernel (gate_up: 2/3 of the bytes) against the
              8 TB/s HBM peak, timed live with HIP events the library records
              between its kernels
-  cpu_baseline = the fp64 CPU oracle on the host cores, same workload
+  cpu_baseline = the fp64 CPU oracle on the host cores, same workload (every
+                 token up to 32 tokens; above that an evenly spaced sample
+                 of 32 tokens, the time scaled to the whole layer)
+
+--config c5 runs the prefill chunk (4096 tokens) with MXFP8 activations on
+the scaled FP4 x FP8 matrix cores; its roofline is the gate_up kernel's
+TFLOP/s against the dense FP8 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -29,6 +35,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0   # dense MFMA with an FP8 operand (the FP4 x FP8 instruction's rate)
+FP4_PEAK_TFLOPS = 10100.0  # dense MFMA, FP4 x FP4
+CPU_SAMPLE_TOKENS = 32
 METRIC = "MoE layer µs + achieved HBM GB/s (% peak) at 9-token verify step, 1 GPU"
 STAGES = ["route", "gate_up", "down_combine"]
 
@@ -38,7 +47,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c2", help="workload key c1..c4 (default: c2, 9-token verify)")
+    p.add_argument("--config", default="c2",
+                   help="workload key c1..c5 (default: c2, 9-token verify; c5: MXFP8 prefill)")
     p.add_argument("--path", type=int, default=0,
                    help="1: VALU GEMV over row-major weights; 2 (default): bf16 MFMA over "
                         "the tile layout (weights prepacked once before timing)")
@@ -62,6 +72,7 @@ def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:
 
 
 KERNEL_SOURCES = ["mxfp4_moe_expert_02_amd/csrc/mfma.hip", "mxfp4_moe_expert_02_amd/csrc/gemv.hip",
+                  "mxfp4_moe_expert_02_amd/csrc/mxfp8.hip",
                   "mxfp4_moe_expert_02_amd/csrc/device_common.h",
                   "mxfp4_moe_expert_02_amd/csrc/moe_internal.h"]
 
@@ -112,7 +123,10 @@ def probe_bandwidth(M, torch, nbytes: int = 4 << 30, reps: int = 20) -> float:
 
 
 def cpu_baseline(cfg, gbytes_total: float) -> dict:
-    """The oracle as it stands, on the host cores: the whole layer (all tokens)."""
+    """The oracle as it stands, on the host cores: the whole layer when it
+    has at most CPU_SAMPLE_TOKENS tokens, else that many evenly spaced
+    tokens with the time scaled by T / sample (the oracle's cost is per
+    token and per routed expert)."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     from workloads import make_logits, make_weight_fp32, make_x_bf16
@@ -120,7 +134,9 @@ def cpu_baseline(cfg, gbytes_total: float) -> dict:
     lg = make_logits(cfg)
     x = make_x_bf16(cfg)
     ids = oracle.route(lg, cfg.k)["ids"]
-    experts = sorted(set(int(e) for e in ids.ravel()))
+    n = min(cfg.T, CPU_SAMPLE_TOKENS)
+    tokens = np.unique(np.linspace(0, cfg.T - 1, n).round().astype(np.int32))
+    experts = sorted(set(int(e) for e in ids[tokens].ravel()))
 
     def prep(e):
         gp, gs = oracle.quantize_mxfp4(make_weight_fp32(cfg, "gate_up", e))
@@ -131,12 +147,15 @@ def cpu_baseline(cfg, gbytes_total: float) -> dict:
         weights = dict(ex.map(prep, experts))
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    oracle.forward(x, lg, cfg.k, cfg.H, cfg.I, weights)
-    dt = time.perf_counter() - t0
+    oracle.forward(x, lg, cfg.k, cfg.H, cfg.I, weights, tokens=tokens,
+                   act_mxfp8=cfg.act == "mxfp8")
+    dt = (time.perf_counter() - t0) * cfg.T / len(tokens)
+    what = (f"whole layer: all {cfg.T} tokens" if len(tokens) == cfg.T else
+            f"{len(tokens)} of {cfg.T} tokens evenly spaced, time scaled by {cfg.T}/{len(tokens)}")
     return {"value": round(gbytes_total / dt, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "us_per_layer": round(dt * 1e6, 1),
-            "sample": f"whole layer: all {cfg.T} tokens x top-{cfg.k} "
-                      f"({len(experts)} touched experts), fp64, OpenMP threads={cores}"}
+            "sample": f"{what} x top-{cfg.k} ({len(experts)} experts in the sample), fp64, "
+                      f"OpenMP threads={cores}"}
 
 
 def main():
@@ -152,8 +171,11 @@ def main():
     from workloads import get_config
 
     cfg = get_config(args.config)
-    if cfg.act != "bf16":
-        print("bench.py: the MXFP8 prefill workload is not wired into this bench", file=sys.stderr)
+    mx8 = cfg.act == "mxfp8"
+    act = M.MOE_ACT_MXFP8 if mx8 else M.MOE_ACT_BF16
+    if mx8 and args.path == M.MOE_PATH_GEMV:
+        print("bench.py: MXFP8 activations run on the matrix cores only (--path 0 or 2)",
+              file=sys.stderr)
         sys.exit(2)
     print(f"[bench] building {cfg.name}", file=sys.stderr, flush=True)
     layer = build_layer(cfg)
@@ -165,7 +187,7 @@ def main():
     wgu, wdn, scales = layer.weights(layout)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
-                           gemm_path=path, weight_layout=layout, counts=counts)
+                           gemm_path=path, weight_layout=layout, counts=counts, act_format=act)
     torch.cuda.synchronize()
     counts_np = counts.cpu().numpy()
     gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
@@ -173,7 +195,8 @@ def main():
 
     def step(events=None):
         M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
-                               gemm_path=path, weight_layout=layout, events=events)
+                               gemm_path=path, weight_layout=layout, events=events,
+                               act_format=act)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -243,7 +266,8 @@ def main():
         cold = float(np.median(times))
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
-    kname = "mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else "gemv_gate_up_kernel"
+    kname = ("mx8_gate_up_kernel" if mx8 else
+             "mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else "gemv_gate_up_kernel")
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -255,6 +279,27 @@ def main():
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     gu_ms = stage_ms["gate_up"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    S = cfg.T * cfg.k
+    gu_flops = 2.0 * S * 2 * cfg.I * cfg.H
+    dn_flops = 2.0 * S * cfg.H * cfg.I
+    if mx8:
+        gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma",
+                "kernel": kname + " (fused gate+up MXFP4 x MXFP8 scaled-MFMA GEMM + SiLU*up)",
+                "achieved": round(gu_tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_tf / FP8_PEAK_TFLOPS, 4),
+                "frac_of_fp4_peak": round(gu_tf / FP4_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(cfg.name, kname),
+                "algorithmic_flops_per_launch": gu_flops,
+                "algorithmic_bytes_per_launch": int(gu_bytes)}
+    else:
+        roof = {"bound": "hbm",
+                "kernel": kname + " (fused gate+up MXFP4 GEMM + SiLU*up)",
+                "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(cfg.name, kname),
+                "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
+                "algorithmic_bytes_per_launch": int(gu_bytes)}
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -270,23 +315,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4xbf16->f32",
+        "dtype": "mxfp4xmxfp8->f32" if mx8 else "mxfp4xbf16->f32",
         "data": "synthetic",
         "config": dict(cfg.describe(), touched_experts=int((counts_np > 0).sum()),
                        max_tokens_per_expert=int(counts_np.max()),
                        touched_weight_bytes=int(total_bytes),
                        gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
-                       weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows"),
+                       weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",
+                       activations="mxfp8" if mx8 else "bf16"),
+        "tflops": {"layer": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
+                   "gate_up": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
+                   "down_combine": round(dn_flops / (dn_ms * 1e-3) / 1e12, 2)},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "hbm",
-                     "kernel": kname + " (fused gate+up MXFP4 GEMM + SiLU*up)",
-                     "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name, kname),
-                     "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
-                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+        "roofline": roof,
     }
     if graph_ms is not None:
         result["graph_us_per_layer"] = round(graph_ms * 1e3, 2)

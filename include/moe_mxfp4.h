@@ -75,7 +75,9 @@ extern "C" {
 
 /* activation formats fed to the expert GEMMs */
 #define MOE_ACT_BF16 0       /* x and h in bf16 (verify token counts) */
-#define MOE_ACT_MXFP8 1      /* x and h encoded to MXFP8 E4M3 + E8M0 per 32 (prefill) */
+#define MOE_ACT_MXFP8 1      /* x and h encoded to MXFP8 E4M3 + E8M0 per 32 (prefill);
+                                requires MOE_LAYOUT_TILES and runs on the scaled
+                                FP4 x FP8 matrix cores (gemm_path AUTO or MFMA) */
 
 /* GEMM path selection (moe_mxfp4_options.gemm_path) */
 #define MOE_PATH_AUTO 0      /* the path that reads the given weight layout */
@@ -96,7 +98,10 @@ typedef struct moe_mxfp4_scales {
  * The optional outputs are device buffers the call fills (NULL to skip):
  * the routing result and, with MOE_ACT_MXFP8, the MXFP8 encoding of x. */
 typedef struct moe_mxfp4_options {
-    int32_t act_format;  /* MOE_ACT_BF16 or MOE_ACT_MXFP8 */
+    int32_t act_format;  /* MOE_ACT_BF16 or MOE_ACT_MXFP8 (E4M3 elements, ties to
+                            even, saturating; scale 2^(floor(log2 amax) - 8) per 32
+                            along K, the weights' rule with the E4M3 range: OCP MX
+                            specification) */
     int32_t gemm_path;   /* MOE_PATH_* */
     int32_t* ids;        /* [T, top_k] expert per slot, slot order (logit desc, index asc) */
     float* weights;      /* [T, top_k] renormalised softmax weights */
@@ -106,7 +111,8 @@ typedef struct moe_mxfp4_options {
     uint8_t* x_codes;    /* [T, H] E4M3 codes of x (MOE_ACT_MXFP8 only) */
     uint8_t* x_scales;   /* [T, H/32] E8M0 scales of x (MOE_ACT_MXFP8 only) */
     /* Optional hipEvent_t handles recorded on `stream` at the stage
-     * boundaries: [0] before routing, [1] after routing, [2] after the
+     * boundaries: [0] before routing, [1] after routing (and, with
+     * MOE_ACT_MXFP8, after the encoding of x), [2] after the
      * gate_up GEMM, [3] after the down GEMM and the combine.  Only the
      * first num_events (<= 4) are recorded; used to time the kernels. */
     void* const* events;

@@ -58,6 +58,10 @@ size_t layout(Workspace* ws, char* base) {
     ws->tile_done = (int32_t*)take((size_t)ws->max_tokens * (ws->H / moe::kMfmaDownRows) * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
+    ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
+    ws->x_scales = (uint8_t*)take((size_t)ws->max_tokens * (ws->H / 32));
+    ws->h_codes = (uint8_t*)take(S * ws->I);
+    ws->h_scales = (uint8_t*)take(S * (ws->I / 32));
     return off;
 }
 
@@ -148,7 +152,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     if (opt) o = *opt;
     // context-free checks first
     if (num_tokens < 0) return MOE_E_SHAPE;
-    if (o.act_format != MOE_ACT_BF16) return MOE_E_OPTION;  // MXFP8 path not built yet
+    if (o.act_format != MOE_ACT_BF16 && o.act_format != MOE_ACT_MXFP8) return MOE_E_OPTION;
     if (o.weight_layout != MOE_LAYOUT_ROWS && o.weight_layout != MOE_LAYOUT_TILES)
         return MOE_E_OPTION;
     // the GEMV path reads row-major weights, the MFMA path the tile layout
@@ -156,6 +160,10 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     if (o.gemm_path == MOE_PATH_MFMA && o.weight_layout != MOE_LAYOUT_TILES) return MOE_E_OPTION;
     if (o.gemm_path != MOE_PATH_AUTO && o.gemm_path != MOE_PATH_GEMV &&
         o.gemm_path != MOE_PATH_MFMA)
+        return MOE_E_OPTION;
+    // MXFP8 activations run on the scaled matrix cores over the tile layout
+    if (o.act_format == MOE_ACT_MXFP8 &&
+        (o.weight_layout != MOE_LAYOUT_TILES || o.gemm_path == MOE_PATH_GEMV))
         return MOE_E_OPTION;
     if (o.num_events < 0 || o.num_events > 4 || (o.num_events > 0 && !o.events))
         return MOE_E_OPTION;
@@ -185,7 +193,13 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
     const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
-    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, st);
+    const bool mx8 = o.act_format == MOE_ACT_MXFP8;
+    const int item_tok = mx8 ? moe::kMx8Tok : moe::kMfmaTok;
+    if (mx8) {  // x is encoded in the routing stage (events [0]..[1])
+        err = moe::launch_quantize_x_mxfp8((const uint16_t*)x, T, H, ws->x_codes, ws->x_scales, st);
+        if (err != hipSuccess) return hip_fail(err, "quantize x");
+    }
+    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, item_tok, st);
     if (err != hipSuccess) return hip_fail(err, "route");
     if ((err = mark(1)) != hipSuccess) return hip_fail(err, "hipEventRecord");
 
@@ -213,7 +227,18 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.pos = ws->pos;
     a.out = (uint16_t*)out;
     a.col_tiles = ws->col_tiles;
-    if (path == MOE_PATH_GEMV) {
+    a.xq = ws->x_codes;
+    a.xs = ws->x_scales;
+    a.hq = ws->h_codes;
+    a.hs = ws->h_scales;
+    if (mx8) {
+        const int max_items = max_active + S / moe::kMx8Tok + 1;
+        err = moe::launch_mx8_gate_up(a, max_items, st);
+        if (err != hipSuccess) return hip_fail(err, "gate_up");
+        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        err = moe::launch_mx8_down(a, max_items, st);
+        if (err != hipSuccess) return hip_fail(err, "down");
+    } else if (path == MOE_PATH_GEMV) {
         err = moe::launch_gemv_gate_up(a, max_active, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
@@ -240,6 +265,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         {o.ids, ws->ids, (size_t)S * 4},         {o.weights, ws->wts, (size_t)S * 4},
         {o.counts, ws->counts, (size_t)E * 4},   {o.offsets, ws->offsets, (size_t)(E + 1) * 4},
         {o.sorted, ws->sorted, (size_t)S * 4},
+        {mx8 ? o.x_codes : nullptr, ws->x_codes, (size_t)T * H},
+        {mx8 ? o.x_scales : nullptr, ws->x_scales, (size_t)T * (H / 32)},
     };
     for (auto& c : copies) {
         if (!c.dst) continue;

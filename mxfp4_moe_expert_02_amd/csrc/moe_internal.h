@@ -38,6 +38,9 @@ constexpr int kColTile = 2 * kDownUnits;
 // kMfmaDownRows output rows (also its combine tile width); the 4 waves of a
 // workgroup split K.
 constexpr int kMfmaTok = 16;
+// MXFP8 (prefill) path: items of up to kMx8Tok tokens (four 16-token MFMA
+// column tiles), weights in the same tile layout.
+constexpr int kMx8Tok = 64;
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaDownRows = 32;
 constexpr int kMfmaThreads = 256;
@@ -63,6 +66,10 @@ struct Workspace {
     int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
     float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order
+    uint8_t* x_codes = nullptr;   // [Tmax, H] E4M3 codes of x (MXFP8 path)
+    uint8_t* x_scales = nullptr;  // [Tmax, H/32] E8M0
+    uint8_t* h_codes = nullptr;   // [Tmax*kmax, I] E4M3 codes of h, rows in sorted order
+    uint8_t* h_scales = nullptr;  // [Tmax*kmax, I/32] E8M0
 };
 
 // Arguments common to the expert GEMM kernels.
@@ -84,6 +91,11 @@ struct GemmArgs {
     // combine state
     int32_t* tile_done;         // [T * tiles] experts done per (token, column tile)
     const int4* items;          // MFMA path: (expert, first sorted row, tokens, 0) per item
+    // MXFP8 path
+    const uint8_t* xq;          // [T, H] E4M3 codes of x
+    const uint8_t* xs;          // [T, H/32] E8M0 scales of x
+    uint8_t* hq;                // [T*k, I] E4M3 codes of h (sorted rows)
+    uint8_t* hs;                // [T*k, I/32] E8M0 scales of h
     const float* wts;           // [T*k] routing weights
     const int32_t* pos;         // [T*k] slot -> row of y
     uint16_t* out;              // [T, H] bf16
@@ -92,8 +104,9 @@ struct GemmArgs {
 
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch.
+// item_tok: tokens per MFMA item (kMfmaTok for bf16, kMx8Tok for MXFP8).
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
-                        int gemv_max_tokens, int path, hipStream_t stream);
+                        int gemv_max_tokens, int path, int item_tok, hipStream_t stream);
 // GEMV path: gate_up (+ SiLU * up -> h), then down (-> y) whose last
 // finisher per (token, column tile) also combines that tile of the output.
 // max_active bounds the number of routed experts (grids are sized by it).
@@ -103,6 +116,12 @@ hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t strea
 // max_items bounds their number.
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
+// MXFP8 (prefill) path: encode x per token along H, then the scaled
+// FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue).
+hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx8_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_mx8_down(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                                  uint8_t* scales, hipStream_t stream);
 

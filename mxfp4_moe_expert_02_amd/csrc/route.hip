@@ -96,7 +96,8 @@ __device__ void topk_tokens(const float* lg, int nt, int t0, int E, int k, int* 
 // s, in LDS or global memory), the active-expert lists, and the reset of
 // the combine counters.  One workgroup.
 __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Workspace& ws,
-                           int gemv_max_tokens, int path, int* hist, int* s_cnt, int* s_off) {
+                           int gemv_max_tokens, int path, int item_tok, int* hist, int* s_cnt,
+                           int* s_off) {
     __shared__ int s_n[3];
     const int tid = threadIdx.x, nthr = blockDim.x;
     // R ranges (power of two) of L consecutive slots: R ~ sqrt(S), R*E fits in LDS
@@ -157,7 +158,7 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
             const int c = (e < E) ? s_cnt[e] : 0;
             const bool g = c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens));
             const bool m = c > 0 && !g;
-            const int groups = m ? (c + kMfmaTok - 1) / kMfmaTok : 0;
+            const int groups = m ? (c + item_tok - 1) / item_tok : 0;
             const int ig = wave_incl_scan(g ? 1 : 0);
             const int im = wave_incl_scan(m ? 1 : 0);
             const int ii = wave_incl_scan(groups);
@@ -167,7 +168,7 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
                 ws.mfma_list[slot] = e;
                 for (int q = 0; q < groups; q++)
                     ws.mfma_items[first + q] =
-                        make_int4(e, s_off[e] + q * kMfmaTok, min(kMfmaTok, c - q * kMfmaTok), 0);
+                        make_int4(e, s_off[e] + q * item_tok, min(item_tok, c - q * item_tok), 0);
             }
             n_g += __builtin_amdgcn_readlane(ig, kWave - 1);
             n_m += __builtin_amdgcn_readlane(im, kWave - 1);
@@ -189,7 +190,7 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
 
 __global__ void __launch_bounds__(kRouteThreads)
 route_fused_kernel(const float* __restrict__ logits, int T, int E, int k, Workspace ws,
-                   int gemv_max_tokens, int path) {
+                   int gemv_max_tokens, int path, int item_tok) {
     __shared__ float lg[kFusedPairs];
     __shared__ int sel_id[kRouteThreads];
     __shared__ float sel_l[kRouteThreads];
@@ -201,7 +202,7 @@ route_fused_kernel(const float* __restrict__ logits, int T, int E, int k, Worksp
     topk_tokens(lg, T, 0, E, k, sel_id, sel_l, ws.ids, ws.wts);
     __syncthreads();
     // the ids of all T*k slots are still in LDS (sel_id), read them there
-    sort_slots(sel_id, T * k, E, T, ws, gemv_max_tokens, path, hist, s_cnt, s_off);
+    sort_slots(sel_id, T * k, E, T, ws, gemv_max_tokens, path, item_tok, hist, s_cnt, s_off);
 }
 
 // grid over token groups: each block ranks tokens [t0, t0 + nt)
@@ -220,20 +221,20 @@ route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int tok
 }
 
 __global__ void __launch_bounds__(kRouteThreads)
-route_sort_kernel(int T, int E, int k, Workspace ws, int gemv_max_tokens, int path) {
+route_sort_kernel(int T, int E, int k, Workspace ws, int gemv_max_tokens, int path, int item_tok) {
     __shared__ int hist[kSortLdsInts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
-    sort_slots(ws.ids, T * k, E, T, ws, gemv_max_tokens, path, hist, s_cnt, s_off);
+    sort_slots(ws.ids, T * k, E, T, ws, gemv_max_tokens, path, item_tok, hist, s_cnt, s_off);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
-                        int gemv_max_tokens, int path, hipStream_t stream) {
+                        int gemv_max_tokens, int path, int item_tok, hipStream_t stream) {
     if ((int64_t)T * E <= kFusedPairs && T * k <= kRouteThreads) {
         route_fused_kernel<<<1, kRouteThreads, 0, stream>>>(logits, T, E, k, ws,
-                                                            gemv_max_tokens, path);
+                                                            gemv_max_tokens, path, item_tok);
         return hipGetLastError();
     }
     const int tpb = E >= kTopkThreads ? 1 : kTopkThreads / E;
@@ -243,7 +244,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const Workspac
                                                              ws.wts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_sort_kernel<<<1, kRouteThreads, 0, stream>>>(T, E, k, ws, gemv_max_tokens, path);
+    route_sort_kernel<<<1, kRouteThreads, 0, stream>>>(T, E, k, ws, gemv_max_tokens, path,
+                                                       item_tok);
     return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ class DeviceLayer:
 
 def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
                 x_bf16: np.ndarray | None = None, logits: np.ndarray | None = None,
-                tiles: bool = True) -> DeviceLayer:
+                tiles: bool = True, weights_from: DeviceLayer | None = None) -> DeviceLayer:
+    """``weights_from``: a layer built from the same weight draws (same seed
+    and E, H, I) whose device weights are shared instead of rebuilt."""
     import torch
     dev = torch.device(device)
     T, E, H, I = cfg.T, cfg.E, cfg.H, cfg.I
@@ -62,6 +64,14 @@ def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
     lg = make_logits(cfg) if logits is None else logits
     x = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).to(dev)
     lt = torch.from_numpy(np.ascontiguousarray(lg, np.float32)).to(dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if weights_from is not None:
+        d = weights_from.cfg
+        if (d.seed, d.E, d.H, d.I) != (cfg.seed, E, H, I):
+            raise ValueError(f"{d.name} and {cfg.name} do not share weight draws")
+        src = weights_from
+        return DeviceLayer(cfg, x, lt, src.wgu, src.sgu, src.wdn, src.sdn, out,
+                           src.wgu_t, src.sgu_t, src.wdn_t, src.sdn_t)
     wgu = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
     sgu = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
     wdn = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
@@ -74,7 +84,6 @@ def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
             staging.copy_(torch.from_numpy(w))
             _lib.moe_mxfp4_quantize(staging, wp[e], sp[e])
         del staging
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     layer = DeviceLayer(cfg, x, lt, wgu, sgu, wdn, sdn, out)
     if tiles:
         layer.wgu_t, layer.sgu_t = torch.empty_like(wgu), torch.empty_like(sgu)

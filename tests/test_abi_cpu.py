@@ -99,6 +99,14 @@ def test_forward_validation_without_gpu(L):
     assert _fwd(L, opt=tiles_gemv) == L.MOE_E_OPTION      # GEMV reads row-major weights
     rows_mfma = L.moe_mxfp4_options(0, L.MOE_PATH_MFMA)
     assert _fwd(L, opt=rows_mfma) == L.MOE_E_OPTION       # MFMA reads the tile layout
+    mx8_rows = L.moe_mxfp4_options(L.MOE_ACT_MXFP8, 0)
+    assert _fwd(L, opt=mx8_rows) == L.MOE_E_OPTION        # MXFP8 runs on the tile layout
+    mx8_gemv = L.moe_mxfp4_options(L.MOE_ACT_MXFP8, L.MOE_PATH_GEMV)
+    mx8_gemv.weight_layout = L.MOE_LAYOUT_TILES
+    assert _fwd(L, opt=mx8_gemv) == L.MOE_E_OPTION        # ... on the matrix cores only
+    mx8 = L.moe_mxfp4_options(L.MOE_ACT_MXFP8, 0)
+    mx8.weight_layout = L.MOE_LAYOUT_TILES
+    assert _fwd(L, opt=mx8) == L.MOE_E_NOT_INIT          # a valid request
     bad_layout = L.moe_mxfp4_options(0, 0)
     bad_layout.weight_layout = 5
     assert _fwd(L, opt=bad_layout) == L.MOE_E_OPTION

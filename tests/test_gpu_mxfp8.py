@@ -1,0 +1,180 @@
+"""GPU parity of the prefill path (MXFP8 activations, scaled FP4 x FP8
+matrix cores) against the CPU oracle run with the same MXFP8 rule.
+
+* the MXFP8 encoding of x (E4M3 codes and E8M0 scales) bit-exact: both
+  sides start from the same bf16 values and the encoding is exact
+  arithmetic on them
+* routing bit-exact (the prefill path groups 64 tokens per work item)
+* layer output: max |out - ref| <= 2e-2 * rms(ref); h is encoded from fp32
+  on the GPU and from fp64 in the oracle, so a code of h may differ where
+  the value sits on a rounding boundary -- far below the bar
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_common import (bf16_tensor_to_f64, get_layer, oracle_experts, parity_ratio, run,
+                              say)
+from workloads import Config, get_config, make_logits, make_x_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+MX8 = 1  # MOE_ACT_MXFP8
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mxfp4_moe_expert_02_amd as M
+    assert M.MOE_ACT_MXFP8 == MX8
+    return M
+
+
+def _bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float32 values that are exact in bf16 -> their bf16 bit patterns."""
+    v = np.ascontiguousarray(v, np.float32)
+    bits = v.view(np.uint32)
+    assert not (bits & 0xFFFF).any(), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def _x_codes_ref(oracle_lib, x_bits: np.ndarray):
+    x = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return oracle_lib.quantize_mxfp8(x)
+
+
+def _parity(M, oracle_lib, cfg, layer, tokens, logits=None, x_bits=None):
+    dbg = run(M, layer, act=MX8, debug=True)
+    lg = make_logits(cfg) if logits is None else logits
+    xb = make_x_bf16(cfg) if x_bits is None else x_bits
+    route = oracle_lib.route(lg, cfg.k)
+    assert np.array_equal(dbg["ids"], route["ids"])
+    assert np.array_equal(dbg["sorted"], route["sorted"])
+    assert np.array_equal(dbg["offsets"], route["offsets"])
+    ex = oracle_experts(oracle_lib, cfg, route["ids"][tokens].ravel())
+    ref = oracle_lib.forward(xb, lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens, act_mxfp8=True)
+    full = bf16_tensor_to_f64(layer.out)
+    assert np.isfinite(full).all()  # every (token, column) was written
+    ratio = parity_ratio(full[tokens], ref)
+    say(f"mxfp8 parity {cfg.name} tokens={list(tokens)[:8]} max|d|/rms = {ratio:.3e}")
+    assert ratio <= TOL
+    return dbg
+
+
+def test_x_encoding_edge_blocks_bit_exact(torch_dev, M, oracle_lib):
+    """Blocks that exercise every branch of the E4M3 block encoding: ties to
+    the even code, saturation at 448, the subnormal range, scale clamping,
+    signed zeros, an all-zero block and a non-finite block."""
+    from mxfp4_moe_expert_02_amd.layer import build_layer
+    base = Config("mx8e", "mxfp8_edges_t6_e8_h256_i128_k2", 6, 8, 256, 128, 2, "normal",
+                  "mxfp8", 41)
+    rng = np.random.default_rng(3)
+    blk = rng.standard_normal((base.T, base.H // 32, 32)).astype(np.float32)
+    # amax 256 -> scale 2^0, so the elements are quantised as given
+    blk[0, 0] = [256.0, 1.0625, 1.1875, -1.0625, 3.0e-3, 2.0 ** -10, 3 * 2.0 ** -10, 300.0,
+                 -304.0, 0.0, -0.0, 2.0 ** -7, 2.0 ** -9, 7.5, 0.5, 0.625] + [1.0] * 16
+    blk[0, 1] = 0.0                                  # all-zero block: scale code 0
+    blk[0, 2] = -0.0
+    blk[0, 3, :] = 448.0 * 2.0 ** -3
+    blk[0, 3, 5] = 500.0 * 2.0 ** -3                 # saturates
+    blk[1, 0, :] = 2.0 ** -133                       # bf16 subnormal: scale clamps at 2^-127
+    blk[1, 1, :] = np.linspace(-3e38, 3e38, 32).astype(np.float32)
+    blk[1, 2, :] = np.float32(3.3895314e38)          # largest bf16
+    blk[2, 0, 7] = np.inf                            # non-finite block: scale 0xFF
+    blk[2, 1, 3] = np.nan
+    blk[3, :, :] = rng.integers(-16, 17, size=(base.H // 32, 32)) * 2.0 ** -4
+    xv = blk.reshape(base.T, base.H).astype(np.float32)
+    xv = (xv.view(np.uint32) & 0xFFFF0000).view(np.float32)   # make every value bf16-exact
+    bits = _bf16_bits(xv)
+    layer = build_layer(base, x_bf16=bits, weights_from=get_layer(base))
+    dbg = run(M, layer, act=MX8, debug=True)
+    codes, scales = _x_codes_ref(oracle_lib, bits)
+    assert np.array_equal(dbg["x_scales"], scales)
+    assert np.array_equal(dbg["x_codes"], codes)
+
+
+def test_x_encoding_prefill_rows_bit_exact(torch_dev, M, oracle_lib):
+    cfg = get_config("c5")
+    dbg = run(M, get_layer(cfg), act=MX8, debug=True)
+    xb = make_x_bf16(cfg)
+    for rows in (slice(0, 128), slice(cfg.T - 128, cfg.T)):
+        codes, scales = _x_codes_ref(oracle_lib, xb[rows])
+        assert np.array_equal(dbg["x_codes"][rows], codes)
+        assert np.array_equal(dbg["x_scales"][rows], scales)
+
+
+def test_mxfp8_forward_tiny_all_tokens(torch_dev, M, oracle_lib):
+    cfg = get_config("c1")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(cfg.T)))
+
+
+@pytest.mark.parametrize("T,k", [(1, 1), (1, 8), (2, 5)])
+def test_mxfp8_forward_small_edges(torch_dev, M, oracle_lib, T, k):
+    cfg = Config("edge", f"edge_t{T}_e8_h256_i128_k{k}", T, 8, 256, 128, k, "normal", "bf16", 21 + T)
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(T)))
+
+
+def test_mxfp8_forward_one_hot_expert_ragged_items(torch_dev, M, oracle_lib):
+    """150 tokens all pick expert 3 first: its items hold 64, 64 and 22
+    tokens; the other experts get ragged small items."""
+    cfg = Config("hot8", "hot_t150_e8_h384_i256_k3", 150, 8, 384, 256, 3, "normal", "mxfp8", 13)
+    logits = make_logits(cfg)
+    logits[:, 3] += 100.0
+    layer = get_layer(cfg, logits=logits)
+    _parity(M, oracle_lib, cfg, layer, list(range(0, cfg.T, 7)) + [cfg.T - 1], logits=logits)
+
+
+def test_mxfp8_forward_batched_shape_sampled(torch_dev, M, oracle_lib):
+    """72 tokens over 128 experts at the full hidden sizes (mostly 1-10
+    token items) with MXFP8 activations."""
+    cfg = get_config("c3")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71])
+
+
+def test_mxfp8_forward_prefill_sampled(torch_dev, M, oracle_lib):
+    cfg = get_config("c5")
+    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 1, 2047, 4095])
+
+
+def test_mxfp8_forward_deterministic(torch_dev, M):
+    cfg = get_config("c5")
+    layer = get_layer(cfg)
+    run(M, layer, act=MX8)
+    a = layer.out.clone()
+    run(M, layer, act=MX8)
+    assert torch_dev.equal(a.view(torch_dev.int16), layer.out.view(torch_dev.int16))
+
+
+def test_mxfp8_untouched_experts_are_not_read(torch_dev, M):
+    import torch
+    cfg = Config("pois8", "poison_t70_e16_h256_i128_k2", 70, 16, 256, 128, 2, "normal", "mxfp8", 31)
+    logits = make_logits(cfg)
+    logits[:, 10:] -= 100.0
+    layer = get_layer(cfg, logits=logits)
+    run(M, layer, act=MX8)
+    base = layer.out.clone()
+    saved = [s.clone() for s in (layer.sgu_t, layer.sdn_t)]
+    layer.sgu_t[10:] = 255
+    layer.sdn_t[10:] = 255
+    run(M, layer, act=MX8)
+    assert torch.isfinite(layer.out.float()).all()
+    assert torch.equal(base.view(torch.int16), layer.out.view(torch.int16))
+    for s, v in zip((layer.sgu_t, layer.sdn_t), saved):
+        s.copy_(v)
+
+
+def test_mxfp8_needs_tile_layout(torch_dev, M):
+    cfg = get_config("c1")
+    layer = get_layer(cfg)
+    M.moe_mxfp4_init(cfg.T, cfg.E, cfg.H, cfg.I, cfg.k)
+    rc = M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, layer.wgu, layer.wdn, layer.scales,
+                                layer.out, act_format=MX8, weight_layout=M.MOE_LAYOUT_ROWS,
+                                check=False)
+    assert rc == M.MOE_E_OPTION

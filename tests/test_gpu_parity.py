@@ -10,7 +10,8 @@
 import numpy as np
 import pytest
 
-from tests.gpu_common import bf16_tensor_to_f64, oracle_experts, parity_ratio, say
+from tests.gpu_common import (bf16_tensor_to_f64, get_layer, oracle_experts, parity_ratio, run,
+                              say)
 from workloads import Config, get_config, make_logits, make_weight_fp32, make_x_bf16
 
 pytestmark = pytest.mark.gpu
@@ -30,41 +31,6 @@ def torch_dev():
 def M():
     import mxfp4_moe_expert_02_amd as M
     return M
-
-
-_layers = {}
-
-
-def get_layer(cfg: Config, logits=None):
-    from mxfp4_moe_expert_02_amd.layer import build_layer
-    key = (cfg, None if logits is None else logits.tobytes())
-    if key not in _layers:
-        say(f"building layer {cfg.name} seed {cfg.seed}")
-        _layers[key] = build_layer(cfg, logits=logits)
-    return _layers[key]
-
-
-def run(M, layer, path=0, debug=False):
-    import torch
-    c = layer.cfg
-    M.moe_mxfp4_init(c.T, c.E, c.H, c.I, c.k)
-    dbg = {}
-    if debug:
-        S = c.T * c.k
-        dbg = dict(ids=torch.empty((c.T, c.k), dtype=torch.int32, device="cuda"),
-                   weights=torch.empty((c.T, c.k), dtype=torch.float32, device="cuda"),
-                   counts=torch.empty(c.E, dtype=torch.int32, device="cuda"),
-                   offsets=torch.empty(c.E + 1, dtype=torch.int32, device="cuda"),
-                   sorted=torch.empty(S, dtype=torch.int32, device="cuda"))
-    layer.out.fill_(float("nan"))  # every element must be written by this call
-    torch.cuda.synchronize()
-    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path}")
-    layout = M.MOE_LAYOUT_TILES if path == M.MOE_PATH_MFMA else M.MOE_LAYOUT_ROWS
-    wgu, wdn, scales = layer.weights(layout)
-    M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, wgu, wdn, scales, layer.out,
-                           gemm_path=path, weight_layout=layout, **dbg)
-    torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in dbg.items()}
 
 
 def test_loads_in_tree_library(torch_dev, M):
@@ -101,6 +67,8 @@ def test_quantize_edge_blocks_bit_exact(torch_dev, M, oracle_lib):
     w[5, :32] = np.float32(2.0 ** -130)       # scale clamps at 2^-127
     w[6, :32] = np.nan
     w[6, 40] = np.inf
+    w[7, 3] = np.nan                          # NaN mid-block, finite values after it
+    w[7, 40] = -np.inf
     p, s = _gpu_quantize(M, w)
     po, so = oracle_lib.quantize_mxfp4(w)
     assert np.array_equal(s, so)
@@ -298,14 +266,15 @@ def test_untouched_experts_are_not_read(torch_dev, M, path):
     layer = get_layer(cfg, logits=logits)
     run(M, layer, path=path)
     base = layer.out.clone()
-    sgu, sdn = layer.sgu.clone(), layer.sdn.clone()
-    layer.sgu[10:] = 255
-    layer.sdn[10:] = 255
+    scale_sets = (layer.sgu, layer.sdn, layer.sgu_t, layer.sdn_t)  # both layouts
+    saved = [s.clone() for s in scale_sets]
+    for s in scale_sets:
+        s[10:] = 255
     run(M, layer, path=path)
     assert torch.isfinite(layer.out.float()).all()
     assert torch.equal(base.view(torch.int16), layer.out.view(torch.int16))
-    layer.sgu.copy_(sgu)
-    layer.sdn.copy_(sdn)
+    for s, v in zip(scale_sets, saved):
+        s.copy_(v)
 
 
 def test_synchronous_errors_leave_out_untouched(torch_dev, M):
