@@ -36,22 +36,39 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// out[t, n0 .. n0+width) = sum_j w[t,j] * y[pos[t,j], ...] summed in slot
-// order j = 0..k-1 in fp32, rounded to bf16.  y is read with agent-coherent
-// loads because other workgroups of the running kernel wrote it.
-__device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width) {
-    for (int c = threadIdx.x; c < width; c += blockDim.x) {
-        const int n = n0 + c;
-        float acc = 0.f;
-        for (int j = 0; j < a.k; j++) {
-            const float w = a.wts[(int64_t)t * a.k + j];
-            const int p = a.pos[(int64_t)t * a.k + j];
-            const float v = __hip_atomic_load(a.y + (int64_t)p * a.H + n, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-            acc = fmaf(w, v, acc);
+// sum_j w[t,j] * y[pos[t,j], n] over the k slots of token t, in slot order
+// j = 0..k-1, fp32.  y is read with agent-coherent loads because other
+// workgroups of the running kernel wrote it.  The slot indices and weights,
+// then the y values, are fetched 8 slots at a time with unconditional loads
+// (indices clamped to k-1), so each batch costs two memory latencies rather
+// than two per slot.
+__device__ inline float combine_column(const GemmArgs& a, int t, int n) {
+    const int64_t base = (int64_t)t * a.k;
+    float v = 0.f;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        int p[8];
+        float w[8], yv[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int j = min(j0 + u, a.k - 1);
+            p[u] = a.pos[base + j];
+            w[u] = a.wts[base + j];
         }
-        a.out[(int64_t)t * a.H + n] = f32_to_bf16_rne(acc);
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            yv[u] = __hip_atomic_load(a.y + (int64_t)p[u] * a.H + n, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (j0 + u < a.k) v = fmaf(w[u], yv[u], v);
     }
+    return v;
+}
+
+// out[t, n0 .. n0+width) rounded to bf16, one column per thread of the block
+__device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width) {
+    for (int c = threadIdx.x; c < width; c += blockDim.x)
+        a.out[(int64_t)t * a.H + n0 + c] = f32_to_bf16_rne(combine_column(a, t, n0 + c));
 }
 
 }  // namespace moe

@@ -269,14 +269,7 @@ mfma_down_kernel(GemmArgs a) {
         todo &= todo - 1;
         const int t = __builtin_amdgcn_readlane(token, src);
         // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-        float v = 0.f;
-        for (int j = 0; j < a.k; j++) {
-            const float wt = a.wts[(int64_t)t * a.k + j];
-            const int p = a.pos[(int64_t)t * a.k + j];
-            v = fmaf(wt, __hip_atomic_load(a.y + (int64_t)p * a.H + n0 + lane, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT), v);
-        }
-        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(v);
+        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
     }
 }
 

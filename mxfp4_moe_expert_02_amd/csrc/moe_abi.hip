@@ -56,6 +56,7 @@ size_t layout(Workspace* ws, char* base) {
     ws->meta = (int32_t*)take(moe::kMetaWords * 4);
     ws->col_tiles = (int)(ws->H / moe::kColTile);
     ws->tile_done = (int32_t*)take((size_t)ws->max_tokens * (ws->H / moe::kMfmaDownRows) * 4);
+    ws->bhist = (int32_t*)take((S + moe::kRouteSlotBlock - 1) / moe::kRouteSlotBlock * ws->E * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);

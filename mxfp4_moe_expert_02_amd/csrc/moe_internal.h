@@ -20,6 +20,7 @@ constexpr int kGateUpUnits = 32;
 constexpr int kDownUnits = 64;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
+constexpr int kRouteSlotBlock = 256;  // slots per block of the multi-block routing sort
 
 // meta[] words in the workspace
 enum Meta : int {
@@ -38,9 +39,9 @@ constexpr int kColTile = 2 * kDownUnits;
 // kMfmaDownRows output rows (also its combine tile width); the 4 waves of a
 // workgroup split K.
 constexpr int kMfmaTok = 16;
-// MXFP8 (prefill) path: items of up to kMx8Tok tokens (four 16-token MFMA
+// MXFP8 (prefill) path: items of up to kMx8Tok tokens (eight 16-token MFMA
 // column tiles), weights in the same tile layout.
-constexpr int kMx8Tok = 64;
+constexpr int kMx8Tok = 128;
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaDownRows = 32;
 constexpr int kMfmaThreads = 256;
@@ -63,6 +64,7 @@ struct Workspace {
     int4* mfma_items = nullptr;    // [E + Tmax*kmax/kMfmaTok] MFMA items: (expert, first sorted row, tokens, 0)
     int32_t* meta = nullptr;       // [kMetaWords]
     int32_t* tile_done = nullptr;  // [Tmax * H/kMfmaDownRows] finished down tiles per (token, column tile)
+    int32_t* bhist = nullptr;      // [ceil(Tmax*kmax/kRouteSlotBlock) * E] per-block expert histograms
     int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
     float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order

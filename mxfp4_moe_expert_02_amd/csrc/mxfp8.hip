@@ -4,13 +4,13 @@
 // At a prefill chunk every expert sees hundreds of tokens and the layer is
 // compute-bound, so the activations are encoded too: x per token along H and
 // h per assignment along I, each block of 32 as E4M3 elements with one E8M0
-// scale (the same block rule as the weights, with the E4M3 element range),
-// and both GEMMs run on v_mfma_scale_f32_16x16x128_f8f6f4 with the FP4
-// weights as operand A and the FP8 activations as operand B; the hardware
-// applies both block scales.  The weights are the MXFP4 format the pages
-// give the experts (bjdmk.com.cn news page, co-design section); the pages
-// keep everything else at 8-bit or higher precision (tilert.ai blog, second
-// leap), which is what MXFP8 activations are.
+// scale (the weights' block rule with the E4M3 element range), and both
+// GEMMs run on v_mfma_scale_f32_16x16x128_f8f6f4 with the FP4 weights as
+// operand A and the FP8 activations as operand B; the hardware applies both
+// block scales.  The weights are the MXFP4 format the pages give the experts
+// (bjdmk.com.cn news page, co-design section); the pages keep everything
+// else at 8-bit or higher precision (tilert.ai blog, second leap), which is
+// what MXFP8 activations are.
 //
 // Operands of one 16x16x128 MFMA (lane l = (r, g) = (l % 16, l / 16)):
 //   A (FP4) = 16 weight rows x 128 k: lane (r, g) holds MX block g of row r,
@@ -22,8 +22,18 @@
 //     (the hardware pairs B's k with A's block layout this way; measured
 //     with one-hot operands on gfx950).
 //   D = 16 rows x 16 tokens; lane (c, g) holds rows 4g..4g+3 of token c.
-// A workgroup covers one 64-row quad (wave w = group w) against up to 64
-// tokens (four 16-token column tiles) over the whole K.
+//
+// Tiling: a workgroup computes 128 weight rows (two 64-row quads of the tile
+// layout) against one item of up to 128 tokens, over the whole K.  Its four
+// waves form a 2 x 2 grid: wave (wr, wt) owns quad wr and the token tiles
+// wt, wt+2, wt+4, wt+6 of 16 tokens (4 row groups x 4 column tiles = 16
+// MFMAs per 128-k chunk).
+// A comes straight from global memory in operand order (one 1 KB wave load
+// per row group); B, shared by the two waves of a token half, is staged per
+// chunk through double-buffered LDS (rows padded to 144 bytes so that the
+// 16-byte operand reads of a quarter-wave hit distinct banks).  The token
+// rows of x are gathered through the routing order; h rows are already in
+// that order.
 #include "device_common.h"
 
 namespace moe {
@@ -31,8 +41,19 @@ namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kMx8Threads = 256;
-constexpr int kTiles = kMx8Tok / 16;  // 4 column tiles
+#ifndef MOE_PF_SCHED_BARRIERS
+#define MOE_PF_SCHED_BARRIERS 0
+#endif
+#ifndef MOE_PF_WAVES_PER_EU
+#define MOE_PF_WAVES_PER_EU 2
+#endif
+
+constexpr int kPfThreads = 256;
+constexpr int kPfTiles = 4;               // 16-token column tiles per wave
+constexpr int kBRow = 144;                // LDS bytes per staged token row
+constexpr int kStageRows = kMx8Tok / 32;  // token rows staged per thread (4)
+
+static_assert(kMx8Tok == 128, "the prefill tiling assumes 128-token items");
 
 // nearest E4M3 (OCP FN) magnitude code of a >= 0: ties to the even code,
 // saturating at 448 (code 126); subnormals below 2^-6 in steps of 2^-9
@@ -52,40 +73,26 @@ __device__ inline int floor_log2_bits(uint32_t bits) {
     return (31 - __clz((int)(bits & 0x7fffffu))) - 149;
 }
 
-// MXFP8 encoding of one block of 32 values: scale 2^(floor(log2 amax) - 8)
-// (exponent clamped to [-127, 127]; amax == 0 -> code 0), elements RNE to
-// E4M3 with saturation; a non-finite value gives scale 0xFF and codes 0.
-__device__ inline void encode_block_mxfp8(const float (&v)[32], uint32_t (&codes)[8], uint8_t& scale) {
-    uint32_t amax_bits = 0;
-    bool finite = true;
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-        const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
-        finite = finite && b < 0x7f800000u;
-        amax_bits = b > amax_bits ? b : amax_bits;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) codes[i] = 0;
-    if (!finite) {
-        scale = 255;
-        return;
-    }
-    int se = amax_bits == 0 ? -127 : floor_log2_bits(amax_bits) - 8;
-    se = se < -127 ? -127 : (se > 127 ? 127 : se);
-    scale = (uint8_t)(se + 127);
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-        const float q = ldexpf(v[i], -se);  // exact: a power-of-two scaling
-        const uint32_t c = e4m3_mag_code(fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
-        codes[i / 4] |= c << (8 * (i % 4));
-    }
+// Block scale exponent of the MXFP8 rule from the block's largest |v| as
+// float bits: floor(log2 amax) - 8, clamped to [-127, 127]; amax == 0 gives
+// -127.  amax_bits >= 0x7f800000 (a NaN or an infinity in the block) is the
+// caller's case: scale 0xFF, codes 0.
+__device__ inline int mxfp8_scale_exp(uint32_t amax_bits) {
+    const int se = amax_bits == 0 ? -127 : floor_log2_bits(amax_bits) - 8;
+    return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// E4M3 code (sign included) of v / 2^se
+__device__ inline uint32_t e4m3_code(float v, int se) {
+    const float q = ldexpf(v, -se);  // exact: a power-of-two scaling
+    return e4m3_mag_code(fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
 }
 
 constexpr int kQuantThreads = 256;
 
-// one thread per block of 32 elements of x
+// MXFP8 encoding of x: one thread per block of 32 elements
 __global__ void __launch_bounds__(kQuantThreads)
-quantize_x_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int H,
+quantize_x_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
     if (b >= nblocks) return;
@@ -101,204 +108,302 @@ quantize_x_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int H,
             v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
         }
     }
-    uint32_t c[8];
-    uint8_t s;
-    encode_block_mxfp8(v, c, s);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        const uint32_t m = __float_as_uint(v[i]) & 0x7fffffffu;
+        amax = m > amax ? m : amax;  // NaN bits order above every finite value
+    }
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint8_t s = 255;
+    if (amax < 0x7f800000u) {
+        const int se = mxfp8_scale_exp(amax);
+        s = (uint8_t)(se + 127);
+#pragma unroll
+        for (int i = 0; i < 32; i++) c[i / 4] |= e4m3_code(v[i], se) << (8 * (i % 4));
+    }
     uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
     dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
     dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
     scales[b] = s;
-    (void)H;
 }
 
-// Operand B of one column tile for chunk `chunk`: codes k = 16g..16g+15 and
-// 64+16g..64+16g+15 of the chunk and the scale of block 4*chunk+g of this
-// lane's token row (zero column if null).
-struct BOperand {
-    i32x8_t v;
-    int scale;
+struct PfSmem {
+    alignas(16) uint8_t b[2][kMx8Tok * kBRow];  // staged B codes, [buffer][token][144]
+    // staged B scales: the chunk's 4 blocks per token in [0, 128); every
+    // thread stores one word, threads 128..255 into the unused upper half
+    alignas(16) uint32_t bs[2][kPfThreads];
 };
 
-__device__ inline BOperand load_b(const uint8_t* row, const uint8_t* srow, int chunk, int g) {
-    BOperand b;
-    if (row) {
-        const uint4* p = reinterpret_cast<const uint4*>(row + chunk * 128 + 16 * g);
-        const uint4 lo = p[0], hi = p[4];
-        b.v = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        b.scale = srow[4 * chunk + g];
-    } else {
-        b.v = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        b.scale = 127;
-    }
-    return b;
+// The B rows this thread stages: codes of token rows 32q + tid/8 (piece
+// tid % 8 of each 128-byte chunk) and the scales of token row tid (threads
+// >= 128 load row m-1 again).  Rows past the item's m tokens repeat row
+// m-1: they only feed
+// output columns that are never stored, and keeping every load
+// unconditional lets the loads of the next chunk stay in flight across the
+// MFMAs of the current one.
+struct StageSrc {
+    const uint8_t* row[kStageRows];
+    const uint8_t* srow;
+};
+
+struct StageRegs {
+    uint4 v[kStageRows];
+    uint32_t s;
+};
+
+__device__ __attribute__((always_inline)) inline void stage_load(const StageSrc& src, int chunk, StageRegs& r) {
+#pragma unroll
+    for (int q = 0; q < kStageRows; q++)
+        r.v[q] = *reinterpret_cast<const uint4*>(src.row[q] + chunk * 128);
+    r.s = *reinterpret_cast<const uint32_t*>(src.srow + chunk * 4);
 }
 
-// One wave: group w of a quad over all chunks against up to kTiles token
-// tiles.  rows[t] / srows[t]: this lane's token row (codes, scales) in
-// column tile t, or null.
-__device__ inline void mx8_group(const uint8_t* tiles, const uint8_t* tscales, int w,
-                                 const uint8_t* const (&rows)[kTiles],
-                                 const uint8_t* const (&srows)[kTiles], int chunks,
-                                 f32x4_t (&acc)[kTiles]) {
-    const int lane = threadIdx.x % kWave, g = lane / 16;
+__device__ __attribute__((always_inline)) inline void stage_store(PfSmem& sm, int buf, const StageRegs& r) {
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int t = 0; t < kTiles; t++) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 wa = make_uint4(0, 0, 0, 0);
-    uint32_t sa = 0;
-    if (chunks > 0) {
-        wa = load_stream16(tiles + w * 1024 + lane * 16);
-        sa = *reinterpret_cast<const uint32_t*>(tscales + lane * 4);
+    for (int q = 0; q < kStageRows; q++)
+        *reinterpret_cast<uint4*>(&sm.b[buf][(32 * q + tid / 8) * kBRow + 16 * (tid % 8)]) = r.v[q];
+    sm.bs[buf][tid] = r.s;
+}
+
+struct AOperand {
+    uint4 w[4];  // row groups 0..3 of the quad
+    uint32_t s;  // their four scale bytes
+};
+
+__device__ __attribute__((always_inline)) inline void load_a(const uint8_t* tiles, const uint8_t* tscales, int chunk, AOperand& a) {
+    const int lane = threadIdx.x % kWave;
+    const uint8_t* t = tiles + (int64_t)chunk * 4096 + lane * 16;
+#pragma unroll
+    for (int rg = 0; rg < 4; rg++) a.w[rg] = *reinterpret_cast<const uint4*>(t + rg * 1024);
+    a.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)chunk * 256 + lane * 4);
+}
+
+// Column tile t of wave (wr, wt) is token tile 2t + wt of the item
+// (interleaved, so the two token waves stay balanced on ragged items).
+__device__ inline int tile_token(int t, int wt, int c) { return 16 * (2 * t + wt) + c; }
+
+// One 128-k chunk: staging of chunk `nxt` into registers, A of chunk `nxt`
+// into an, the 4*NT MFMAs of chunk `s` from LDS buffer `cur` and A ac, and
+// the staged registers stored into the other buffer.  The last step reloads
+// and restages its own chunk into the idle buffer (nothing reads it again):
+// with no branch around them the loads are issued before the MFMAs.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void pf_step(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
+                               int s, int chunks, int cur, PfSmem& sm, const AOperand& ac,
+                               AOperand& an, f32x4_t (&acc)[4][kPfTiles]) {
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int wt = (threadIdx.x / kWave) >> 1;
+    const int nxt = s + 1 < chunks ? s + 1 : s;
+    StageRegs st;
+    stage_load(src, nxt, st);
+    load_a(tiles, tscales, nxt, an);
+    // keep the loads ahead of the MFMAs: the staging store at the end of the
+    // step is the first use of st, a's first use is the next step
+    if (MOE_PF_SCHED_BARRIERS) __builtin_amdgcn_sched_barrier(0);
+    i32x8_t B[NT > 0 ? NT : 1];
+    int sb[NT > 0 ? NT : 1];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int row = tile_token(t, wt, c);
+        const uint8_t* bp = &sm.b[cur][row * kBRow + 16 * g];
+        const uint4 lo = *reinterpret_cast<const uint4*>(bp);
+        const uint4 hi = *reinterpret_cast<const uint4*>(bp + 64);
+        sb[t] = (int)((sm.bs[cur][row] >> (8 * g)) & 0xffu);
+        B[t] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    for (int c = 0; c < chunks; c++) {
-        uint4 wn = make_uint4(0, 0, 0, 0);
-        uint32_t sn = 0;
-        if (c + 1 < chunks) {  // prefetch the next chunk's weights
-            wn = load_stream16(tiles + (int64_t)(c + 1) * 4096 + w * 1024 + lane * 16);
-            sn = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)(c + 1) * 256 + lane * 4);
-        }
-        BOperand b[kTiles];
 #pragma unroll
-        for (int t = 0; t < kTiles; t++) b[t] = load_b(rows[t], srows[t], c, g);
-        const i32x8_t A = i32x8_t{(int)wa.x, (int)wa.y, (int)wa.z, (int)wa.w, 0, 0, 0, 0};
-        const int sca = (int)((sa >> (8 * w)) & 0xffu);
+    for (int rg = 0; rg < 4; rg++) {
+        const i32x8_t A = i32x8_t{(int)ac.w[rg].x, (int)ac.w[rg].y, (int)ac.w[rg].z,
+                                  (int)ac.w[rg].w, 0, 0, 0, 0};
+        const int sa = (int)((ac.s >> (8 * rg)) & 0xffu);
 #pragma unroll
-        for (int t = 0; t < kTiles; t++)
-            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                A, b[t].v, acc[t], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sca, 0, b[t].scale);
-        wa = wn;
-        sa = sn;
+        for (int t = 0; t < NT; t++)
+            acc[rg][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A, B[t], acc[rg][t], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, sb[t]);
+    }
+    if (MOE_PF_SCHED_BARRIERS) __builtin_amdgcn_sched_barrier(0);
+    stage_store(sm, cur ^ 1, st);
+    __syncthreads();
+}
+
+// The main loop of one workgroup: acc[rg][t] = quad rows (group rg) x
+// column tile t of this wave (t < NT), summed over all `chunks` 128-k
+// chunks.  tiles/tscales point at this wave's quad.  Every wave runs the
+// same number of barriers whatever its NT.
+template <int NT>
+__device__ inline void pf_mainloop(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
+                                   int chunks, PfSmem& sm, f32x4_t (&acc)[4][kPfTiles]) {
+#pragma unroll
+    for (int rg = 0; rg < 4; rg++)
+#pragma unroll
+        for (int t = 0; t < kPfTiles; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    AOperand a0, a1;
+    {
+        StageRegs st;
+        stage_load(src, 0, st);
+        load_a(tiles, tscales, 0, a0);
+        stage_store(sm, 0, st);
+        __syncthreads();
+    }
+    for (int s = 0; s < chunks; s += 2) {
+        pf_step<NT>(tiles, tscales, src, s, chunks, 0, sm, a0, a1, acc);
+        if (s + 1 >= chunks) break;
+        pf_step<NT>(tiles, tscales, src, s + 1, chunks, 1, sm, a1, a0, acc);
     }
 }
 
-// gate_up, MXFP8 activations: blockIdx.x = item * quads + quad.  Waves 0, 1
-// hold gate groups, waves 2, 3 the matching up groups; SiLU(gate) * up is
-// formed through LDS and h (32 rows = one MX block per token) is encoded to
-// MXFP8 straight from fp32.
-__global__ void __launch_bounds__(kMx8Threads)
+__device__ inline void pf_gemm(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
+                               int chunks, int ntile, PfSmem& sm, f32x4_t (&acc)[4][kPfTiles]) {
+    switch (ntile) {
+        case 4: pf_mainloop<4>(tiles, tscales, src, chunks, sm, acc); break;
+        case 3: pf_mainloop<3>(tiles, tscales, src, chunks, sm, acc); break;
+        case 2: pf_mainloop<2>(tiles, tscales, src, chunks, sm, acc); break;
+        case 1: pf_mainloop<1>(tiles, tscales, src, chunks, sm, acc); break;
+        default: pf_mainloop<0>(tiles, tscales, src, chunks, sm, acc); break;
+    }
+}
+
+// column tiles of token wave wt that hold any of the item's m tokens
+__device__ inline int wave_tiles(int m, int wt) {
+    const int all = (m + 15) / 16;
+    return (all - wt + 1) / 2;
+}
+
+// gate_up, MXFP8 activations: blockIdx.x = item * (I / 64) + row block; the
+// row block holds quads 2rb, 2rb+1, each 32 gate rows (groups 0, 1) with
+// their 32 up rows (groups 2, 3), so SiLU(gate) * up is formed in
+// registers, and the 32 h values of one quad and token -- one MX block of h
+// -- sit in the four lanes (c, 0..3), which agree on the block scale through
+// two cross-lane maxima.
+__global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
 mx8_gate_up_kernel(GemmArgs a) {
-    __shared__ f32x4_t up[2][kTiles][kWave];
-    __shared__ float hbuf[kMx8Tok][33];
-    const int quads = a.I / 32;
-    const int item = blockIdx.x / quads, quad = blockIdx.x % quads;
+    __shared__ PfSmem sm;
+    const int rowblocks = a.I / 64;
+    const int item = blockIdx.x / rowblocks, rb = blockIdx.x % rowblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
-    const int K = a.H, chunks = K / 128;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int wr = w & 1, wt = w >> 1;
+    const int K = a.H, chunks = K / 128, quads = a.I / 32;
+    const int quad = 2 * rb + wr;
     const int64_t quad_id = (int64_t)e * quads + quad;
-    const uint8_t* rows[kTiles];
-    const uint8_t* srows[kTiles];
+    StageSrc src;
 #pragma unroll
-    for (int t = 0; t < kTiles; t++) {
-        const int j = 16 * t + c;
+    for (int q = 0; q < kStageRows; q++) {
+        const int j = min(32 * q + tid / 8, m - 1);
+        src.row[q] = a.xq + (int64_t)(a.sorted[row0 + j] / a.k) * K + 16 * (tid % 8);
+    }
+    src.srow = a.xs + (int64_t)(a.sorted[row0 + min(tid, m - 1)] / a.k) * (K / 32);
+    const int ntile = uniform(wave_tiles(m, wt));
+    f32x4_t acc[4][kPfTiles];
+    pf_gemm(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, src, chunks, ntile, sm,
+            acc);
+#pragma unroll
+    for (int t = 0; t < kPfTiles; t++) {
+        if (t >= ntile) break;
+        float hv[8];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float v = silu_mul(acc[h2][t][i], acc[h2 + 2][t][i]);
+                hv[4 * h2 + i] = v;
+                const uint32_t mb = __float_as_uint(v) & 0x7fffffffu;
+                amax = mb > amax ? mb : amax;
+            }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        uint32_t code[2] = {0, 0};
+        uint32_t scale = 255;
+        if (amax < 0x7f800000u) {
+            const int se = mxfp8_scale_exp(amax);
+            scale = (uint32_t)(se + 127);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) code[h2] |= e4m3_code(hv[4 * h2 + i], se) << (8 * i);
+        }
+        const int j = tile_token(t, wt, c);
         if (j < m) {
-            const int token = a.sorted[row0 + j] / a.k;
-            rows[t] = a.xq + (int64_t)token * K;
-            srows[t] = a.xs + (int64_t)token * (K / 32);
-        } else {
-            rows[t] = nullptr;
-            srows[t] = nullptr;
+            uint8_t* hrow = a.hq + (int64_t)(row0 + j) * a.I + 32 * quad + 4 * g;
+            *reinterpret_cast<uint32_t*>(hrow) = code[0];       // h rows 32q + 4g + i
+            *reinterpret_cast<uint32_t*>(hrow + 16) = code[1];  // h rows 32q + 16 + 4g + i
+            if (g == 0) a.hs[(int64_t)(row0 + j) * (a.I / 32) + quad] = (uint8_t)scale;
         }
-    }
-    f32x4_t acc[kTiles];
-    mx8_group(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, w, rows, srows,
-              chunks, acc);
-    if (w >= 2) {
-#pragma unroll
-        for (int t = 0; t < kTiles; t++) up[w - 2][t][lane] = acc[t];
-    }
-    __syncthreads();
-    if (w < 2) {
-#pragma unroll
-        for (int t = 0; t < kTiles; t++) {
-            const f32x4_t u = up[w][t][lane];
-#pragma unroll
-            for (int i = 0; i < 4; i++) hbuf[16 * t + c][16 * w + 4 * g + i] = silu_mul(acc[t][i], u[i]);
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x < m) {
-        const int j = threadIdx.x;
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 32; i++) v[i] = hbuf[j][i];
-        uint32_t cw[8];
-        uint8_t s;
-        encode_block_mxfp8(v, cw, s);
-        uint4* dst = reinterpret_cast<uint4*>(a.hq + (int64_t)(row0 + j) * a.I + 32 * quad);
-        dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-        dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-        a.hs[(int64_t)(row0 + j) * (a.I / 32) + quad] = s;
     }
 }
 
-// down, MXFP8 h: blockIdx.x = item * quads + quad (output rows 64q..64q+63,
-// wave w = rows 64q+16w..).  y goes out through agent-coherent stores; the
-// block that completes a token's k experts on this quad combines it.
-__global__ void __launch_bounds__(kMx8Threads)
+// down, MXFP8 h: blockIdx.x = item * (H / 128) + row block (quads 2rb,
+// 2rb+1 of the output rows).  y goes out through agent-coherent stores;
+// each wave then counts its (token, quad) tiles done, and the wave that
+// completes a token's k experts on a quad combines those 64 columns (the
+// last finisher, as in the other paths).
+__global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
 mx8_down_kernel(GemmArgs a) {
-    __shared__ int s_last[kMx8Tok];
-    __shared__ int s_nlast;
-    const int quads = a.H / 64;
-    const int item = blockIdx.x / quads, quad = blockIdx.x % quads;
+    __shared__ PfSmem sm;
+    const int rowblocks = a.H / 128;
+    const int item = blockIdx.x / rowblocks, rb = blockIdx.x % rowblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
-    const int K = a.I, chunks = K / 128;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int wr = w & 1, wt = w >> 1;
+    const int K = a.I, chunks = K / 128, quads = a.H / 64;
+    const int quad = 2 * rb + wr;
     const int64_t quad_id = (int64_t)e * quads + quad;
-    const uint8_t* rows[kTiles];
-    const uint8_t* srows[kTiles];
+    StageSrc src;
 #pragma unroll
-    for (int t = 0; t < kTiles; t++) {
-        const int j = 16 * t + c;
-        rows[t] = j < m ? a.hq + (int64_t)(row0 + j) * K : nullptr;
-        srows[t] = j < m ? a.hs + (int64_t)(row0 + j) * (K / 32) : nullptr;
+    for (int q = 0; q < kStageRows; q++) {
+        const int j = min(32 * q + tid / 8, m - 1);
+        src.row[q] = a.hq + (int64_t)(row0 + j) * K + 16 * (tid % 8);
     }
-    f32x4_t acc[kTiles];
-    mx8_group(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, w, rows, srows,
-              chunks, acc);
+    src.srow = a.hs + (int64_t)(row0 + min(tid, m - 1)) * (K / 32);
+    const int ntile = uniform(wave_tiles(m, wt));
+    f32x4_t acc[4][kPfTiles];
+    pf_gemm(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, src, chunks, ntile, sm,
+            acc);
     const int n0 = 64 * quad;
 #pragma unroll
-    for (int t = 0; t < kTiles; t++) {
-        const int j = 16 * t + c;
-        if (j < m) {
-            float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 16 * w + 4 * g;
-            const uint64_t lo = (uint64_t)__float_as_uint(acc[t][0]) |
-                                ((uint64_t)__float_as_uint(acc[t][1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(acc[t][2]) |
-                                ((uint64_t)__float_as_uint(acc[t][3]) << 32);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), lo, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 2), hi, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's y stores done
-    if (threadIdx.x == 0) s_nlast = 0;
-    __syncthreads();
-    if (threadIdx.x < m) {
-        const int token = a.sorted[row0 + threadIdx.x] / a.k;
-        if (atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1)
-            s_last[atomicAdd(&s_nlast, 1)] = token;
-    }
-    __syncthreads();
-    const int nlast = s_nlast;
-    // combine: four tokens at a time, one column per thread
-    for (int i0 = 0; i0 < nlast; i0 += kMx8Threads / 64) {
-        const int i = i0 + (int)(threadIdx.x / 64);
-        if (i < nlast) {
-            const int t = s_last[i], n = n0 + lane;
-            float v = 0.f;
-            for (int j = 0; j < a.k; j++) {
-                const float wt = a.wts[(int64_t)t * a.k + j];
-                const int p = a.pos[(int64_t)t * a.k + j];
-                v = fmaf(wt, __hip_atomic_load(a.y + (int64_t)p * a.H + n, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT), v);
+    for (int t = 0; t < kPfTiles; t++) {
+        const int j = tile_token(t, wt, c);
+        if (t < ntile && j < m) {
+            float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
+#pragma unroll
+            for (int rg = 0; rg < 4; rg++) {
+                const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
+                                    ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
+                const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
+                                    ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            a.out[(int64_t)t * a.H + n] = f32_to_bf16_rne(v);
         }
+    }
+    // every y store of this wave has completed before it counts its tiles
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // lane (c, g) counts token tile_token(g, wt, c): the tokens whose y rows
+    // this wave stored (column tiles g < ntile)
+    const int j = tile_token(g, wt, c);
+    int token = -1;
+    bool last = false;
+    if (g < ntile && j < m) {
+        token = a.sorted[row0 + j] / a.k;
+        last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
+    }
+    uint64_t todo = __ballot(last);
+    while (todo) {
+        const int srcl = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int t = __builtin_amdgcn_readlane(token, srcl);
+        // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
+        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
     }
 }
 
@@ -309,17 +414,17 @@ hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* cod
     const int64_t nblocks = (int64_t)T * H / 32;
     if (nblocks == 0) return hipSuccess;
     quantize_x_mxfp8_kernel<<<(unsigned)((nblocks + kQuantThreads - 1) / kQuantThreads),
-                              kQuantThreads, 0, stream>>>(x, nblocks, H, codes, scales);
+                              kQuantThreads, 0, stream>>>(x, nblocks, codes, scales);
     return hipGetLastError();
 }
 
 hipError_t launch_mx8_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
-    mx8_gate_up_kernel<<<max_items * (a.I / 32), kMx8Threads, 0, stream>>>(a);
+    mx8_gate_up_kernel<<<max_items * (a.I / 64), kPfThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_mx8_down(const GemmArgs& a, int max_items, hipStream_t stream) {
-    mx8_down_kernel<<<max_items * (a.H / 64), kMx8Threads, 0, stream>>>(a);
+    mx8_down_kernel<<<max_items * (a.H / 128), kPfThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

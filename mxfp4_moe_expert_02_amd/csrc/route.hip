@@ -17,9 +17,10 @@
 // result deterministic.  Selection, counts, offsets and order are integer or
 // compare-only, hence bit-exact; only the weights use exp.
 //
-// Small layers (T*E <= kFusedPairs) route in one workgroup (one launch);
-// larger ones use a grid for top-k and one workgroup for the sort.  Both
-// also reset the per-(token, column tile) combine counters.
+// Small layers (T*E <= kFusedMaxPairs) route in one workgroup (one
+// launch); larger ones use a grid for top-k and a multi-block counting sort
+// (per-block histograms, one scan, per-block stable scatter).  Both also
+// reset the per-(token, column tile) combine counters.
 #include <float.h>
 #include <limits.h>
 
@@ -29,7 +30,9 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kFusedPairs = 12288;    // T*E routed by the single-workgroup kernel
+constexpr int kFusedPairs = 12288;    // logits held in LDS by the single-workgroup kernel
+constexpr int kFusedMaxPairs = 4096;  // T*E routed by the single-workgroup kernel
+constexpr int kSlotBlock = kRouteSlotBlock;
 constexpr int kTopkThreads = 256;
 constexpr int kSortLdsInts = 12288;   // per-range histograms
 
@@ -92,41 +95,11 @@ __device__ void topk_tokens(const float* lg, int nt, int t0, int E, int k, int* 
     }
 }
 
-// Stable counting sort of the S slots by expert (ids[s] = expert of slot
-// s, in LDS or global memory), the active-expert lists, and the reset of
-// the combine counters.  One workgroup.
-__device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Workspace& ws,
-                           int gemv_max_tokens, int path, int item_tok, int* hist, int* s_cnt,
-                           int* s_off) {
-    __shared__ int s_n[3];
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    // R ranges (power of two) of L consecutive slots: R ~ sqrt(S), R*E fits in LDS
-    int R = 1;
-    while (R * 2 <= nthr && R * 2 * E <= kSortLdsInts && R * R * 4 <= S) R *= 2;
-    const int L = (S + R - 1) / R;
-
-    for (int i = tid; i < R * E; i += nthr) hist[i] = 0;
-    if (tid < 3) s_n[tid] = 0;
-    // reset the combine counters of the down kernels (sized for the finest tile)
-    for (int i = tid; i < T * (int)(ws.H / kMfmaDownRows); i += nthr) ws.tile_done[i] = 0;
-    __syncthreads();
-    if (tid < R) {  // 1. per-range histogram
-        const int s0 = tid * L, s1 = min(S, s0 + L);
-        for (int s = s0; s < s1; s++) hist[tid * E + ids[s]]++;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += nthr) {  // 2. per expert: exclusive scan over ranges
-        int run = 0;
-        for (int r = 0; r < R; r++) {
-            const int c = hist[r * E + e];
-            hist[r * E + e] = run;
-            run += c;
-        }
-        s_cnt[e] = run;
-        ws.counts[e] = run;
-    }
-    __syncthreads();
-    if (tid < kWave) {  // 3. exclusive scan over experts, one wave, 64 at a time
+// s_off[e] = exclusive prefix sum of s_cnt over experts, s_off[E] = total
+// (LDS arrays); one wave, 64 experts at a time.
+__device__ inline void scan_experts(int E, const int* s_cnt, int* s_off) {
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
         int carry = 0;
         for (int base = 0; base < E; base += kWave) {
             const int e = base + tid;
@@ -137,20 +110,18 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
         }
         if (tid == 0) s_off[E] = carry;
     }
-    __syncthreads();
-    for (int e = tid; e <= E; e += nthr) ws.offsets[e] = s_off[e];
-    if (tid < R) {  // 4. stable scatter: each range walks its slots in order
-        const int s0 = tid * L, s1 = min(S, s0 + L);
-        for (int s = s0; s < s1; s++) {
-            const int e = ids[s];
-            const int p = s_off[e] + hist[tid * E + e]++;
-            ws.sorted[p] = s;
-            ws.pos[s] = p;
-        }
-    }
-    // 5. active-expert lists in ascending expert index, compacted with wave
-    //    scans: the GEMV list, and the MFMA list with its items of up to
-    //    kMfmaTok tokens each: (expert, first row in sorted order, tokens).
+}
+
+// Active-expert lists in ascending expert index, compacted with wave
+// scans: the GEMV list, and the MFMA list with its items of up to item_tok
+// tokens each: (expert, first row in sorted order, tokens), ceil(c /
+// item_tok) items per expert of equal numbers of 16-token tiles (+-1).
+// s_cnt/s_off: the per-expert counts and exclusive offsets, in LDS.  Writes
+// the list lengths to meta.  Called by every thread of one block.
+__device__ void build_lists(int E, const Workspace& ws, int gemv_max_tokens, int path, int item_tok,
+                            const int* s_cnt, const int* s_off) {
+    __shared__ int s_n[3];
+    const int tid = threadIdx.x;
     if (tid < kWave) {
         int n_g = 0, n_m = 0, n_items = 0;
         for (int base = 0; base < E; base += kWave) {
@@ -166,9 +137,15 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
             if (m) {
                 const int slot = n_m + im - 1, first = n_items + ii - groups;
                 ws.mfma_list[slot] = e;
-                for (int q = 0; q < groups; q++)
+                // the expert's 16-token tiles dealt out as evenly as possible
+                const int tiles = (c + 15) / 16, per = tiles / groups, extra = tiles % groups;
+                int t0 = 0;
+                for (int q = 0; q < groups; q++) {
+                    const int nt = per + (q < extra ? 1 : 0);
                     ws.mfma_items[first + q] =
-                        make_int4(e, s_off[e] + q * item_tok, min(item_tok, c - q * item_tok), 0);
+                        make_int4(e, s_off[e] + 16 * t0, min(16 * nt, c - 16 * t0), 0);
+                    t0 += nt;
+                }
             }
             n_g += __builtin_amdgcn_readlane(ig, kWave - 1);
             n_m += __builtin_amdgcn_readlane(im, kWave - 1);
@@ -188,6 +165,53 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
     }
 }
 
+// Stable counting sort of the S slots by expert (ids[s] = expert of slot
+// s, in LDS or global memory), the active-expert lists, and the reset of
+// the combine counters.  One workgroup.
+__device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Workspace& ws,
+                           int gemv_max_tokens, int path, int item_tok, int* hist, int* s_cnt,
+                           int* s_off) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    // R ranges (power of two) of L consecutive slots: R ~ sqrt(S), R*E fits in LDS
+    int R = 1;
+    while (R * 2 <= nthr && R * 2 * E <= kSortLdsInts && R * R * 4 <= S) R *= 2;
+    const int L = (S + R - 1) / R;
+
+    for (int i = tid; i < R * E; i += nthr) hist[i] = 0;
+    // reset the combine counters of the down kernels (sized for the finest tile)
+    for (int i = tid; i < T * (int)(ws.H / kMfmaDownRows); i += nthr) ws.tile_done[i] = 0;
+    __syncthreads();
+    if (tid < R) {  // 1. per-range histogram
+        const int s0 = tid * L, s1 = min(S, s0 + L);
+        for (int s = s0; s < s1; s++) hist[tid * E + ids[s]]++;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nthr) {  // 2. per expert: exclusive scan over ranges
+        int run = 0;
+        for (int r = 0; r < R; r++) {
+            const int c = hist[r * E + e];
+            hist[r * E + e] = run;
+            run += c;
+        }
+        s_cnt[e] = run;
+        ws.counts[e] = run;
+    }
+    __syncthreads();
+    scan_experts(E, s_cnt, s_off);  // 3. exclusive scan over experts
+    __syncthreads();
+    for (int e = tid; e <= E; e += nthr) ws.offsets[e] = s_off[e];
+    if (tid < R) {  // 4. stable scatter: each range walks its slots in order
+        const int s0 = tid * L, s1 = min(S, s0 + L);
+        for (int s = s0; s < s1; s++) {
+            const int e = ids[s];
+            const int p = s_off[e] + hist[tid * E + e]++;
+            ws.sorted[p] = s;
+            ws.pos[s] = p;
+        }
+    }
+    build_lists(E, ws, gemv_max_tokens, path, item_tok, s_cnt, s_off);
+}
+
 __global__ void __launch_bounds__(kRouteThreads)
 route_fused_kernel(const float* __restrict__ logits, int T, int E, int k, Workspace ws,
                    int gemv_max_tokens, int path, int item_tok) {
@@ -205,47 +229,112 @@ route_fused_kernel(const float* __restrict__ logits, int T, int E, int k, Worksp
     sort_slots(sel_id, T * k, E, T, ws, gemv_max_tokens, path, item_tok, hist, s_cnt, s_off);
 }
 
-// grid over token groups: each block ranks tokens [t0, t0 + nt)
+// ---- larger layers: top-k over a grid, then a stable counting sort over
+// blocks of kSlotBlock slots (per-block histograms, one scan, per-block
+// scatter), four launches whose work all scales out.
+
+// grid over token groups: each block ranks tokens [t0, t0 + nt) and resets
+// their combine counters
 __global__ void __launch_bounds__(kTopkThreads)
 route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int tokens_per_block,
-                  int32_t* __restrict__ ids, float* __restrict__ wts) {
+                  int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ tile_done,
+                  int done_per_token) {
     extern __shared__ float dyn[];
     const int t0 = blockIdx.x * tokens_per_block;
     const int nt = min(tokens_per_block, T - t0);
     float* lg = dyn;
     int* sel_id = reinterpret_cast<int*>(dyn + tokens_per_block * E);
     float* sel_l = dyn + tokens_per_block * E + tokens_per_block * k;
+    for (int i = threadIdx.x; i < nt * done_per_token; i += blockDim.x)
+        tile_done[(int64_t)t0 * done_per_token + i] = 0;
     for (int i = threadIdx.x; i < nt * E; i += blockDim.x) lg[i] = logits[(int64_t)t0 * E + i];
     __syncthreads();
     topk_tokens(lg, nt, t0, E, k, sel_id, sel_l, ids, wts);
 }
 
+// bhist[b][e] = slots of block b (slots [b*kSlotBlock, ...)) routed to e
+__global__ void __launch_bounds__(kSlotBlock)
+route_hist_kernel(const int32_t* __restrict__ ids, int S, int E, int32_t* __restrict__ bhist) {
+    __shared__ int h[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += kSlotBlock) h[e] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * kSlotBlock + threadIdx.x;
+    if (s < S) atomicAdd(&h[ids[s]], 1);  // counts only: order-free
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kSlotBlock) bhist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block: counts, offsets, the first sorted position of every (block,
+// expert) pair (bhist rewritten in place), and the lists and items.
 __global__ void __launch_bounds__(kRouteThreads)
-route_sort_kernel(int T, int E, int k, Workspace ws, int gemv_max_tokens, int path, int item_tok) {
-    __shared__ int hist[kSortLdsInts];
+route_scan_kernel(int nblk, int E, Workspace ws, int32_t* __restrict__ bhist, int gemv_max_tokens,
+                  int path, int item_tok) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
-    sort_slots(ws.ids, T * k, E, T, ws, gemv_max_tokens, path, item_tok, hist, s_cnt, s_off);
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    for (int e = tid; e < E; e += nthr) {  // per expert: exclusive scan over blocks
+        int run = 0;
+        for (int b = 0; b < nblk; b++) {
+            const int c = bhist[(int64_t)b * E + e];
+            bhist[(int64_t)b * E + e] = run;
+            run += c;
+        }
+        s_cnt[e] = run;
+        ws.counts[e] = run;
+    }
+    __syncthreads();
+    scan_experts(E, s_cnt, s_off);
+    __syncthreads();
+    for (int e = tid; e <= E; e += nthr) ws.offsets[e] = s_off[e];
+    for (int i = tid; i < nblk * E; i += nthr) bhist[i] += s_off[i % E];
+    build_lists(E, ws, gemv_max_tokens, path, item_tok, s_cnt, s_off);
+}
+
+// Stable scatter: slot s goes to bhist[b][e] + (slots before it in its
+// block routed to the same expert).
+__global__ void __launch_bounds__(kSlotBlock)
+route_scatter_kernel(const int32_t* __restrict__ ids, int S, int E,
+                     const int32_t* __restrict__ bhist, int32_t* __restrict__ sorted,
+                     int32_t* __restrict__ pos) {
+    __shared__ int sid[kSlotBlock];
+    const int s = blockIdx.x * kSlotBlock + threadIdx.x;
+    const int e = s < S ? ids[s] : -1;
+    sid[threadIdx.x] = e;
+    __syncthreads();
+    if (s < S) {
+        int rank = 0;
+        for (int i = 0; i < (int)threadIdx.x; i++) rank += sid[i] == e ? 1 : 0;
+        const int p = bhist[(int64_t)blockIdx.x * E + e] + rank;
+        sorted[p] = s;
+        pos[s] = p;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
                         int gemv_max_tokens, int path, int item_tok, hipStream_t stream) {
-    if ((int64_t)T * E <= kFusedPairs && T * k <= kRouteThreads) {
+    if ((int64_t)T * E <= kFusedMaxPairs && T * k <= kRouteThreads) {
         route_fused_kernel<<<1, kRouteThreads, 0, stream>>>(logits, T, E, k, ws,
                                                             gemv_max_tokens, path, item_tok);
         return hipGetLastError();
     }
+    const int S = T * k;
     const int tpb = E >= kTopkThreads ? 1 : kTopkThreads / E;
     const int blocks = (T + tpb - 1) / tpb;
     const size_t lds = (size_t)tpb * (E + 2 * k) * 4;
-    route_topk_kernel<<<blocks, kTopkThreads, lds, stream>>>(logits, T, E, k, tpb, ws.ids,
-                                                             ws.wts);
+    route_topk_kernel<<<blocks, kTopkThreads, lds, stream>>>(logits, T, E, k, tpb, ws.ids, ws.wts,
+                                                             ws.tile_done,
+                                                             (int)(ws.H / kMfmaDownRows));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_sort_kernel<<<1, kRouteThreads, 0, stream>>>(T, E, k, ws, gemv_max_tokens, path,
+    const int nblk = (S + kSlotBlock - 1) / kSlotBlock;
+    route_hist_kernel<<<nblk, kSlotBlock, 0, stream>>>(ws.ids, S, E, ws.bhist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    route_scan_kernel<<<1, kRouteThreads, 0, stream>>>(nblk, E, ws, ws.bhist, gemv_max_tokens, path,
                                                        item_tok);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    route_scatter_kernel<<<nblk, kSlotBlock, 0, stream>>>(ws.ids, S, E, ws.bhist, ws.sorted, ws.pos);
     return hipGetLastError();
 }
 
