@@ -24,6 +24,24 @@ __device__ inline float e8m0_to_f32(uint32_t s) {
     return s == 255u ? __builtin_nanf("") : f;
 }
 
+// E8M0 code as the fp32 scale operand of v_cvt_scalef32_* (the code in the
+// exponent field: 2^(s-127) for s in 1..254)
+__device__ inline float e8m0_as_scale(uint32_t s) { return __uint_as_float(s << 23); }
+
+// 8 E2M1 codes of one word (element 2i in the low nibble of byte i) -> 8
+// bf16, block scale applied by the conversion (exact for scale codes 1..254)
+__device__ inline bf16x8_t decode8(uint32_t word, float scale) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ inline uint32_t word_of(const uint4& v, int q) {
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)

@@ -29,8 +29,10 @@
 // the expert reads the same token rows, so these are L1/L2 hits), D = 16
 // rows x 16 tokens (lane (c, g) holds rows 4g..4g+3 of token c).  The 4
 // waves of a workgroup split the chunks in four ranges and add their
-// accumulators through LDS at the end.  Items come from the route:
-// (expert slot, first token) with up to 16 tokens each.
+// accumulators through LDS at the end.  Items come from the route: (expert,
+// first row in sorted order, tokens) with up to 16 tokens each (wider items
+// go to mfma_wide.hip).  The quad routine is written for NT column tiles;
+// these kernels use NT = 1.
 #include "device_common.h"
 
 namespace moe {
@@ -47,46 +49,47 @@ constexpr int kWaves = kMfmaThreads / kWave;  // 4, split K
 constexpr int kChunksPerStep = MOE_MFMA_CHUNKS_PER_STEP;  // 128-column chunks per prefetch step
 constexpr int kGroups = 4;                    // 16-row groups per quad
 
-// E8M0 code as the fp32 scale operand of v_cvt_scalef32_* (the code in the
-// exponent field: 2^(s-127) for s in 1..254)
-__device__ inline float e8m0_as_scale(uint32_t s) { return __uint_as_float(s << 23); }
+// chunks per prefetch step: kChunksPerStep for single-tile items, one for
+// wider ones (their x operands alone fill 16 VGPRs per tile and chunk)
+#ifndef MOE_MFMA_WIDE_CPS
+#define MOE_MFMA_WIDE_CPS 1
+#endif
 
-// 8 E2M1 codes of one word (element 2i in the low nibble of byte i) -> 8 bf16
-__device__ inline bf16x8_t decode8(uint32_t word, float scale) {
-    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
-    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
-    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
-    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
-    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
+template <int NT>
+struct Cps {
+    static constexpr int value = NT == 1 ? kChunksPerStep : NT == 2 ? MOE_MFMA_WIDE_CPS : 1;
+};
 
-__device__ inline uint32_t word_of(const uint4& v, int q) {
-    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
-}
-
+template <int CPS>
 struct WStep {
-    uint4 w[kChunksPerStep][kGroups];
-    uint32_t s[kChunksPerStep];
+    uint4 w[CPS][kGroups];
+    uint32_t s[CPS];
 };
 
+template <int NT>
 struct XStep {
-    uint4 x[kChunksPerStep][4];
+    uint4 x[Cps<NT>::value][NT][4];
 };
 
-// One wave: chunks [c_begin, c_end) of one quad against up to 16 tokens.
-// tiles/tscales point at the quad's chunk 0; row_of() gives this lane's
-// token row (bf16) or null for a zero column, and is called only after the
-// first weight loads are in flight (it usually waits on an index load).
-template <typename RowFn>
-__device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowFn row_of,
-                                 int c_begin, int c_end, f32x4_t (&acc)[kGroups]) {
+// One wave: chunks [c_begin, c_end) of one quad against NT column tiles of
+// 16 tokens.  tiles/tscales point at the quad's chunk 0; rows_of(xrow)
+// fills this lane's token row (bf16) of every tile, or null for a zero
+// column, and is called only after the first weight loads are in flight
+// (it usually waits on an index load).  Each weight word is decoded once and
+// feeds the NT tiles' MFMAs.
+template <int NT, typename RowsFn>
+__device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowsFn rows_of,
+                                 int c_begin, int c_end, f32x4_t (&acc)[kGroups][NT]) {
+    constexpr int CPS = Cps<NT>::value;
     const int lane = threadIdx.x % kWave, g = lane / 16;
-    const uint16_t* xrow = nullptr;
+    const uint16_t* xrow[NT];
 #pragma unroll
-    for (int rg = 0; rg < kGroups; rg++) acc[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto load_w = [&](int c0, WStep& b) {
+    for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
-        for (int i = 0; i < kChunksPerStep; i++) {
+        for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto load_w = [&](int c0, WStep<CPS>& b) {
+#pragma unroll
+        for (int i = 0; i < CPS; i++) {
             const bool ok = c0 + i < c_end;
             const uint8_t* t = tiles + (int64_t)(c0 + i) * 4096 + lane * 16;
 #pragma unroll
@@ -97,43 +100,49 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
                         : 0x7f7f7f7fu;
         }
     };
-    auto load_x = [&](int c0, XStep& xb) {
+    auto load_x = [&](int c0, XStep<NT>& xb) {
 #pragma unroll
-        for (int i = 0; i < kChunksPerStep; i++) {
-            const bool ok = xrow && (c0 + i < c_end);
-            const uint4* src = reinterpret_cast<const uint4*>(xrow + (int64_t)(4 * (c0 + i) + g) * 32);
+        for (int i = 0; i < CPS; i++)
 #pragma unroll
-            for (int q = 0; q < 4; q++) xb.x[i][q] = ok ? src[q] : make_uint4(0, 0, 0, 0);
-        }
+            for (int t = 0; t < NT; t++) {
+                const bool ok = xrow[t] && (c0 + i < c_end);
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(xrow[t] + (int64_t)(4 * (c0 + i) + g) * 32);
+#pragma unroll
+                for (int q = 0; q < 4; q++) xb.x[i][t][q] = ok ? src[q] : make_uint4(0, 0, 0, 0);
+            }
     };
-    auto compute = [&](const WStep& b, const XStep& xb) {
+    auto compute = [&](const WStep<CPS>& b, const XStep<NT>& xb) {
 #pragma unroll
-        for (int i = 0; i < kChunksPerStep; i++) {
+        for (int i = 0; i < CPS; i++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const bf16x8_t B = __builtin_bit_cast(bf16x8_t, xb.x[i][q]);
 #pragma unroll
                 for (int rg = 0; rg < kGroups; rg++) {
                     const float sc = e8m0_as_scale((b.s[i] >> (8 * rg)) & 0xffu);
                     const bf16x8_t A = decode8(word_of(b.w[i][rg], q), sc);
-                    acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[rg], 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < NT; t++) {
+                        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, xb.x[i][t][q]);
+                        acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[rg][t], 0, 0, 0);
+                    }
                 }
             }
         }
     };
-    WStep wa, wb;
-    XStep xa;
+    WStep<CPS> wa, wb;
+    XStep<NT> xa;
     int c = c_begin;
     if (c < c_end) load_w(c, wa);
-    xrow = row_of();
+    rows_of(xrow);
     while (c < c_end) {
-        const int n1 = c + kChunksPerStep;
+        const int n1 = c + CPS;
         if (n1 < c_end) load_w(n1, wb);  // prefetch the next step's weights
         load_x(c, xa);
         compute(wa, xa);
         c = n1;
         if (c >= c_end) break;
-        const int n2 = c + kChunksPerStep;
+        const int n2 = c + CPS;
         if (n2 < c_end) load_w(n2, wa);
         load_x(c, xa);
         compute(wb, xa);
@@ -142,18 +151,25 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
 }
 
 // Sum the 4 waves' accumulators (split K) through LDS; wave 0 gets the total.
-__device__ inline void reduce_waves(f32x4_t (&acc)[kGroups], f32x4_t* red) {
+template <int NT>
+__device__ inline void reduce_waves(f32x4_t (&acc)[kGroups][NT], f32x4_t* red) {
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
     if (w > 0) {
 #pragma unroll
-        for (int rg = 0; rg < kGroups; rg++) red[((w - 1) * kGroups + rg) * kWave + lane] = acc[rg];
+        for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                red[(((w - 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
     }
     __syncthreads();
     if (w == 0) {
 #pragma unroll
         for (int v = 1; v < kWaves; v++)
 #pragma unroll
-            for (int rg = 0; rg < kGroups; rg++) acc[rg] += red[((v - 1) * kGroups + rg) * kWave + lane];
+            for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    acc[rg][t] += red[(((v - 1) * kGroups + rg) * NT + t) * kWave + lane];
     }
 }
 
@@ -164,91 +180,115 @@ __device__ inline void wave_chunk_range(int chunks, int& c_begin, int& c_end) {
     c_end = min(chunks, c_begin + per);
 }
 
+// LDS for the cross-wave sums of single-tile items
+constexpr int kRedGateUp = (kWaves - 1) * kGroups * kWave;
+constexpr int kRedDown = 2 * kGroups * kWave;
+
+// gate_up body for items of NT column tiles
+template <int NT>
+__device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, int row0, int m,
+                                    f32x4_t* red) {
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int K = a.H, chunks = K / 128, quads = a.I / 32;
+    const int64_t quad_id = (int64_t)e * quads + quad;
+    int cb, ce;
+    wave_chunk_range(chunks, cb, ce);
+    f32x4_t acc[kGroups][NT];
+    mfma_quad<NT>(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256,
+                  [&](const uint16_t* (&xrow)[NT]) {
+#pragma unroll
+                      for (int t = 0; t < NT; t++) {
+                          const int j = 16 * t + c;
+                          xrow[t] = j < m ? a.x + (int64_t)(a.sorted[row0 + j] / a.k) * K : nullptr;
+                      }
+                  },
+                  cb, ce, acc);
+    reduce_waves<NT>(acc, red);
+    if (threadIdx.x < kWave) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const int j = 16 * t + c;
+            if (j >= m) continue;
+            uint16_t* hrow = a.h + (int64_t)(row0 + j) * a.I + 32 * quad + 4 * g;
+#pragma unroll
+            for (int rg = 0; rg < 2; rg++) {
+                ushort4 o;
+                o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
+                o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
+                o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
+                o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
+                *reinterpret_cast<ushort4*>(hrow + 16 * rg) = o;
+            }
+        }
+    }
+}
+
 // gate_up: blockIdx.x = item * quads + quad; quad q = gate rows 32q..32q+31
-// (groups 0, 1) with up rows I+32q..I+32q+31 (groups 2, 3).
+// (groups 0, 1) with up rows I+32q..I+32q+31 (groups 2, 3).  WIDE: items of
+// up to kMfmaItemTok tokens (1..4 column tiles of 16); otherwise items of
+// at most 16 tokens, compiled without the wider cases (fewer registers).
 __global__ void __launch_bounds__(kMfmaThreads)
 __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
 mfma_gate_up_kernel(GemmArgs a) {
-    __shared__ f32x4_t red[(kWaves - 1) * kGroups * kWave];
+    __shared__ f32x4_t red[kRedGateUp];
     const int quads = a.I / 32;
     const int item = blockIdx.x / quads, quad = blockIdx.x % quads;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
-    const int K = a.H, chunks = K / 128;
-    const int64_t quad_id = (int64_t)e * quads + quad;
-    const uint8_t* tiles = a.wgu + quad_id * chunks * 4096;
-    const uint8_t* tsc = a.sgu + quad_id * chunks * 256;
-    int cb, ce;
-    wave_chunk_range(chunks, cb, ce);
-    f32x4_t acc[kGroups];
-    mfma_quad(tiles, tsc, [&]() -> const uint16_t* {
-        return c < m ? a.x + (int64_t)(a.sorted[row0 + c] / a.k) * K : nullptr;
-    }, cb, ce, acc);
-    reduce_waves(acc, red);
-    if (threadIdx.x < kWave && c < m) {
-        uint16_t* hrow = a.h + (int64_t)(row0 + c) * a.I + 32 * quad + 4 * g;
-#pragma unroll
-        for (int rg = 0; rg < 2; rg++) {
-            ushort4 o;
-            o.x = f32_to_bf16_rne(silu_mul(acc[rg][0], acc[rg + 2][0]));
-            o.y = f32_to_bf16_rne(silu_mul(acc[rg][1], acc[rg + 2][1]));
-            o.z = f32_to_bf16_rne(silu_mul(acc[rg][2], acc[rg + 2][2]));
-            o.w = f32_to_bf16_rne(silu_mul(acc[rg][3], acc[rg + 2][3]));
-            *reinterpret_cast<ushort4*>(hrow + 16 * rg) = o;
-        }
-    }
+    gate_up_item<1>(a, quad, e, row0, m, red);
 }
 
-// down: a workgroup takes two quads (output rows 64q..64q+63), each split
-// in two K halves over two waves; blockIdx.x = item * ceil(quads / 2) +
-// pair.  A quad is also the combine tile: the wave holding the summed
-// accumulator counts the tile done for its tokens, and the one that
-// completes a token's k experts combines it (the last finisher, as in
-// gemv.hip).  y moves through agent-coherent stores and loads.
-__global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
-mfma_down_kernel(GemmArgs a) {
-    __shared__ f32x4_t red[2 * kGroups * kWave];
-    const int quads = a.H / 64, pairs = (quads + 1) / 2;
-    const int item = blockIdx.x / pairs;
+// down body for items of NT column tiles (see mfma_down_kernel)
+template <int NT>
+__device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, int m,
+                                 f32x4_t* red) {
+    const int quads = a.H / 64;
     const int w = threadIdx.x / kWave, half = w & 1;
-    const int quad = (blockIdx.x % pairs) * 2 + (w >> 1);
-    if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
-    const int4 it = a.items[item];
-    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+    const int quad = pair * 2 + (w >> 1);
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int K = a.I, chunks = K / 128;
     const bool live = quad < quads;
-    f32x4_t acc[kGroups];
+    f32x4_t acc[kGroups][NT];
     if (live) {
         const int64_t quad_id = (int64_t)e * quads + quad;
-        const uint8_t* tiles = a.wdn + quad_id * chunks * 4096;
-        const uint8_t* tsc = a.sdn + quad_id * chunks * 256;
         const int hc = (chunks + 1) / 2;
-        mfma_quad(tiles, tsc, [&]() -> const uint16_t* {
-            return c < m ? a.h + (int64_t)(row0 + c) * K : nullptr;
-        }, half ? hc : 0, half ? chunks : hc, acc);
+        mfma_quad<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256,
+                      [&](const uint16_t* (&xrow)[NT]) {
+#pragma unroll
+                          for (int t = 0; t < NT; t++) {
+                              const int j = 16 * t + c;
+                              xrow[t] = j < m ? a.h + (int64_t)(row0 + j) * K : nullptr;
+                          }
+                      },
+                      half ? hc : 0, half ? chunks : hc, acc);
         if (half) {
 #pragma unroll
-            for (int rg = 0; rg < kGroups; rg++) red[((w >> 1) * kGroups + rg) * kWave + lane] = acc[rg];
+            for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
         }
     }
     __syncthreads();
     if (!live || half) return;
 #pragma unroll
-    for (int rg = 0; rg < kGroups; rg++) acc[rg] += red[((w >> 1) * kGroups + rg) * kWave + lane];
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
     const int n0 = 64 * quad;
-    if (c < m) {
-        float* dst = a.y + (int64_t)(row0 + c) * a.H + n0 + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if (j >= m) continue;
+        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
 #pragma unroll
         for (int rg = 0; rg < kGroups; rg++) {
             // agent-coherent stores: the combining wave may run on another XCD
-            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][0]) |
-                                ((uint64_t)__float_as_uint(acc[rg][1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][2]) |
-                                ((uint64_t)__float_as_uint(acc[rg][3]) << 32);
+            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
+            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
             __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
@@ -271,6 +311,24 @@ mfma_down_kernel(GemmArgs a) {
         // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
         a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
     }
+}
+
+// down: a workgroup takes two quads (output rows 64q..64q+63), each split
+// in two K halves over two waves; blockIdx.x = item * ceil(quads / 2) +
+// pair.  A quad is also the combine tile: the wave holding the summed
+// accumulator counts the tile done for its tokens, and the one that
+// completes a token's k experts combines it (the last finisher, as in
+// gemv.hip).  y moves through agent-coherent stores and loads.
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+mfma_down_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[kRedDown];
+    const int quads = a.H / 64, pairs = (quads + 1) / 2;
+    const int item = blockIdx.x / pairs, pair = blockIdx.x % pairs;
+    if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
+    const int4 it = a.items[item];
+    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+    down_item<1>(a, pair, e, row0, m, red);
 }
 
 }  // namespace

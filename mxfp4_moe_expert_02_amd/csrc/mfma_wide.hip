@@ -1,0 +1,297 @@
+// mfma_wide.hip -- the bf16 expert GEMMs for items of up to 64 tokens
+// (layers whose experts average several tokens each, e.g. the batched and
+// skewed verify steps), over the prepacked MFMA tile layout.
+//
+// With wide items the activation loads, not the weight bytes, limit the
+// split-K kernels of mfma.hip: every quad workgroup loads every token row of
+// its item, so x costs NT times the address and cache work of the weights.
+// Here a workgroup owns four quads (256 weight rows) and the whole K; each
+// 128-k chunk of the item's x rows (NT x 16 tokens, bf16) is loaded once
+// into LDS and read by all four waves.  Wave w computes quad 4qb+w against
+// all NT column tiles:
+//   A: the quad's 4 KB tile of the chunk, 16 bytes per lane per row group,
+//      decoded with v_cvt_scalef32_pk_bf16_fp4 (block scale applied), two
+//      chunks of weights in flight ahead of the MFMAs;
+//   B: lane (c, g) reads elements 32g + 8q .. +7 of token row c from LDS
+//      (rows padded to 272 bytes: a quarter-wave's 16-byte reads then cover
+//      all banks once);
+//   D: 16 rows x 16 tokens per (row group, tile), fp32.
+// x is staged one chunk ahead through double-buffered LDS with
+// unconditional loads (rows past the item repeat its last token: they only
+// feed output columns that are never stored).  No cross-wave reduction is
+// needed: each wave ends with its quad's complete sums.
+#include "device_common.h"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_WIDE_WAVES_PER_EU
+#define MOE_WIDE_WAVES_PER_EU 2
+#endif
+#ifndef MOE_WIDE_WBUF
+#define MOE_WIDE_WBUF 2
+#endif
+
+constexpr int kWThreads = 256;
+constexpr int kWQuads = 4;                     // quads per workgroup (one per wave)
+constexpr int kWMaxTiles = kMfmaItemTok / 16;  // 4
+constexpr int kXRow = 272;                     // LDS bytes per staged token row (256 + 16)
+constexpr int kGroups = 4;
+
+struct WSmem {
+    alignas(16) uint8_t x[2][kWMaxTiles * 16 * kXRow];  // [buffer][token row][272]
+};
+
+struct WChunk {
+    uint4 w[kGroups];
+    uint32_t s;
+};
+
+__device__ inline void load_chunk(const uint8_t* tiles, const uint8_t* tscales, int chunk, WChunk& b) {
+    const int lane = threadIdx.x % kWave;
+    const uint8_t* t = tiles + (int64_t)chunk * 4096 + lane * 16;
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++) b.w[rg] = load_stream16(t + rg * 1024);
+    b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)chunk * 256 + lane * 4);
+}
+
+// x staging: thread tid copies 16 bytes (8 bf16) of token row 16n + tid/16
+// for n < NT: elements 8*(tid % 16) .. +7 of the chunk.
+template <int NT>
+struct XStage {
+    uint4 v[NT];
+};
+
+template <int NT>
+__device__ inline void x_load(const uint16_t* const (&rows)[NT], int chunk, XStage<NT>& st) {
+#pragma unroll
+    for (int n = 0; n < NT; n++)
+        st.v[n] = *reinterpret_cast<const uint4*>(rows[n] + chunk * 128);
+}
+
+template <int NT>
+__device__ inline void x_store(WSmem& sm, int buf, const XStage<NT>& st) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int n = 0; n < NT; n++)
+        *reinterpret_cast<uint4*>(&sm.x[buf][(16 * n + tid / 16) * kXRow + 16 * (tid % 16)]) = st.v[n];
+}
+
+// The 16*NT MFMAs of one chunk: weights b (this wave's quad), x from LDS
+// buffer `buf`.
+template <int NT>
+__device__ inline void chunk_mfma(const WSmem& sm, int buf, const WChunk& b,
+                                  f32x4_t (&acc)[kGroups][NT]) {
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        bf16x8_t B[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            B[t] = *reinterpret_cast<const bf16x8_t*>(
+                &sm.x[buf][(16 * t + c) * kXRow + 64 * g + 16 * q]);
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++) {
+            const bf16x8_t A = decode8(word_of(b.w[rg], q), e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[t], acc[rg][t], 0, 0, 0);
+        }
+    }
+}
+
+// Main loop of one workgroup over all `chunks` chunks.  live: this wave's
+// quad exists (all waves stage x and meet every barrier either way).
+template <int NT>
+__device__ inline void wide_mainloop(const uint8_t* tiles, const uint8_t* tscales, bool live,
+                                     const uint16_t* const (&rows)[NT], int chunks, WSmem& sm,
+                                     f32x4_t (&acc)[kGroups][NT]) {
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    XStage<NT> st;
+    x_load<NT>(rows, 0, st);
+#if MOE_WIDE_WBUF == 3
+    WChunk w0, w1, w2;
+    if (live) {
+        load_chunk(tiles, tscales, 0, w0);
+        if (chunks > 1) load_chunk(tiles, tscales, 1, w1);
+    }
+#else
+    WChunk w0, w1;
+    if (live) load_chunk(tiles, tscales, 0, w0);
+#endif
+    x_store<NT>(sm, 0, st);
+    __syncthreads();
+    // weight buffers in rotation: chunk s + WBUF - 1 is loaded while s computes
+    auto step = [&](int s, WChunk& cur, WChunk& ahead) {
+        const int nxt = s + 1 < chunks ? s + 1 : s;
+        x_load<NT>(rows, nxt, st);
+        if (live && s + MOE_WIDE_WBUF - 1 < chunks)
+            load_chunk(tiles, tscales, s + MOE_WIDE_WBUF - 1, ahead);
+        if (live) chunk_mfma<NT>(sm, s & 1, cur, acc);
+        x_store<NT>(sm, (s & 1) ^ 1, st);
+        __syncthreads();
+    };
+    int s = 0;
+    while (true) {
+#if MOE_WIDE_WBUF == 3
+        if (s >= chunks) break;
+        step(s, w0, w2);
+        if (++s >= chunks) break;
+        step(s, w1, w0);
+        if (++s >= chunks) break;
+        step(s, w2, w1);
+        ++s;
+#else
+        if (s >= chunks) break;
+        step(s, w0, w1);
+        if (++s >= chunks) break;
+        step(s, w1, w0);
+        ++s;
+#endif
+    }
+}
+
+template <int NT>
+__device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int K = a.H, chunks = K / 128, quads = a.I / 32;
+    const int quad = kWQuads * qb + w;  // quads % 4 == 0: always live
+    const int64_t quad_id = (int64_t)e * quads + quad;
+    const uint16_t* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; n++) {
+        const int j = min(16 * n + tid / 16, m - 1);
+        rows[n] = a.x + (int64_t)(a.sorted[row0 + j] / a.k) * K + 8 * (tid % 16);
+    }
+    f32x4_t acc[kGroups][NT];
+    wide_mainloop<NT>(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, true, rows,
+                      chunks, sm, acc);
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if (j >= m) continue;
+        uint16_t* hrow = a.h + (int64_t)(row0 + j) * a.I + 32 * quad + 4 * g;
+#pragma unroll
+        for (int rg = 0; rg < 2; rg++) {
+            ushort4 o;
+            o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
+            o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
+            o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
+            o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
+            *reinterpret_cast<ushort4*>(hrow + 16 * rg) = o;
+        }
+    }
+}
+
+template <int NT>
+__device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int K = a.I, chunks = K / 128, quads = a.H / 64;
+    const int quad = kWQuads * qb + w;
+    const bool live = quad < quads;
+    const int64_t quad_id = (int64_t)e * quads + (live ? quad : 0);
+    const uint16_t* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; n++) {
+        const int j = min(16 * n + tid / 16, m - 1);
+        rows[n] = a.h + (int64_t)(row0 + j) * K + 8 * (tid % 16);
+    }
+    f32x4_t acc[kGroups][NT];
+    wide_mainloop<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
+                      chunks, sm, acc);
+    if (!live) return;
+    const int n0 = 64 * quad;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if (j >= m) continue;
+        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++) {
+            // agent-coherent stores: the combining wave may run on another XCD
+            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
+            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // every y store of this wave has completed before it counts the tile
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    int token = -1;
+    bool last = false;
+    if (lane < m) {
+        token = a.sorted[row0 + lane] / a.k;
+        last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
+    }
+    uint64_t todo = __ballot(last);
+    while (todo) {
+        const int src = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int t = __builtin_amdgcn_readlane(token, src);
+        // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
+        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
+    }
+}
+
+// gate_up: blockIdx.x = item * (I / 128) + quad block (quads 4qb..4qb+3)
+__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_gate_up_kernel(GemmArgs a) {
+    __shared__ WSmem sm;
+    const int qblocks = a.I / 128;
+    const int item = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
+    if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
+    const int4 it = a.items[item];
+    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+    switch ((m + 15) / 16) {
+        case 1: wide_gate_up<1>(a, qb, e, row0, m, sm); break;
+#if MOE_WIDE_ITEM_TOK > 32
+        case 2: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
+        case 3: wide_gate_up<3>(a, qb, e, row0, m, sm); break;
+        default: wide_gate_up<4>(a, qb, e, row0, m, sm); break;
+#else
+        default: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
+#endif
+    }
+}
+
+// down: blockIdx.x = item * ceil(H / 256) + quad block; a quad is also the
+// combine tile (the last finisher of a token's k experts combines it)
+__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_kernel(GemmArgs a) {
+    __shared__ WSmem sm;
+    const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
+    const int item = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
+    if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
+    const int4 it = a.items[item];
+    const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+    switch ((m + 15) / 16) {
+        case 1: wide_down<1>(a, qb, e, row0, m, sm); break;
+#if MOE_WIDE_ITEM_TOK > 32
+        case 2: wide_down<2>(a, qb, e, row0, m, sm); break;
+        case 3: wide_down<3>(a, qb, e, row0, m, sm); break;
+        default: wide_down<4>(a, qb, e, row0, m, sm); break;
+#else
+        default: wide_down<2>(a, qb, e, row0, m, sm); break;
+#endif
+    }
+}
+
+}  // namespace
+
+hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
+    wide_gate_up_kernel<<<max_items * (a.I / 128), kWThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream) {
+    const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
+    wide_down_kernel<<<max_items * qblocks, kWThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -195,7 +195,10 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
     const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
     const bool mx8 = o.act_format == MOE_ACT_MXFP8;
-    const int item_tok = mx8 ? moe::kMx8Tok : moe::kMfmaTok;
+    // bf16 MFMA items: 16 tokens, or up to 64 when experts average >= 8
+    // tokens (an expert's weights are then read once per 64 tokens)
+    const bool wide = (int64_t)T * k >= (int64_t)moe::kMfmaWideMeanTok * E;
+    const int item_tok = mx8 ? moe::kMx8Tok : wide ? moe::kMfmaItemTok : moe::kMfmaTok;
     if (mx8) {  // x is encoded in the routing stage (events [0]..[1])
         err = moe::launch_quantize_x_mxfp8((const uint16_t*)x, T, H, ws->x_codes, ws->x_scales, st);
         if (err != hipSuccess) return hip_fail(err, "quantize x");
@@ -248,11 +251,12 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     } else {
         a.list = ws->mfma_list;
         a.list_meta = moe::kMetaNumMfma;
-        const int max_items = max_active + S / moe::kMfmaTok + 1;
-        err = moe::launch_mfma_gate_up(a, max_items, st);
+        const int max_items = max_active + S / item_tok + 1;
+        err = wide ? moe::launch_wide_gate_up(a, max_items, st)
+                   : moe::launch_mfma_gate_up(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-        err = moe::launch_mfma_down(a, max_items, st);
+        err = wide ? moe::launch_wide_down(a, max_items, st) : moe::launch_mfma_down(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "down");
     }
     if ((err = mark(3)) != hipSuccess) return hip_fail(err, "hipEventRecord");

@@ -38,7 +38,16 @@ constexpr int kColTile = 2 * kDownUnits;
 // gate_up tile is kMfmaRows gate rows with their up rows, a down tile is
 // kMfmaDownRows output rows (also its combine tile width); the 4 waves of a
 // workgroup split K.
-constexpr int kMfmaTok = 16;
+constexpr int kMfmaTok = 16;      // tokens per MFMA column tile
+#ifndef MOE_WIDE_ITEM_TOK
+#define MOE_WIDE_ITEM_TOK 64
+#endif
+constexpr int kMfmaItemTok = MOE_WIDE_ITEM_TOK;  // tokens per wide item of the bf16 MFMA path
+// wide items when the layer averages at least this many tokens per expert
+#ifndef MOE_WIDE_MEAN_TOK
+#define MOE_WIDE_MEAN_TOK 8
+#endif
+constexpr int kMfmaWideMeanTok = MOE_WIDE_MEAN_TOK;
 // MXFP8 (prefill) path: items of up to kMx8Tok tokens (eight 16-token MFMA
 // column tiles), weights in the same tile layout.
 constexpr int kMx8Tok = 128;
@@ -106,7 +115,7 @@ struct GemmArgs {
 
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch.
-// item_tok: tokens per MFMA item (kMfmaTok for bf16, kMx8Tok for MXFP8).
+// item_tok: tokens per MFMA item (kMfmaItemTok for bf16, kMx8Tok for MXFP8).
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
                         int gemv_max_tokens, int path, int item_tok, hipStream_t stream);
 // GEMV path: gate_up (+ SiLU * up -> h), then down (-> y) whose last
@@ -115,9 +124,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const Workspac
 hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t stream);
 hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream);
 // MFMA path: same contract, items from the route's MFMA item list;
-// max_items bounds their number.
+// max_items bounds their number.  Items of at most kMfmaTok tokens (split-K
+// kernels) or, for the wide kernels, up to kMfmaItemTok tokens.
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream);
 // MXFP8 (prefill) path: encode x per token along H, then the scaled
 // FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue).
 hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* codes,

@@ -226,6 +226,18 @@ def test_forward_one_hot_expert_many_tokens(torch_dev, M, oracle_lib, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_forward_wide_items_ragged(torch_dev, M, oracle_lib, path):
+    """Enough tokens per expert for the wide MFMA items (up to 64 tokens):
+    expert 1 takes all 100 tokens first (items of 64 and 36 tokens), the
+    other slots spread over three experts."""
+    cfg = Config("wide", "wide_t100_e4_h256_i256_k2", 100, 4, 256, 256, 2, "normal", "bf16", 17)
+    logits = make_logits(cfg)
+    logits[:, 1] += 100.0
+    _parity(M, oracle_lib, cfg, get_layer(cfg, logits=logits), list(range(0, cfg.T, 3)) + [99],
+            path=path, logits=logits)
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T,k", [(1, 1), (1, 8), (2, 5)])
 def test_forward_small_edges(torch_dev, M, oracle_lib, T, k, path):
     cfg = Config("edge", f"edge_t{T}_e8_h256_i128_k{k}", T, 8, 256, 128, k, "normal", "bf16", 21 + T)
