@@ -29,9 +29,10 @@
 // wt, wt+2, wt+4, wt+6 of 16 tokens (4 row groups x 4 column tiles = 16
 // MFMAs per 128-k chunk).
 // A comes straight from global memory in operand order (one 1 KB wave load
-// per row group); B, shared by the two waves of a token half, is staged per
-// chunk through double-buffered LDS (rows padded to 144 bytes so that the
-// 16-byte operand reads of a quarter-wave hit distinct banks).  The token
+// per row group); B, shared by the two waves of a token half, goes from
+// global memory directly into double-buffered LDS (global_load_lds, 16
+// bytes per lane, lane l at byte 16l of the wave's 1 KB destination),
+// XOR-swizzled so that operand reads are free of bank conflicts.  The token
 // rows of x are gathered through the routing order; h rows are already in
 // that order.
 #include "device_common.h"
@@ -50,8 +51,6 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kPfThreads = 256;
 constexpr int kPfTiles = 4;               // 16-token column tiles per wave
-constexpr int kBRow = 144;                // LDS bytes per staged token row
-constexpr int kStageRows = kMx8Tok / 32;  // token rows staged per thread (4)
 
 static_assert(kMx8Tok == 128, "the prefill tiling assumes 128-token items");
 
@@ -128,51 +127,49 @@ quantize_x_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
     scales[b] = s;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Staged B of one chunk: 128 token rows of 128 code bytes, 16-byte piece p
+// of row r stored in slot p ^ ((r >> 1) & 7).  A 16-lane quarter of an
+// operand read (rows c = 0..15, one piece) then covers the 64 banks once.
 struct PfSmem {
-    alignas(16) uint8_t b[2][kMx8Tok * kBRow];  // staged B codes, [buffer][token][144]
-    // staged B scales: the chunk's 4 blocks per token in [0, 128); every
-    // thread stores one word, threads 128..255 into the unused upper half
-    alignas(16) uint32_t bs[2][kPfThreads];
+    alignas(16) uint8_t b[2][kMx8Tok * 128];
+    alignas(16) uint32_t bs[2][kMx8Tok];  // the chunk's 4 block scales per token
 };
 
-// The B rows this thread stages: codes of token rows 32q + tid/8 (piece
-// tid % 8 of each 128-byte chunk) and the scales of token row tid (threads
-// >= 128 load row m-1 again).  Rows past the item's m tokens repeat row
-// m-1: they only feed
-// output columns that are never stored, and keeping every load
-// unconditional lets the loads of the next chunk stay in flight across the
-// MFMAs of the current one.
+__device__ inline int b_slot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+
+// Where this lane's direct-to-LDS loads come from.  Wave w fills LDS rows
+// 32w .. 32w+31 of a chunk with four 1 KB loads (lane l: row 32w + 8i +
+// l/8, slot l % 8); waves 0 and 1 also load the scale words of tokens
+// 64w + l.  Rows past the item's m tokens repeat row m-1: they only feed
+// output columns that are never stored.
 struct StageSrc {
-    const uint8_t* row[kStageRows];
-    const uint8_t* srow;
+    const uint8_t* row[4];  // code bytes of the row's piece for this lane, chunk 0
+    const uint8_t* srow;    // scale bytes of this lane's token, chunk 0 (waves 0, 1)
 };
 
-struct StageRegs {
-    uint4 v[kStageRows];
-    uint32_t s;
-};
-
-__device__ __attribute__((always_inline)) inline void stage_load(const StageSrc& src, int chunk, StageRegs& r) {
+__device__ inline void stage_issue(const StageSrc& src, int chunk, PfSmem& sm, int buf) {
+    const int w = threadIdx.x / kWave;
 #pragma unroll
-    for (int q = 0; q < kStageRows; q++)
-        r.v[q] = *reinterpret_cast<const uint4*>(src.row[q] + chunk * 128);
-    r.s = *reinterpret_cast<const uint32_t*>(src.srow + chunk * 4);
+    for (int i = 0; i < 4; i++)
+        __builtin_amdgcn_global_load_lds(src.row[i] + chunk * 128,
+                                         (lds_void_t*)&sm.b[buf][(32 * w + 8 * i) * 128], 16, 0, 0);
+    if (w < 2)
+        __builtin_amdgcn_global_load_lds(src.srow + chunk * 4, (lds_void_t*)&sm.bs[buf][64 * w], 4,
+                                         0, 0);
 }
 
-__device__ __attribute__((always_inline)) inline void stage_store(PfSmem& sm, int buf, const StageRegs& r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int q = 0; q < kStageRows; q++)
-        *reinterpret_cast<uint4*>(&sm.b[buf][(32 * q + tid / 8) * kBRow + 16 * (tid % 8)]) = r.v[q];
-    sm.bs[buf][tid] = r.s;
-}
+// lane's LDS row for staging load i of wave w, and the piece it carries
+__device__ inline int stage_row(int i) { return 32 * (threadIdx.x / kWave) + 8 * i + (threadIdx.x % kWave) / 8; }
+__device__ inline int stage_piece(int i) { return b_slot(stage_row(i), threadIdx.x % 8); }
 
 struct AOperand {
     uint4 w[4];  // row groups 0..3 of the quad
     uint32_t s;  // their four scale bytes
 };
 
-__device__ __attribute__((always_inline)) inline void load_a(const uint8_t* tiles, const uint8_t* tscales, int chunk, AOperand& a) {
+__device__ inline void load_a(const uint8_t* tiles, const uint8_t* tscales, int chunk, AOperand& a) {
     const int lane = threadIdx.x % kWave;
     const uint8_t* t = tiles + (int64_t)chunk * 4096 + lane * 16;
 #pragma unroll
@@ -184,36 +181,32 @@ __device__ __attribute__((always_inline)) inline void load_a(const uint8_t* tile
 // (interleaved, so the two token waves stay balanced on ragged items).
 __device__ inline int tile_token(int t, int wt, int c) { return 16 * (2 * t + wt) + c; }
 
-// One 128-k chunk: staging of chunk `nxt` into registers, A of chunk `nxt`
-// into an, the 4*NT MFMAs of chunk `s` from LDS buffer `cur` and A ac, and
-// the staged registers stored into the other buffer.  The last step reloads
-// and restages its own chunk into the idle buffer (nothing reads it again):
-// with no branch around them the loads are issued before the MFMAs.
 template <int NT>
-__device__ __attribute__((always_inline)) inline void pf_step(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
-                               int s, int chunks, int cur, PfSmem& sm, const AOperand& ac,
-                               AOperand& an, f32x4_t (&acc)[4][kPfTiles]) {
+struct BOperands {
+    i32x8_t v[NT > 0 ? NT : 1];
+    int s[NT > 0 ? NT : 1];
+};
+
+// this wave's B operands of the chunk in LDS buffer `buf`
+template <int NT>
+__device__ inline void read_b(const PfSmem& sm, int buf, BOperands<NT>& b) {
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int wt = (threadIdx.x / kWave) >> 1;
-    const int nxt = s + 1 < chunks ? s + 1 : s;
-    StageRegs st;
-    stage_load(src, nxt, st);
-    load_a(tiles, tscales, nxt, an);
-    // keep the loads ahead of the MFMAs: the staging store at the end of the
-    // step is the first use of st, a's first use is the next step
-    if (MOE_PF_SCHED_BARRIERS) __builtin_amdgcn_sched_barrier(0);
-    i32x8_t B[NT > 0 ? NT : 1];
-    int sb[NT > 0 ? NT : 1];
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         const int row = tile_token(t, wt, c);
-        const uint8_t* bp = &sm.b[cur][row * kBRow + 16 * g];
-        const uint4 lo = *reinterpret_cast<const uint4*>(bp);
-        const uint4 hi = *reinterpret_cast<const uint4*>(bp + 64);
-        sb[t] = (int)((sm.bs[cur][row] >> (8 * g)) & 0xffu);
-        B[t] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint8_t* base = &sm.b[buf][row * 128];
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * b_slot(row, g));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * b_slot(row, g + 4));
+        b.s[t] = (int)((sm.bs[buf][row] >> (8 * g)) & 0xffu);
+        b.v[t] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
+}
+
+template <int NT>
+__device__ inline void chunk_mfma(const AOperand& ac, const BOperands<NT>& b,
+                                  f32x4_t (&acc)[4][kPfTiles]) {
 #pragma unroll
     for (int rg = 0; rg < 4; rg++) {
         const i32x8_t A = i32x8_t{(int)ac.w[rg].x, (int)ac.w[rg].y, (int)ac.w[rg].z,
@@ -222,17 +215,21 @@ __device__ __attribute__((always_inline)) inline void pf_step(const uint8_t* til
 #pragma unroll
         for (int t = 0; t < NT; t++)
             acc[rg][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                A, B[t], acc[rg][t], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, sb[t]);
+                A, b.v[t], acc[rg][t], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, b.s[t]);
     }
-    if (MOE_PF_SCHED_BARRIERS) __builtin_amdgcn_sched_barrier(0);
-    stage_store(sm, cur ^ 1, st);
-    __syncthreads();
 }
 
 // The main loop of one workgroup: acc[rg][t] = quad rows (group rg) x
 // column tile t of this wave (t < NT), summed over all `chunks` 128-k
-// chunks.  tiles/tscales point at this wave's quad.  Every wave runs the
-// same number of barriers whatever its NT.
+// chunks.  tiles/tscales point at this wave's quad.
+//
+// Step s: wait for this wave's loads (its share of chunk s in LDS buffer
+// s%2, A of chunk s) and meet the other waves at a barrier; read the B
+// operands of chunk s; issue A of chunk s+1 and the direct-to-LDS loads of
+// chunk s+1 into the other buffer (whose readers all passed this barrier);
+// run the MFMAs.  The loads of chunk s+1 thus fly during the MFMAs of chunk
+// s, and no staging registers are needed.  Every wave runs the same number
+// of barriers whatever its NT.
 template <int NT>
 __device__ inline void pf_mainloop(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
                                    int chunks, PfSmem& sm, f32x4_t (&acc)[4][kPfTiles]) {
@@ -241,17 +238,23 @@ __device__ inline void pf_mainloop(const uint8_t* tiles, const uint8_t* tscales,
 #pragma unroll
         for (int t = 0; t < kPfTiles; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     AOperand a0, a1;
-    {
-        StageRegs st;
-        stage_load(src, 0, st);
-        load_a(tiles, tscales, 0, a0);
-        stage_store(sm, 0, st);
-        __syncthreads();
-    }
+    stage_issue(src, 0, sm, 0);
+    load_a(tiles, tscales, 0, a0);
+    auto step = [&](int s, const AOperand& acur, AOperand& anext) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of chunk s
+        __syncthreads();                      // everyone's
+        BOperands<NT> b;
+        read_b<NT>(sm, s & 1, b);
+        if (s + 1 < chunks) {
+            load_a(tiles, tscales, s + 1, anext);
+            stage_issue(src, s + 1, sm, (s & 1) ^ 1);
+        }
+        chunk_mfma<NT>(acur, b, acc);
+    };
     for (int s = 0; s < chunks; s += 2) {
-        pf_step<NT>(tiles, tscales, src, s, chunks, 0, sm, a0, a1, acc);
+        step(s, a0, a1);
         if (s + 1 >= chunks) break;
-        pf_step<NT>(tiles, tscales, src, s + 1, chunks, 1, sm, a1, a0, acc);
+        step(s + 1, a1, a0);
     }
 }
 
@@ -293,11 +296,11 @@ mx8_gate_up_kernel(GemmArgs a) {
     const int64_t quad_id = (int64_t)e * quads + quad;
     StageSrc src;
 #pragma unroll
-    for (int q = 0; q < kStageRows; q++) {
-        const int j = min(32 * q + tid / 8, m - 1);
-        src.row[q] = a.xq + (int64_t)(a.sorted[row0 + j] / a.k) * K + 16 * (tid % 8);
+    for (int i = 0; i < 4; i++) {
+        const int j = min(stage_row(i), m - 1);
+        src.row[i] = a.xq + (int64_t)(a.sorted[row0 + j] / a.k) * K + 16 * stage_piece(i);
     }
-    src.srow = a.xs + (int64_t)(a.sorted[row0 + min(tid, m - 1)] / a.k) * (K / 32);
+    src.srow = a.xs + (int64_t)(a.sorted[row0 + min(64 * (w & 1) + lane, m - 1)] / a.k) * (K / 32);
     const int ntile = uniform(wave_tiles(m, wt));
     f32x4_t acc[4][kPfTiles];
     pf_gemm(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, src, chunks, ntile, sm,
@@ -358,11 +361,11 @@ mx8_down_kernel(GemmArgs a) {
     const int64_t quad_id = (int64_t)e * quads + quad;
     StageSrc src;
 #pragma unroll
-    for (int q = 0; q < kStageRows; q++) {
-        const int j = min(32 * q + tid / 8, m - 1);
-        src.row[q] = a.hq + (int64_t)(row0 + j) * K + 16 * (tid % 8);
+    for (int i = 0; i < 4; i++) {
+        const int j = min(stage_row(i), m - 1);
+        src.row[i] = a.hq + (int64_t)(row0 + j) * K + 16 * stage_piece(i);
     }
-    src.srow = a.hs + (int64_t)(row0 + min(tid, m - 1)) * (K / 32);
+    src.srow = a.hs + (int64_t)(row0 + min(64 * (w & 1) + lane, m - 1)) * (K / 32);
     const int ntile = uniform(wave_tiles(m, wt));
     f32x4_t acc[4][kPfTiles];
     pf_gemm(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, src, chunks, ntile, sm,
