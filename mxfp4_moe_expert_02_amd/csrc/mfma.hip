@@ -239,43 +239,15 @@ mfma_gate_up_kernel(GemmArgs a) {
     gate_up_item<1>(a, quad, e, row0, m, red);
 }
 
-// down body for items of NT column tiles (see mfma_down_kernel)
+// Epilogue of a down tile (one wave holding the summed accumulator of
+// quad `quad` for the item's m tokens): y rows through agent-coherent
+// stores, then the (token, quad) completion counts; the wave that completes
+// a token's k experts on the quad combines those 64 columns.
 template <int NT>
-__device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, int m,
-                                 f32x4_t* red) {
+__device__ inline void down_epilogue(const GemmArgs& a, int quad, int row0, int m,
+                                     const f32x4_t (&acc)[kGroups][NT]) {
     const int quads = a.H / 64;
-    const int w = threadIdx.x / kWave, half = w & 1;
-    const int quad = pair * 2 + (w >> 1);
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
-    const int K = a.I, chunks = K / 128;
-    const bool live = quad < quads;
-    f32x4_t acc[kGroups][NT];
-    if (live) {
-        const int64_t quad_id = (int64_t)e * quads + quad;
-        const int hc = (chunks + 1) / 2;
-        mfma_quad<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256,
-                      [&](const uint16_t* (&xrow)[NT]) {
-#pragma unroll
-                          for (int t = 0; t < NT; t++) {
-                              const int j = 16 * t + c;
-                              xrow[t] = j < m ? a.h + (int64_t)(row0 + j) * K : nullptr;
-                          }
-                      },
-                      half ? hc : 0, half ? chunks : hc, acc);
-        if (half) {
-#pragma unroll
-            for (int rg = 0; rg < kGroups; rg++)
-#pragma unroll
-                for (int t = 0; t < NT; t++)
-                    red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
-        }
-    }
-    __syncthreads();
-    if (!live || half) return;
-#pragma unroll
-    for (int rg = 0; rg < kGroups; rg++)
-#pragma unroll
-        for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
     const int n0 = 64 * quad;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
@@ -311,6 +283,46 @@ __device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, i
         // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
         a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
     }
+}
+
+// down body for items of NT column tiles (see mfma_down_kernel)
+template <int NT>
+__device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, int m,
+                                 f32x4_t* red) {
+    const int quads = a.H / 64;
+    const int w = threadIdx.x / kWave, half = w & 1;
+    const int quad = pair * 2 + (w >> 1);
+    const int lane = threadIdx.x % kWave, c = lane % 16;
+    const int K = a.I, chunks = K / 128;
+    const bool live = quad < quads;
+    f32x4_t acc[kGroups][NT];
+    if (live) {
+        const int64_t quad_id = (int64_t)e * quads + quad;
+        const int hc = (chunks + 1) / 2;
+        mfma_quad<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256,
+                      [&](const uint16_t* (&xrow)[NT]) {
+#pragma unroll
+                          for (int t = 0; t < NT; t++) {
+                              const int j = 16 * t + c;
+                              xrow[t] = j < m ? a.h + (int64_t)(row0 + j) * K : nullptr;
+                          }
+                      },
+                      half ? hc : 0, half ? chunks : hc, acc);
+        if (half) {
+#pragma unroll
+            for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
+        }
+    }
+    __syncthreads();
+    if (!live || half) return;
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
+    down_epilogue<NT>(a, quad, row0, m, acc);
 }
 
 // down: a workgroup takes two quads (output rows 64q..64q+63), each split
