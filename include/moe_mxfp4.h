@@ -84,6 +84,17 @@ extern "C" {
 #define MOE_PATH_GEMV 1      /* VALU GEMV with DPP reductions (row-major weights) */
 #define MOE_PATH_MFMA 2      /* bf16 matrix cores (weights in the MFMA tile layout) */
 
+/* How the expert GEMMs are launched (moe_mxfp4_options.launch); the bf16
+ * MFMA path only (the other paths always run split) */
+#define MOE_LAUNCH_AUTO 0    /* the library's choice for the path */
+#define MOE_LAUNCH_SPLIT 1   /* gate_up and down (+ combine) as two kernels */
+#define MOE_LAUNCH_FUSED 2   /* one persistent kernel after the route: workgroups
+                                dequeue gate_up units, then down units; a down unit
+                                waits (bounded) for its item's gate_up units.  The
+                                pages' persistent, gap-free execution (tilert.ai
+                                blog, first leap; bjdmk.com.cn news page, road to
+                                1000 tokens/s) applied to this layer */
+
 /* Weight layouts (moe_mxfp4_options.weight_layout) */
 #define MOE_LAYOUT_ROWS 0    /* row-major packed codes + scales, as described above */
 #define MOE_LAYOUT_TILES 1   /* the MFMA tile layout written by moe_mxfp4_prepack */
@@ -113,7 +124,8 @@ typedef struct moe_mxfp4_options {
     /* Optional hipEvent_t handles recorded on `stream` at the stage
      * boundaries: [0] before routing, [1] after routing (and, with
      * MOE_ACT_MXFP8, after the encoding of x), [2] after the
-     * gate_up GEMM, [3] after the down GEMM and the combine.  Only the
+     * gate_up GEMM (after the single expert kernel in a fused launch),
+     * [3] after the down GEMM and the combine.  Only the
      * first num_events (<= 4) are recorded; used to time the kernels. */
     void* const* events;
     int32_t num_events;
@@ -121,6 +133,14 @@ typedef struct moe_mxfp4_options {
      * W_gate_up, W_down and the scales.  ROWS runs the GEMV path, TILES the
      * MFMA path; asking for the other path returns MOE_E_OPTION. */
     int32_t weight_layout;
+    /* MOE_LAUNCH_AUTO, MOE_LAUNCH_SPLIT or MOE_LAUNCH_FUSED (see above) */
+    int32_t launch;
+    /* Optional [1] int32 device output: nonzero if, in the fused launch, a
+     * down unit gave up waiting for its gate_up units (it then went on, and
+     * out is not to be trusted).  The waits are bounded at about four
+     * million polls; a correct launch never reaches that.  0 in split
+     * launches. */
+    int32_t* wait_error;
 } moe_mxfp4_options;
 
 /* Allocate the workspace on the current device for layers with at most

@@ -33,6 +33,9 @@ MOE_PATH_GEMV = 1
 MOE_PATH_MFMA = 2
 MOE_LAYOUT_ROWS = 0
 MOE_LAYOUT_TILES = 1
+MOE_LAUNCH_AUTO = 0
+MOE_LAUNCH_SPLIT = 1
+MOE_LAUNCH_FUSED = 2
 
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
@@ -56,7 +59,8 @@ class moe_mxfp4_options(ctypes.Structure):
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("sorted", ctypes.c_void_p), ("x_codes", ctypes.c_void_p),
                 ("x_scales", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
-                ("num_events", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
+                ("num_events", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
+                ("launch", ctypes.c_int32), ("wait_error", ctypes.c_void_p)]
 
 
 _lib = None
@@ -139,6 +143,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                          gemm_path: int = MOE_PATH_AUTO, ids=None, weights=None,
                          counts=None, offsets=None, sorted=None, x_codes=None,
                          x_scales=None, events=None, weight_layout: int = MOE_LAYOUT_ROWS,
+                         launch: int = MOE_LAUNCH_AUTO, wait_error=None,
                          check: bool = True, validate: bool = True) -> int:
     """Enqueue one layer on ``stream`` (default: torch's current stream).
 
@@ -146,8 +151,9 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     W_down [E,H,I/2] uint8, scales = (gate_up [E,2I,H/32], down [E,H,I/32])
     uint8, out [T,H] bfloat16.  ``validate=False`` skips the Python-side
     shape checks so the library's own validation can be exercised.
-    ``events``: up to 5 torch.cuda.Event (timing enabled) recorded by the
-    library at its stage boundaries.
+    ``events``: up to 4 torch.cuda.Event (timing enabled) recorded by the
+    library at its stage boundaries.  ``launch``: MOE_LAUNCH_*;
+    ``wait_error``: optional int32 [1] device tensor (see the header).
     """
     import torch
     if validate:
@@ -176,7 +182,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     opt = moe_mxfp4_options(act_format, gemm_path, _ptr(ids), _ptr(weights), _ptr(counts),
                             _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
                             ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
-                            n_ev, weight_layout)
+                            n_ev, weight_layout, launch, _ptr(wait_error))
     T = x.shape[0] if x is not None else 0
     rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,

@@ -54,6 +54,30 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Four bf16 of h through an agent-coherent 8-byte store: in the
+// single-launch layer the down unit that reads them may run on another XCD
+// in the same launch (its L2 never held these lines in this launch).
+__device__ inline void store_h4(uint16_t* dst, ushort4 v) {
+    const uint64_t u = (uint64_t)v.x | ((uint64_t)v.y << 16) | ((uint64_t)v.z << 32) |
+                       ((uint64_t)v.w << 48);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin (sleeping) until *count >= need, reading it agent-coherently.  Gives
+// up after a bounded number of polls (well beyond any real wait) and raises
+// *err instead of hanging; the caller goes on either way.
+constexpr int kSpinLimit = 1 << 22;
+__device__ inline void wait_count(const int32_t* count, int need, int32_t* err) {
+    for (int it = 0;; it++) {
+        if (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return;
+        if (it >= kSpinLimit) {
+            atomicOr(err, 1);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // sum_j w[t,j] * y[pos[t,j], n] over the k slots of token t, in slot order
 // j = 0..k-1, fp32.  y is read with agent-coherent loads because other
 // workgroups of the running kernel wrote it.  The slot indices and weights,

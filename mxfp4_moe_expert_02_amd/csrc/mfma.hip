@@ -217,7 +217,7 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, int row0
                 o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
                 o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
                 o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
-                *reinterpret_cast<ushort4*>(hrow + 16 * rg) = o;
+                store_h4(hrow + 16 * rg, o);
             }
         }
     }
@@ -343,6 +343,71 @@ mfma_down_kernel(GemmArgs a) {
     down_item<1>(a, pair, e, row0, m, red);
 }
 
+
+// The expert layer after routing in one persistent launch: every workgroup
+// dequeues units from one counter, first the gate_up units (item, quad),
+// then the down units (item, quad pair), until the queue is exhausted.  A
+// gate_up unit publishes its h rows (agent-coherent stores, completed)
+// before it counts itself done for its item; a down unit first waits until
+// all I/32 gate_up units of its item are done.  No wait can deadlock: the
+// units a down unit waits for were dequeued before it, by workgroups that
+// are running and never wait themselves.  The wait is bounded (wait_count)
+// and raises queue[kQueueError] if it ever gives up.
+#ifndef MOE_FUSED_WAVES_PER_EU
+#define MOE_FUSED_WAVES_PER_EU 2
+#endif
+
+// The expert layer after routing in one persistent launch: every workgroup
+// dequeues units from one counter, first the gate_up units (item, quad),
+// then the down units (item, quad pair), until the queue is exhausted.  A
+// down unit first waits until all I/32 gate_up units of its item are done.
+// No wait can deadlock: the units a down unit waits for were dequeued
+// before it, by workgroups that are running and never wait themselves.
+// The wait is bounded (wait_count) and raises queue[kQueueError] if it ever
+// gives up.
+//
+// Each unit has a workgroup barrier inside (the split-K sum, or the wait),
+// which keeps the four waves within one unit of each other; the LDS of the
+// sums alternates between two buffers, so no barrier is needed between
+// units.  The next unit is dequeued while the current one runs.  Wave 0
+// stores a gate_up unit's h (agent-coherent stores) and alone waits for
+// them to complete before it counts the unit done for its item; the other
+// waves go on with the next unit meanwhile.  Holding a dequeued unit cannot
+// block anyone: a workgroup holds a gate_up unit only while running a
+// gate_up unit, which never waits.
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_FUSED_WAVES_PER_EU)))
+mfma_fused_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[2][kRedGateUp];
+    __shared__ int s_unit[2];
+    const int n_items = uniform(a.meta[kMetaNumMfmaItems]);
+    const int gu_units = a.I / 32, dn_units = (a.H / 64 + 1) / 2;
+    const int n_gu = n_items * gu_units, n_all = n_gu + n_items * dn_units;
+    if (threadIdx.x == 0) s_unit[0] = atomicAdd(&a.queue[kQueueNext], 1);
+    __syncthreads();
+    for (int cur = 0;; cur ^= 1) {
+        const int u = uniform(s_unit[cur]);
+        if (u >= n_all) return;
+        // read by every wave after this unit's barrier
+        if (threadIdx.x == 0) s_unit[cur ^ 1] = atomicAdd(&a.queue[kQueueNext], 1);
+        if (u < n_gu) {
+            const int item = u / gu_units;
+            const int4 it = a.items[item];
+            gate_up_item<1>(a, u % gu_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
+            if (threadIdx.x < kWave) {  // wave 0 stored the h rows
+                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): they are complete
+                if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
+            }
+        } else {
+            const int v = u - n_gu, item = v / dn_units;
+            const int4 it = a.items[item];
+            if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
+            __syncthreads();
+            down_item<1>(a, v % dn_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
@@ -354,6 +419,15 @@ hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int pairs = (a.H / 64 + 1) / 2;
     mfma_down_kernel<<<max_items * pairs, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_fused(const GemmArgs& a, int max_items, hipStream_t stream) {
+    const int64_t units = (int64_t)max_items * (a.I / 32 + (a.H / 64 + 1) / 2);
+    int grid = 0;
+    hipError_t err = resident_grid(reinterpret_cast<const void*>(mfma_fused_kernel), kMfmaThreads, &grid);
+    if (err != hipSuccess) return err;
+    mfma_fused_kernel<<<(int)(units < grid ? units : grid), kMfmaThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

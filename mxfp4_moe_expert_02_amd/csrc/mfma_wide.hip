@@ -181,7 +181,7 @@ __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, 
             o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
             o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
             o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
-            *reinterpret_cast<ushort4*>(hrow + 16 * rg) = o;
+            store_h4(hrow + 16 * rg, o);
         }
     }
 }
@@ -281,6 +281,64 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_ke
     }
 }
 
+
+// The wide kernels in one persistent launch (see mfma_fused_kernel in
+// mfma.hip: the same queue, publication and bounded wait; a gate_up unit
+// is (item, quad block of four quads), and every wave stores h of its quad).
+__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_kernel(GemmArgs a) {
+    __shared__ WSmem sm;
+    __shared__ int s_unit[2];
+    const int n_items = uniform(a.meta[kMetaNumMfmaItems]);
+    const int gu_units = a.I / 128, dn_units = (a.H / 64 + kWQuads - 1) / kWQuads;
+    const int n_gu = n_items * gu_units, n_all = n_gu + n_items * dn_units;
+    // the next unit is dequeued while the current one runs (the atomic's
+    // round trip then costs nothing); holding it cannot block anyone: a
+    // workgroup holds a gate_up unit only while running a gate_up unit,
+    // which never waits
+    if (threadIdx.x == 0) s_unit[0] = atomicAdd(&a.queue[kQueueNext], 1);
+    __syncthreads();
+    for (int cur = 0;; cur ^= 1) {
+        const int u = uniform(s_unit[cur]);
+        if (u >= n_all) return;
+        if (threadIdx.x == 0) s_unit[cur ^ 1] = atomicAdd(&a.queue[kQueueNext], 1);
+        if (u < n_gu) {
+            const int item = u / gu_units, qb = u % gu_units;
+            const int4 it = a.items[item];
+            const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+            switch ((m + 15) / 16) {
+                case 1: wide_gate_up<1>(a, qb, e, row0, m, sm); break;
+#if MOE_WIDE_ITEM_TOK > 32
+                case 2: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
+                case 3: wide_gate_up<3>(a, qb, e, row0, m, sm); break;
+                default: wide_gate_up<4>(a, qb, e, row0, m, sm); break;
+#else
+                default: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
+#endif
+            }
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's h stores completed
+            __syncthreads();
+            if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
+        } else {
+            const int v = u - n_gu, item = v / dn_units, qb = v % dn_units;
+            const int4 it = a.items[item];
+            const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+            if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
+            __syncthreads();
+            switch ((m + 15) / 16) {
+                case 1: wide_down<1>(a, qb, e, row0, m, sm); break;
+#if MOE_WIDE_ITEM_TOK > 32
+                case 2: wide_down<2>(a, qb, e, row0, m, sm); break;
+                case 3: wide_down<3>(a, qb, e, row0, m, sm); break;
+                default: wide_down<4>(a, qb, e, row0, m, sm); break;
+#else
+                default: wide_down<2>(a, qb, e, row0, m, sm); break;
+#endif
+            }
+        }
+        __syncthreads();  // LDS free for the next unit, whose index is now visible
+    }
+}
+
 }  // namespace
 
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
@@ -291,6 +349,16 @@ hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
     wide_down_kernel<<<max_items * qblocks, kWThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_fused(const GemmArgs& a, int max_items, hipStream_t stream) {
+    const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
+    const int64_t units = (int64_t)max_items * (a.I / 128 + qblocks);
+    int grid = 0;
+    hipError_t err = resident_grid(reinterpret_cast<const void*>(wide_fused_kernel), kWThreads, &grid);
+    if (err != hipSuccess) return err;
+    wide_fused_kernel<<<(int)(units < grid ? units : grid), kWThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -57,6 +57,9 @@ size_t layout(Workspace* ws, char* base) {
     ws->col_tiles = (int)(ws->H / moe::kColTile);
     ws->tile_done = (int32_t*)take((size_t)ws->max_tokens * (ws->H / moe::kMfmaDownRows) * 4);
     ws->bhist = (int32_t*)take((S + moe::kRouteSlotBlock - 1) / moe::kRouteSlotBlock * ws->E * 4);
+    ws->max_items = (int)(ws->E + S / moe::kMfmaTok + 1);
+    ws->queue = (int32_t*)take(moe::kQueueWords * 4);
+    ws->gu_done = (int32_t*)take((size_t)ws->max_items * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
@@ -89,6 +92,20 @@ Workspace* current_ws() {
 }
 
 }  // namespace
+
+namespace moe {
+
+hipError_t resident_grid(const void* kernel, int block, int* grid) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
+    if (err != hipSuccess) return err;
+    *grid = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    return hipSuccess;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -168,6 +185,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         return MOE_E_OPTION;
     if (o.num_events < 0 || o.num_events > 4 || (o.num_events > 0 && !o.events))
         return MOE_E_OPTION;
+    if (o.launch != MOE_LAUNCH_AUTO && o.launch != MOE_LAUNCH_SPLIT && o.launch != MOE_LAUNCH_FUSED)
+        return MOE_E_OPTION;
     if (num_tokens == 0) return MOE_OK;
     if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
     if (!scales->gate_up || !scales->down) return MOE_E_NULL;
@@ -235,6 +254,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.xs = ws->x_scales;
     a.hq = ws->h_codes;
     a.hs = ws->h_scales;
+    a.queue = ws->queue;
+    a.gu_done = ws->gu_done;
     if (mx8) {
         const int max_items = max_active + S / moe::kMx8Tok + 1;
         err = moe::launch_mx8_gate_up(a, max_items, st);
@@ -252,12 +273,20 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         a.list = ws->mfma_list;
         a.list_meta = moe::kMetaNumMfma;
         const int max_items = max_active + S / item_tok + 1;
-        err = wide ? moe::launch_wide_gate_up(a, max_items, st)
-                   : moe::launch_mfma_gate_up(a, max_items, st);
-        if (err != hipSuccess) return hip_fail(err, "gate_up");
-        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
-        err = wide ? moe::launch_wide_down(a, max_items, st) : moe::launch_mfma_down(a, max_items, st);
-        if (err != hipSuccess) return hip_fail(err, "down");
+        if (o.launch == MOE_LAUNCH_FUSED) {
+            // one kernel: event [2] marks its end as well as [3]
+            err = wide ? moe::launch_wide_fused(a, max_items, st)
+                       : moe::launch_mfma_fused(a, max_items, st);
+            if (err != hipSuccess) return hip_fail(err, "fused expert layer");
+            if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        } else {
+            err = wide ? moe::launch_wide_gate_up(a, max_items, st)
+                       : moe::launch_mfma_gate_up(a, max_items, st);
+            if (err != hipSuccess) return hip_fail(err, "gate_up");
+            if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+            err = wide ? moe::launch_wide_down(a, max_items, st) : moe::launch_mfma_down(a, max_items, st);
+            if (err != hipSuccess) return hip_fail(err, "down");
+        }
     }
     if ((err = mark(3)) != hipSuccess) return hip_fail(err, "hipEventRecord");
 
@@ -272,6 +301,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         {o.sorted, ws->sorted, (size_t)S * 4},
         {mx8 ? o.x_codes : nullptr, ws->x_codes, (size_t)T * H},
         {mx8 ? o.x_scales : nullptr, ws->x_scales, (size_t)T * (H / 32)},
+        {o.wait_error, ws->queue + moe::kQueueError, 4},
     };
     for (auto& c : copies) {
         if (!c.dst) continue;

@@ -22,6 +22,13 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kRouteSlotBlock = 256;  // slots per block of the multi-block routing sort
 
+// words of Workspace::queue (the single-launch expert layer)
+enum Queue : int {
+    kQueueNext = 0,   // next unit to dequeue
+    kQueueError = 1,  // nonzero: a unit gave up waiting for its gate_up units
+    kQueueWords = 4,
+};
+
 // meta[] words in the workspace
 enum Meta : int {
     kMetaNumGemv = 0,   // active experts on the GEMV path
@@ -74,6 +81,9 @@ struct Workspace {
     int32_t* meta = nullptr;       // [kMetaWords]
     int32_t* tile_done = nullptr;  // [Tmax * H/kMfmaDownRows] finished down tiles per (token, column tile)
     int32_t* bhist = nullptr;      // [ceil(Tmax*kmax/kRouteSlotBlock) * E] per-block expert histograms
+    int32_t* queue = nullptr;      // [kQueueWords] single-launch layer: next unit, error flag
+    int32_t* gu_done = nullptr;    // [E + Tmax*kmax/kMfmaTok + 1] finished gate_up units per MFMA item
+    int max_items = 0;             // entries of mfma_items / gu_done
     int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
     float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order
@@ -111,9 +121,16 @@ struct GemmArgs {
     const int32_t* pos;         // [T*k] slot -> row of y
     uint16_t* out;              // [T, H] bf16
     int col_tiles;
+    // single-launch layer (route, then one kernel for gate_up + down + combine)
+    int32_t* queue;             // [kQueueWords], zeroed by the route
+    int32_t* gu_done;           // [max items] finished gate_up units per item, zeroed by the route
 };
 
 // ---------------------------------------------------------------- launchers
+// Workgroups of `kernel` (block threads, static LDS only) that fit on the
+// current device at once: occupancy per CU x CUs.
+hipError_t resident_grid(const void* kernel, int block, int* grid);
+
 // Each returns the hipError_t of its launch.
 // item_tok: tokens per MFMA item (kMfmaItemTok for bf16, kMx8Tok for MXFP8).
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
@@ -130,6 +147,12 @@ hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream);
+// The same two GEMMs (and the combine) in one persistent launch: workgroups
+// dequeue gate_up units (item, row tile), then down units, each of which
+// waits (bounded) until every gate_up unit of its item has published h.
+// Needs the queue words and gu_done zeroed (the route does it).
+hipError_t launch_mfma_fused(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_wide_fused(const GemmArgs& a, int max_items, hipStream_t stream);
 // MXFP8 (prefill) path: encode x per token along H, then the scaled
 // FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue).
 hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* codes,

@@ -20,7 +20,8 @@
 // Small layers (T*E <= kFusedMaxPairs) route in one workgroup (one
 // launch); larger ones use a grid for top-k and a multi-block counting sort
 // (per-block histograms, one scan, per-block stable scatter).  Both also
-// reset the per-(token, column tile) combine counters.
+// reset the per-(token, column tile) combine counters and the unit queue
+// of the single-launch expert layer.
 #include <float.h>
 #include <limits.h>
 
@@ -230,6 +231,9 @@ __device__ void sort_slots(const int32_t* ids, int S, int E, int T, const Worksp
     for (int i = tid; i < R * E; i += nthr) hist[i] = 0;
     // reset the combine counters of the down kernels (sized for the finest tile)
     for (int i = tid; i < T * (int)(ws.H / kMfmaDownRows); i += nthr) ws.tile_done[i] = 0;
+    // and the unit queue and per-item gate_up counts of the single-launch layer
+    for (int i = tid; i < kQueueWords; i += nthr) ws.queue[i] = 0;
+    for (int i = tid; i < ws.max_items; i += nthr) ws.gu_done[i] = 0;
     __syncthreads();
     if (tid < R) {  // 1. per-range histogram
         const int s0 = tid * L, s1 = min(S, s0 + L);
@@ -332,6 +336,8 @@ route_scan_kernel(int nblk, int E, Workspace ws, int32_t* __restrict__ bhist, in
         s_cnt[e] = run;
         ws.counts[e] = run;
     }
+    for (int i = tid; i < kQueueWords; i += nthr) ws.queue[i] = 0;
+    for (int i = tid; i < ws.max_items; i += nthr) ws.gu_done[i] = 0;
     __syncthreads();
     scan_experts(E, s_cnt, s_off);
     __syncthreads();

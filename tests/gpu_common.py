@@ -31,14 +31,17 @@ def get_layer(cfg: Config, logits=None):
     return _layers[key]
 
 
-def run(M, layer, path=0, debug=False, act=0):
+def run(M, layer, path=0, debug=False, act=0, launch=0, init=True):
     """One forward through the C ABI on every token of the layer; returns
     the requested debug outputs (routing; with MXFP8 also the codes of x)
     as numpy arrays.  out is NaN-filled first, so every element it holds
-    afterwards was written by this call."""
+    afterwards was written by this call.  launch: MOE_LAUNCH_* (the fused
+    launch also returns its wait-error flag as "wait_error"); init=False
+    keeps the current workspace (and whatever an earlier call left in it)."""
     import torch
     c = layer.cfg
-    M.moe_mxfp4_init(c.T, c.E, c.H, c.I, c.k)
+    if init:
+        M.moe_mxfp4_init(c.T, c.E, c.H, c.I, c.k)
     dbg = {}
     if debug:
         S = c.T * c.k
@@ -50,14 +53,18 @@ def run(M, layer, path=0, debug=False, act=0):
         if act == M.MOE_ACT_MXFP8:
             dbg["x_codes"] = torch.empty((c.T, c.H), dtype=torch.uint8, device="cuda")
             dbg["x_scales"] = torch.empty((c.T, c.H // 32), dtype=torch.uint8, device="cuda")
+    if launch == M.MOE_LAUNCH_FUSED:
+        dbg["wait_error"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     layer.out.fill_(float("nan"))
     torch.cuda.synchronize()
-    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path} act={act}")
+    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path} act={act} "
+        f"launch={launch}")
     mfma = path == M.MOE_PATH_MFMA or act == M.MOE_ACT_MXFP8
     layout = M.MOE_LAYOUT_TILES if mfma else M.MOE_LAYOUT_ROWS
     wgu, wdn, scales = layer.weights(layout)
     M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, wgu, wdn, scales, layer.out,
-                           gemm_path=path, weight_layout=layout, act_format=act, **dbg)
+                           gemm_path=path, weight_layout=layout, act_format=act, launch=launch,
+                           **dbg)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in dbg.items()}
 
