@@ -113,4 +113,66 @@ __device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width)
         a.out[(int64_t)t * a.H + n0 + c] = f32_to_bf16_rne(combine_column(a, t, n0 + c));
 }
 
+// One wave's share of a down-projection tile: acc[rg][t] holds rows 4g..4g+3
+// of row group rg of output quad `quad` (columns 64q + 16rg + 4g + i of out)
+// for token row 16t + c of the item (lane (c, g), the 16x16 MFMA D layout).
+// The rows of y it covers are written in the item's sorted order.
+//
+// COMBINE = false (split launch): plain 16-byte stores; the combine runs as
+// its own kernel after this one (combine.hip), which the kernel boundary
+// makes see every y row.  COMBINE = true (single-launch layer): the y rows
+// go out through agent-coherent stores, then the wave counts its (token,
+// quad) tiles done and the wave that completes a token's k experts on the
+// quad combines those 64 columns (the last finisher), in slot order.
+template <int NT, bool COMBINE>
+__device__ inline void store_down_tile(const GemmArgs& a, int quad, int row0, int m,
+                                       const f32x4_t (&acc)[4][NT]) {
+    const int quads = a.H / 64;
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int n0 = 64 * quad;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if (j >= m) continue;
+        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
+#pragma unroll
+        for (int rg = 0; rg < 4; rg++) {
+            if (!COMBINE) {
+                *reinterpret_cast<float4*>(dst + 16 * rg) =
+                    make_float4(acc[rg][t][0], acc[rg][t][1], acc[rg][t][2], acc[rg][t][3]);
+                continue;
+            }
+            // agent-coherent stores: the combining wave may run on another XCD
+            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
+            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
+                                ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (!COMBINE) return;
+    // every y store of this wave has completed before it counts the tiles
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    for (int j0 = 0; j0 < m; j0 += kWave) {
+        const int j = j0 + lane;
+        int token = -1;
+        bool last = false;
+        if (j < m) {
+            token = a.sorted[row0 + j] / a.k;
+            last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
+        }
+        uint64_t todo = __ballot(last);
+        while (todo) {
+            const int src = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int t = __builtin_amdgcn_readlane(token, src);
+            // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
+            a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
+        }
+    }
+}
+
 }  // namespace moe

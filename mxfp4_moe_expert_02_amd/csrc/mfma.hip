@@ -239,54 +239,9 @@ mfma_gate_up_kernel(GemmArgs a) {
     gate_up_item<1>(a, quad, e, row0, m, red);
 }
 
-// Epilogue of a down tile (one wave holding the summed accumulator of
-// quad `quad` for the item's m tokens): y rows through agent-coherent
-// stores, then the (token, quad) completion counts; the wave that completes
-// a token's k experts on the quad combines those 64 columns.
-template <int NT>
-__device__ inline void down_epilogue(const GemmArgs& a, int quad, int row0, int m,
-                                     const f32x4_t (&acc)[kGroups][NT]) {
-    const int quads = a.H / 64;
-    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
-    const int n0 = 64 * quad;
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int j = 16 * t + c;
-        if (j >= m) continue;
-        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
-#pragma unroll
-        for (int rg = 0; rg < kGroups; rg++) {
-            // agent-coherent stores: the combining wave may run on another XCD
-            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
-                                ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
-                                ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    // every y store of this wave has completed before it counts the tile
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    int token = -1;
-    bool last = false;
-    if (lane < m) {
-        token = a.sorted[row0 + lane] / a.k;
-        last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
-    }
-    uint64_t todo = __ballot(last);
-    while (todo) {
-        const int src = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int t = __builtin_amdgcn_readlane(token, src);
-        // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
-    }
-}
-
-// down body for items of NT column tiles (see mfma_down_kernel)
-template <int NT>
+// down body for items of NT column tiles (see mfma_down_kernel); COMBINE:
+// see store_down_tile
+template <int NT, bool COMBINE>
 __device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, int m,
                                  f32x4_t* red) {
     const int quads = a.H / 64;
@@ -322,7 +277,7 @@ __device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, i
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
-    down_epilogue<NT>(a, quad, row0, m, acc);
+    store_down_tile<NT, COMBINE>(a, quad, row0, m, acc);
 }
 
 // down: a workgroup takes two quads (output rows 64q..64q+63), each split
@@ -340,7 +295,7 @@ mfma_down_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    down_item<1>(a, pair, e, row0, m, red);
+    down_item<1, false>(a, pair, e, row0, m, red);
 }
 
 
@@ -403,7 +358,7 @@ mfma_fused_kernel(GemmArgs a) {
             const int4 it = a.items[item];
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
-            down_item<1>(a, v % dn_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
+            down_item<1, true>(a, v % dn_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
         }
     }
 }

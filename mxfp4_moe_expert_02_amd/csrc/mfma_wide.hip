@@ -186,9 +186,9 @@ __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, 
     }
 }
 
-template <int NT>
+template <int NT, bool COMBINE>
 __device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int tid = threadIdx.x, w = tid / kWave;
     const int K = a.I, chunks = K / 128, quads = a.H / 64;
     const int quad = kWQuads * qb + w;
     const bool live = quad < quads;
@@ -203,41 +203,7 @@ __device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int
     wide_mainloop<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
                       chunks, sm, acc);
     if (!live) return;
-    const int n0 = 64 * quad;
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int j = 16 * t + c;
-        if (j >= m) continue;
-        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
-#pragma unroll
-        for (int rg = 0; rg < kGroups; rg++) {
-            // agent-coherent stores: the combining wave may run on another XCD
-            const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
-                                ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
-                                ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    // every y store of this wave has completed before it counts the tile
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    int token = -1;
-    bool last = false;
-    if (lane < m) {
-        token = a.sorted[row0 + lane] / a.k;
-        last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
-    }
-    uint64_t todo = __ballot(last);
-    while (todo) {
-        const int src = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int t = __builtin_amdgcn_readlane(token, src);
-        // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
-    }
+    store_down_tile<NT, COMBINE>(a, quad, row0, m, acc);
 }
 
 // gate_up: blockIdx.x = item * (I / 128) + quad block (quads 4qb..4qb+3)
@@ -270,13 +236,13 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_ke
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
     switch ((m + 15) / 16) {
-        case 1: wide_down<1>(a, qb, e, row0, m, sm); break;
+        case 1: wide_down<1, false>(a, qb, e, row0, m, sm); break;
 #if MOE_WIDE_ITEM_TOK > 32
-        case 2: wide_down<2>(a, qb, e, row0, m, sm); break;
-        case 3: wide_down<3>(a, qb, e, row0, m, sm); break;
-        default: wide_down<4>(a, qb, e, row0, m, sm); break;
+        case 2: wide_down<2, false>(a, qb, e, row0, m, sm); break;
+        case 3: wide_down<3, false>(a, qb, e, row0, m, sm); break;
+        default: wide_down<4, false>(a, qb, e, row0, m, sm); break;
 #else
-        default: wide_down<2>(a, qb, e, row0, m, sm); break;
+        default: wide_down<2, false>(a, qb, e, row0, m, sm); break;
 #endif
     }
 }
@@ -325,13 +291,13 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_k
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
             switch ((m + 15) / 16) {
-                case 1: wide_down<1>(a, qb, e, row0, m, sm); break;
+                case 1: wide_down<1, true>(a, qb, e, row0, m, sm); break;
 #if MOE_WIDE_ITEM_TOK > 32
-                case 2: wide_down<2>(a, qb, e, row0, m, sm); break;
-                case 3: wide_down<3>(a, qb, e, row0, m, sm); break;
-                default: wide_down<4>(a, qb, e, row0, m, sm); break;
+                case 2: wide_down<2, true>(a, qb, e, row0, m, sm); break;
+                case 3: wide_down<3, true>(a, qb, e, row0, m, sm); break;
+                default: wide_down<4, true>(a, qb, e, row0, m, sm); break;
 #else
-                default: wide_down<2>(a, qb, e, row0, m, sm); break;
+                default: wide_down<2, true>(a, qb, e, row0, m, sm); break;
 #endif
             }
         }

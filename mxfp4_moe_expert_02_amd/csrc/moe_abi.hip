@@ -3,7 +3,10 @@
 //
 // Launch sequence of a forward on `stream` (no host synchronisation):
 //   route (top-k + stable sort by expert + active-expert lists)
-//   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine.
+//   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine
+// (on the bf16 matrix-core path the combine is its own kernel, or the
+// last-finisher step of the single-launch layer; the VALU and MXFP8 paths
+// combine by last finisher inside their down kernels).
 // Every expert that received no token is absent from the active lists and
 // costs no weight bytes: the layer reads only the experts its tokens use,
 // the property the pages build the 4-bit expert format around (bjdmk.com.cn
@@ -286,6 +289,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
             if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
             err = wide ? moe::launch_wide_down(a, max_items, st) : moe::launch_mfma_down(a, max_items, st);
             if (err != hipSuccess) return hip_fail(err, "down");
+            err = moe::launch_combine(a, st);
+            if (err != hipSuccess) return hip_fail(err, "combine");
         }
     }
     if ((err = mark(3)) != hipSuccess) return hip_fail(err, "hipEventRecord");

@@ -140,13 +140,17 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const Workspac
 // max_active bounds the number of routed experts (grids are sized by it).
 hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t stream);
 hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream);
-// MFMA path: same contract, items from the route's MFMA item list;
-// max_items bounds their number.  Items of at most kMfmaTok tokens (split-K
-// kernels) or, for the wide kernels, up to kMfmaItemTok tokens.
+// MFMA path: items from the route's MFMA item list; max_items bounds their
+// number.  Items of at most kMfmaTok tokens (split-K kernels) or, for the
+// wide kernels, up to kMfmaItemTok tokens.  The down kernels only write y;
+// launch_combine forms out.
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream);
+// out = the weighted sum of the k per-assignment rows of y per token, in
+// slot order (after a down kernel of the split launch).
+hipError_t launch_combine(const GemmArgs& a, hipStream_t stream);
 // The same two GEMMs (and the combine) in one persistent launch: workgroups
 // dequeue gate_up units (item, row tile), then down units, each of which
 // waits (bounded) until every gate_up unit of its item has published h.
