@@ -71,17 +71,18 @@ def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:
     return gu, dn
 
 
-KERNEL_SOURCES = ["mxfp4_moe_expert_02_amd/csrc/mfma.hip", "mxfp4_moe_expert_02_amd/csrc/gemv.hip",
-                  "mxfp4_moe_expert_02_amd/csrc/mxfp8.hip",
-                  "mxfp4_moe_expert_02_amd/csrc/device_common.h",
-                  "mxfp4_moe_expert_02_amd/csrc/moe_internal.h"]
+CSRC = os.path.join(ROOT, "mxfp4_moe_expert_02_amd", "csrc")
 
 
 def sources_sha256() -> str:
+    """sha256 over every HIP source and header of the library: a traffic
+    figure taken with other kernel code does not apply."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
 
@@ -266,8 +267,12 @@ def main():
         cold = float(np.median(times))
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
+    # the gate_up kernel the library runs for this layer (the wide bf16
+    # kernels when the experts average >= 8 tokens each)
+    wide = cfg.T * cfg.k >= 8 * cfg.E
     kname = ("mx8_gate_up_kernel" if mx8 else
-             "mfma_gate_up_kernel" if path == M.MOE_PATH_MFMA else "gemv_gate_up_kernel")
+             ("wide_gate_up_kernel" if wide else "mfma_gate_up_kernel") if path == M.MOE_PATH_MFMA
+             else "gemv_gate_up_kernel")
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

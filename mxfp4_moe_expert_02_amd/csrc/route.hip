@@ -117,90 +117,69 @@ __device__ inline void scan_experts(int E, const int* s_cnt, int* s_off) {
     }
 }
 
-// Items per expert on the MFMA path: ceil(c / item_tok) items of equal
-// numbers of 16-token tiles (+-1); item q of an expert with `tiles` tiles
-// dealt over `groups` items has per + (q < extra) tiles starting at tile
-// q*per + min(q, extra) (per = tiles / groups, extra = tiles % groups).
-constexpr int kMaxItemTiles = 8;  // item_tok / 16 <= 8 (128-token items)
-
-// Number of this expert's items with nt tiles.
-__device__ inline int items_with_tiles(int nt, int groups, int per, int extra) {
-    return (nt == per + 1 ? extra : 0) + (nt == per ? groups - extra : 0);
-}
-
 // Active-expert lists in ascending expert index, compacted with wave
-// scans: the GEMV list, the MFMA list, and the MFMA path's items
-// (expert, first row in sorted order, tokens) ordered by tile count,
-// largest first, and by expert index within one tile count.  The heaviest
-// items (a popular expert's full 64- or 128-token items, whose matrix-core
-// work per weight byte is the largest) are then dispatched first instead
-// of landing in the tail of the grid; the order of items does not change
-// any result (each output element is computed by one item, and the
-// combine sums in slot order).  s_cnt/s_off: the per-expert counts and
-// exclusive offsets, in LDS.  Writes the list lengths to meta.  Called by
-// every thread of one block.
+// scans: the GEMV list and the MFMA list; and the MFMA path's items
+// (expert, first row in sorted order, tokens), ceil(c / item_tok) per expert
+// of equal numbers of 16-token tiles (+-1): item q of an expert with `tiles`
+// tiles over `groups` items has per + (q < extra) tiles from tile q*per +
+// min(q, extra) (per = tiles / groups, extra = tiles % groups).
+//
+// Items are ordered by expert, heaviest expert (most tiles) first, ties by
+// expert index, and an expert's items stay adjacent: the heaviest work is
+// dispatched first instead of landing in the tail of the grid, and the
+// workgroups that stream the same expert's weights for its several items
+// run at about the same time (their re-reads then hit in cache).  The order
+// of items changes no result: each output element is computed by one item,
+// and the combine sums in slot order.  s_cnt/s_off: the per-expert counts
+// and exclusive offsets, in LDS.  Writes the list lengths to meta.  Called
+// by every thread of one block.
 __device__ void build_lists(int E, const Workspace& ws, int gemv_max_tokens, int path, int item_tok,
                             const int* s_cnt, const int* s_off) {
     __shared__ int s_n[3];
-    const int tid = threadIdx.x;
-    const int max_nt = min(kMaxItemTiles, item_tok / 16);
+    __shared__ int s_key[kMaxExperts];   // tiles of an MFMA-path expert, -1 otherwise
+    __shared__ int s_rank[kMaxExperts];  // position of the expert in item order
+    __shared__ int s_base[kMaxExperts];  // by rank: the expert's items, then their first index
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    auto on_gemv = [&](int c) { return c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens)); };
+    for (int e = tid; e < E; e += nthr) {
+        const int c = s_cnt[e];
+        s_key[e] = (c > 0 && !on_gemv(c)) ? (c + 15) / 16 : -1;
+    }
+    __syncthreads();
+    // rank among the MFMA-path experts: (tiles desc, index asc)
+    for (int e = tid; e < E; e += nthr) {
+        const int ke = s_key[e];
+        if (ke < 0) continue;
+        int r = 0;
+        for (int f = 0; f < E; f++) {
+            const int kf = s_key[f];
+            r += (kf > ke || (kf == ke && f < e)) ? 1 : 0;
+        }
+        s_rank[e] = r;
+        s_base[r] = (s_cnt[e] + item_tok - 1) / item_tok;  // the expert's items
+    }
+    __syncthreads();
     if (tid < kWave) {
-        // pass 1: the lists, and the number of items of each tile count
+        // the lists, and the exclusive scan of items over ranks
         int n_g = 0, n_m = 0, n_items = 0;
-        int bucket[kMaxItemTiles];  // items with max_nt - b tiles (wave-uniform)
-#pragma unroll
-        for (int b = 0; b < kMaxItemTiles; b++) bucket[b] = 0;
         for (int base = 0; base < E; base += kWave) {
             const int e = base + tid;
             const int c = (e < E) ? s_cnt[e] : 0;
-            const bool g = c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens));
+            const bool g = on_gemv(c);
             const bool m = c > 0 && !g;
-            const int groups = m ? (c + item_tok - 1) / item_tok : 0;
-            const int tiles = (c + 15) / 16;
-            const int per = groups ? tiles / groups : 0, extra = groups ? tiles % groups : 0;
             const int ig = wave_incl_scan(g ? 1 : 0);
             const int im = wave_incl_scan(m ? 1 : 0);
             if (g) ws.gemv_list[n_g + ig - 1] = e;
             if (m) ws.mfma_list[n_m + im - 1] = e;
             n_g += __builtin_amdgcn_readlane(ig, kWave - 1);
             n_m += __builtin_amdgcn_readlane(im, kWave - 1);
-#pragma unroll
-            for (int b = 0; b < kMaxItemTiles; b++) {
-                const int n = wave_incl_scan(items_with_tiles(max_nt - b, groups, per, extra));
-                bucket[b] += __builtin_amdgcn_readlane(n, kWave - 1);
-            }
         }
-        // pass 2: place each item at its bucket's running position
-        int run[kMaxItemTiles];
-#pragma unroll
-        for (int b = 0; b < kMaxItemTiles; b++) {
-            run[b] = n_items;
-            n_items += bucket[b];
-        }
-        for (int base = 0; base < E; base += kWave) {
-            const int e = base + tid;
-            const int c = (e < E) ? s_cnt[e] : 0;
-            const bool g = c > 0 && ((path == 1) || (path == 0 && c <= gemv_max_tokens));
-            const bool m = c > 0 && !g;
-            const int groups = m ? (c + item_tok - 1) / item_tok : 0;
-            const int tiles = (c + 15) / 16;
-            const int per = groups ? tiles / groups : 0, extra = groups ? tiles % groups : 0;
-#pragma unroll
-            for (int b = 0; b < kMaxItemTiles; b++) {
-                const int nt = max_nt - b;
-                const int n = items_with_tiles(nt, groups, per, extra);
-                const int incl = wave_incl_scan(n);
-                int slot = run[b] + incl - n;
-                // this expert's items with nt tiles: q in [0, extra) if
-                // nt == per + 1, else q in [extra, groups)
-                const int q0 = nt == per + 1 ? 0 : extra;
-                for (int q = q0; q < q0 + n; q++) {
-                    const int t0 = q * per + min(q, extra);
-                    ws.mfma_items[slot++] =
-                        make_int4(e, s_off[e] + 16 * t0, min(16 * nt, c - 16 * t0), 0);
-                }
-                run[b] += __builtin_amdgcn_readlane(incl, kWave - 1);
-            }
+        for (int base = 0; base < n_m; base += kWave) {
+            const int r = base + tid;
+            const int n = r < n_m ? s_base[r] : 0;
+            const int incl = wave_incl_scan(n);
+            if (r < n_m) s_base[r] = n_items + incl - n;
+            n_items += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (tid == 0) {
             s_n[0] = n_g;
@@ -209,6 +188,19 @@ __device__ void build_lists(int E, const Workspace& ws, int gemv_max_tokens, int
         }
     }
     __syncthreads();
+    // each MFMA-path expert writes its items from its first index
+    for (int e = tid; e < E; e += nthr) {
+        if (s_key[e] < 0) continue;
+        const int c = s_cnt[e];
+        const int groups = (c + item_tok - 1) / item_tok;
+        const int tiles = (c + 15) / 16, per = tiles / groups, extra = tiles % groups;
+        int slot = s_base[s_rank[e]];
+        for (int q = 0; q < groups; q++) {
+            const int t0 = q * per + min(q, extra);
+            const int nt = per + (q < extra ? 1 : 0);
+            ws.mfma_items[slot++] = make_int4(e, s_off[e] + 16 * t0, min(16 * nt, c - 16 * t0), 0);
+        }
+    }
     if (tid == 0) {
         ws.meta[kMetaNumGemv] = s_n[0];
         ws.meta[kMetaNumMfma] = s_n[1];
