@@ -4,9 +4,9 @@
 // Launch sequence of a forward on `stream` (no host synchronisation):
 //   route (top-k + stable sort by expert + active-expert lists)
 //   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine
-// (on the bf16 matrix-core path the combine is its own kernel, or the
-// last-finisher step of the single-launch layer; the VALU and MXFP8 paths
-// combine by last finisher inside their down kernels).
+// (on the matrix-core paths the combine is its own kernel, or the
+// last-finisher step of the single-launch layer; the VALU path combines by
+// last finisher inside its down kernel).
 // Every expert that received no token is absent from the active lists and
 // costs no weight bytes: the layer reads only the experts its tokens use,
 // the property the pages build the 4-bit expert format around (bjdmk.com.cn
@@ -266,6 +266,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
         err = moe::launch_mx8_down(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "down");
+        err = moe::launch_combine(a, st);
+        if (err != hipSuccess) return hip_fail(err, "combine");
     } else if (path == MOE_PATH_GEMV) {
         err = moe::launch_gemv_gate_up(a, max_active, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");

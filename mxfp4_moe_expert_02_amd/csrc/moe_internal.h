@@ -158,7 +158,8 @@ hipError_t launch_combine(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_mfma_fused(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_fused(const GemmArgs& a, int max_items, hipStream_t stream);
 // MXFP8 (prefill) path: encode x per token along H, then the scaled
-// FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue).
+// FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue;
+// down writes y, launch_combine forms out).
 hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* codes,
                                    uint8_t* scales, hipStream_t stream);
 hipError_t launch_mx8_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);

@@ -342,10 +342,8 @@ mx8_gate_up_kernel(GemmArgs a) {
 }
 
 // down, MXFP8 h: blockIdx.x = item * (H / 128) + row block (quads 2rb,
-// 2rb+1 of the output rows).  y goes out through agent-coherent stores;
-// each wave then counts its (token, quad) tiles done, and the wave that
-// completes a token's k experts on a quad combines those 64 columns (the
-// last finisher, as in the other paths).
+// 2rb+1 of the output rows).  y goes out through plain 16-byte stores; the
+// combine runs as its own kernel after this one (combine.hip).
 __global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
 mx8_down_kernel(GemmArgs a) {
     __shared__ PfSmem sm;
@@ -377,36 +375,10 @@ mx8_down_kernel(GemmArgs a) {
         if (t < ntile && j < m) {
             float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
 #pragma unroll
-            for (int rg = 0; rg < 4; rg++) {
-                const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
-                                    ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
-                const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
-                                    ((uint64_t)__float_as_uint(acc[rg][t][3]) << 32);
-                __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg), lo, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + 16 * rg + 2), hi,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int rg = 0; rg < 4; rg++)
+                *reinterpret_cast<float4*>(dst + 16 * rg) =
+                    make_float4(acc[rg][t][0], acc[rg][t][1], acc[rg][t][2], acc[rg][t][3]);
         }
-    }
-    // every y store of this wave has completed before it counts its tiles
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    // lane (c, g) counts token tile_token(g, wt, c): the tokens whose y rows
-    // this wave stored (column tiles g < ntile)
-    const int j = tile_token(g, wt, c);
-    int token = -1;
-    bool last = false;
-    if (g < ntile && j < m) {
-        token = a.sorted[row0 + j] / a.k;
-        last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
-    }
-    uint64_t todo = __ballot(last);
-    while (todo) {
-        const int srcl = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int t = __builtin_amdgcn_readlane(token, srcl);
-        // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-        a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
     }
 }
 
