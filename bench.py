@@ -7,7 +7,9 @@ synthetic seeded inputs (x ~ N(0,1) bf16, router logits ~ N(0,1), expert
 weights ~ N(0,0.02) encoded to MXFP4 on the GPU).
 
 One step = one full layer (route -> gate_up + SiLU*up -> down -> combine) on
-inputs already resident in HBM.  Prints ONE JSON line:
+inputs already resident in HBM; layers of at most 16 tokens run self-routed
+(the GEMM workgroups rank their own experts: no routing kernel).  Prints ONE
+JSON line:
   value  = touched-expert weight bytes (packed E2M1 + E8M0) / mean layer time, GB/s
   roofline = the dominant kernel (gate_up: 2/3 of the bytes) against the
              8 TB/s HBM peak, timed live with HIP events the library records
@@ -52,6 +54,10 @@ def parse():
     p.add_argument("--path", type=int, default=0,
                    help="1: VALU GEMV over row-major weights; 2 (default): bf16 MFMA over "
                         "the tile layout (weights prepacked once before timing)")
+    p.add_argument("--launch", choices=["auto", "split", "self"], default="auto",
+                   help="bf16 MFMA path: auto (the library's choice: self-routed for at most "
+                        "16 tokens), split (routing kernel, then the GEMMs), self (no routing "
+                        "kernel: each GEMM workgroup ranks its own expert)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
@@ -194,10 +200,17 @@ def main():
     gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
     total_bytes = gu_bytes + dn_bytes
 
+    launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
+              "self": M.MOE_LAUNCH_SELF_ROUTED}[args.launch]
+    wide = cfg.T * cfg.k >= 8 * cfg.E  # the library's wide items (experts average >= 8 tokens)
+    self_ok = (path == M.MOE_PATH_MFMA and not mx8 and not wide and cfg.T <= 16
+               and cfg.T * cfg.E <= 4096)
+    self_routed = self_ok and launch in (M.MOE_LAUNCH_AUTO, M.MOE_LAUNCH_SELF_ROUTED)
+
     def step(events=None):
         M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
                                gemm_path=path, weight_layout=layout, events=events,
-                               act_format=act)
+                               act_format=act, launch=launch)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -268,9 +281,10 @@ def main():
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
     # the gate_up kernel the library runs for this layer (the wide bf16
-    # kernels when the experts average >= 8 tokens each)
-    wide = cfg.T * cfg.k >= 8 * cfg.E
+    # kernels when the experts average >= 8 tokens each; the self-routed one
+    # for at most 16 tokens unless the split launch is asked for)
     kname = ("mx8_gate_up_kernel" if mx8 else
+             "self_gate_up_kernel" if self_routed else
              ("wide_gate_up_kernel" if wide else "mfma_gate_up_kernel") if path == M.MOE_PATH_MFMA
              else "gemv_gate_up_kernel")
     if args.copy_bytes:
@@ -326,6 +340,7 @@ def main():
                        max_tokens_per_expert=int(counts_np.max()),
                        touched_weight_bytes=int(total_bytes),
                        gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
+                       launch="self_routed" if self_routed else "split",
                        weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",
                        activations="mxfp8" if mx8 else "bf16"),
         "tflops": {"layer": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),

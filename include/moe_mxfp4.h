@@ -94,6 +94,16 @@ extern "C" {
                                 pages' persistent, gap-free execution (tilert.ai
                                 blog, first leap; bjdmk.com.cn news page, road to
                                 1000 tokens/s) applied to this layer */
+#define MOE_LAUNCH_SELF_ROUTED 3 /* no routing pass: each GEMM workgroup ranks its
+                                own expert for every token from router_logits,
+                                and experts no token chose exit at once; h and
+                                y rows are indexed by slot.  Layers of at most
+                                16 tokens with T*E <= 4096 on the bf16 MFMA
+                                path whose mean tokens per expert (T*top_k/E)
+                                is below 8; other layers return MOE_E_OPTION.
+                                AUTO takes it wherever it applies.  Same output
+                                bits as SPLIT.  With NaN router logits the
+                                result for that token is unspecified. */
 
 /* Weight layouts (moe_mxfp4_options.weight_layout) */
 #define MOE_LAYOUT_ROWS 0    /* row-major packed codes + scales, as described above */
@@ -122,7 +132,8 @@ typedef struct moe_mxfp4_options {
     uint8_t* x_codes;    /* [T, H] E4M3 codes of x (MOE_ACT_MXFP8 only) */
     uint8_t* x_scales;   /* [T, H/32] E8M0 scales of x (MOE_ACT_MXFP8 only) */
     /* Optional hipEvent_t handles recorded on `stream` at the stage
-     * boundaries: [0] before routing, [1] after routing (and, with
+     * boundaries: [0] before routing, [1] after routing (right after [0]
+     * in a self-routed launch that returns no routing output; with
      * MOE_ACT_MXFP8, after the encoding of x), [2] after the
      * gate_up GEMM (after the single expert kernel in a fused launch),
      * [3] after the down GEMM and the combine.  Only the

@@ -36,6 +36,7 @@ MOE_LAYOUT_TILES = 1
 MOE_LAUNCH_AUTO = 0
 MOE_LAUNCH_SPLIT = 1
 MOE_LAUNCH_FUSED = 2
+MOE_LAUNCH_SELF_ROUTED = 3
 
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",

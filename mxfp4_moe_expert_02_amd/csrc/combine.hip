@@ -5,6 +5,8 @@
 //   out[t, n] = sum_{j = 0 .. k-1} w[t, j] * y[pos[t, j], n],  fp32 in slot
 //   order j, rounded to bf16 (nearest even)
 //
+// (pos null: the self-routed layer, whose y rows are the slots t*k + j)
+//
 // (the routing weights renormalised over the token's top-k experts, the
 // standard MoE combine the layer's problem statement names).  The same fmaf
 // chain as the last-finisher combine of the single-launch layer, so both
@@ -28,7 +30,7 @@ __device__ inline void combine_batch(const GemmArgs& a, int64_t base, int j0, in
     float4 y[N];
 #pragma unroll
     for (int u = 0; u < N; u++) {
-        p[u] = a.pos[base + j0 + u];
+        p[u] = a.pos ? a.pos[base + j0 + u] : (int)(base + j0 + u);
         w[u] = a.wts[base + j0 + u];
     }
 #pragma unroll

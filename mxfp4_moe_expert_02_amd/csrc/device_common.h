@@ -113,10 +113,34 @@ __device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width)
         a.out[(int64_t)t * a.H + n0 + c] = f32_to_bf16_rne(combine_column(a, t, n0 + c));
 }
 
+// The token rows of one MFMA item, for the lane's column j of a tile.
+// SortedRows: a routed item, rows row0 .. row0+m-1 of the sorted order
+// (its h and y rows), slot sorted[row0 + j].  SlotRows: a self-routed
+// expert of at most 16 tokens (one column tile), where lane c holds the slot
+// t*k + rank of its column's token, which is also its h and y row.
+struct SortedRows {
+    int row0, m;
+    __device__ int row(int j) const { return row0 + j; }
+    __device__ int slot(const GemmArgs& a, int j) const { return a.sorted[row0 + j]; }
+};
+struct SlotRows {
+    int m, lane_slot;
+    __device__ int row(int) const { return lane_slot; }
+    __device__ int slot(const GemmArgs&, int) const { return lane_slot; }
+};
+// ListRows: a self-routed expert whose slots sit in its slot list (read
+// when needed, after the first weight loads are in flight)
+struct ListRows {
+    int m;
+    const int32_t* slots;
+    __device__ int row(int j) const { return slots[j]; }
+    __device__ int slot(const GemmArgs&, int j) const { return slots[j]; }
+};
+
 // One wave's share of a down-projection tile: acc[rg][t] holds rows 4g..4g+3
 // of row group rg of output quad `quad` (columns 64q + 16rg + 4g + i of out)
 // for token row 16t + c of the item (lane (c, g), the 16x16 MFMA D layout).
-// The rows of y it covers are written in the item's sorted order.
+// Each token's values go to its y row (rows.row).
 //
 // COMBINE = false (split launch): plain 16-byte stores; the combine runs as
 // its own kernel after this one (combine.hip), which the kernel boundary
@@ -124,9 +148,10 @@ __device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width)
 // go out through agent-coherent stores, then the wave counts its (token,
 // quad) tiles done and the wave that completes a token's k experts on the
 // quad combines those 64 columns (the last finisher), in slot order.
-template <int NT, bool COMBINE>
-__device__ inline void store_down_tile(const GemmArgs& a, int quad, int row0, int m,
+template <int NT, bool COMBINE, typename Rows>
+__device__ inline void store_down_tile(const GemmArgs& a, int quad, const Rows& rows,
                                        const f32x4_t (&acc)[4][NT]) {
+    const int m = rows.m;
     const int quads = a.H / 64;
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int n0 = 64 * quad;
@@ -134,7 +159,7 @@ __device__ inline void store_down_tile(const GemmArgs& a, int quad, int row0, in
     for (int t = 0; t < NT; t++) {
         const int j = 16 * t + c;
         if (j >= m) continue;
-        float* dst = a.y + (int64_t)(row0 + j) * a.H + n0 + 4 * g;
+        float* dst = a.y + (int64_t)rows.row(j) * a.H + n0 + 4 * g;
 #pragma unroll
         for (int rg = 0; rg < 4; rg++) {
             if (!COMBINE) {
@@ -153,24 +178,25 @@ __device__ inline void store_down_tile(const GemmArgs& a, int quad, int row0, in
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (!COMBINE) return;
-    // every y store of this wave has completed before it counts the tiles
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    for (int j0 = 0; j0 < m; j0 += kWave) {
-        const int j = j0 + lane;
-        int token = -1;
-        bool last = false;
-        if (j < m) {
-            token = a.sorted[row0 + j] / a.k;
-            last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
-        }
-        uint64_t todo = __ballot(last);
-        while (todo) {
-            const int src = __builtin_ctzll(todo);
-            todo &= todo - 1;
-            const int t = __builtin_amdgcn_readlane(token, src);
-            // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-            a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
+    if constexpr (COMBINE) {  // routed items only (rows.row0)
+        // every y store of this wave has completed before it counts the tiles
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        for (int j0 = 0; j0 < m; j0 += kWave) {
+            const int j = j0 + lane;
+            int token = -1;
+            bool last = false;
+            if (j < m) {
+                token = a.sorted[rows.row0 + j] / a.k;
+                last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
+            }
+            uint64_t todo = __ballot(last);
+            while (todo) {
+                const int src = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                const int t = __builtin_amdgcn_readlane(token, src);
+                // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
+                a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
+            }
         }
     }
 }

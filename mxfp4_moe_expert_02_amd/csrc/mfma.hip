@@ -34,6 +34,7 @@
 // go to mfma_wide.hip).  The quad routine is written for NT column tiles;
 // these kernels use NT = 1.
 #include "device_common.h"
+#include "route_rank.h"
 
 namespace moe {
 namespace {
@@ -184,11 +185,13 @@ __device__ inline void wave_chunk_range(int chunks, int& c_begin, int& c_end) {
 constexpr int kRedGateUp = (kWaves - 1) * kGroups * kWave;
 constexpr int kRedDown = 2 * kGroups * kWave;
 
-// gate_up body for items of NT column tiles
-template <int NT>
-__device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, int row0, int m,
+// gate_up body for items of NT column tiles, token rows from `rows`
+// (SortedRows or SlotRows)
+template <int NT, typename Rows>
+__device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, const Rows& rows,
                                     f32x4_t* red) {
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int m = rows.m;
     const int K = a.H, chunks = K / 128, quads = a.I / 32;
     const int64_t quad_id = (int64_t)e * quads + quad;
     int cb, ce;
@@ -199,7 +202,7 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, int row0
 #pragma unroll
                       for (int t = 0; t < NT; t++) {
                           const int j = 16 * t + c;
-                          xrow[t] = j < m ? a.x + (int64_t)(a.sorted[row0 + j] / a.k) * K : nullptr;
+                          xrow[t] = j < m ? a.x + (int64_t)(rows.slot(a, j) / a.k) * K : nullptr;
                       }
                   },
                   cb, ce, acc);
@@ -209,7 +212,7 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, int row0
         for (int t = 0; t < NT; t++) {
             const int j = 16 * t + c;
             if (j >= m) continue;
-            uint16_t* hrow = a.h + (int64_t)(row0 + j) * a.I + 32 * quad + 4 * g;
+            uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
 #pragma unroll
             for (int rg = 0; rg < 2; rg++) {
                 ushort4 o;
@@ -236,14 +239,15 @@ mfma_gate_up_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    gate_up_item<1>(a, quad, e, row0, m, red);
+    gate_up_item<1>(a, quad, e, SortedRows{row0, m}, red);
 }
 
-// down body for items of NT column tiles (see mfma_down_kernel); COMBINE:
-// see store_down_tile
-template <int NT, bool COMBINE>
-__device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, int m,
+// down body for items of NT column tiles (see mfma_down_kernel), token rows
+// from `rows`; COMBINE: see store_down_tile
+template <int NT, bool COMBINE, typename Rows>
+__device__ inline void down_item(const GemmArgs& a, int pair, int e, const Rows& rows,
                                  f32x4_t* red) {
+    const int m = rows.m;
     const int quads = a.H / 64;
     const int w = threadIdx.x / kWave, half = w & 1;
     const int quad = pair * 2 + (w >> 1);
@@ -259,7 +263,7 @@ __device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, i
 #pragma unroll
                           for (int t = 0; t < NT; t++) {
                               const int j = 16 * t + c;
-                              xrow[t] = j < m ? a.h + (int64_t)(row0 + j) * K : nullptr;
+                              xrow[t] = j < m ? a.h + (int64_t)rows.row(j) * K : nullptr;
                           }
                       },
                       half ? hc : 0, half ? chunks : hc, acc);
@@ -277,15 +281,13 @@ __device__ inline void down_item(const GemmArgs& a, int pair, int e, int row0, i
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
-    store_down_tile<NT, COMBINE>(a, quad, row0, m, acc);
+    store_down_tile<NT, COMBINE>(a, quad, rows, acc);
 }
 
 // down: a workgroup takes two quads (output rows 64q..64q+63), each split
 // in two K halves over two waves; blockIdx.x = item * ceil(quads / 2) +
-// pair.  A quad is also the combine tile: the wave holding the summed
-// accumulator counts the tile done for its tokens, and the one that
-// completes a token's k experts combines it (the last finisher, as in
-// gemv.hip).  y moves through agent-coherent stores and loads.
+// pair.  The wave holding a quad's summed accumulator writes its y rows;
+// the combine kernel reads them after this kernel.
 __global__ void __launch_bounds__(kMfmaThreads)
 __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
 mfma_down_kernel(GemmArgs a) {
@@ -295,19 +297,85 @@ mfma_down_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    down_item<1, false>(a, pair, e, row0, m, red);
+    down_item<1, false>(a, pair, e, SortedRows{row0, m}, red);
 }
 
+// ---- self-routed layer (up to kSelfMaxTok tokens): no routing pass.  The
+// pages name the launches, synchronisations and global-memory round trips
+// at operator boundaries as the fixed costs that surface once a step takes
+// microseconds (tilert.ai blog, first leap; HyperAI transcript, system
+// efficiency); a routing pass ahead of the GEMMs, over a few tokens, is
+// such a cost: a kernel of its own and a boundary.  Here every workgroup ranks
+// its own expert for each token from the router logits (expert_slots: one
+// round of loads, compares and a ballot, about the latency of the item
+// load it replaces), so gate_up starts streaming weights at once.  The
+// GEMM arithmetic and its order are those of the routed kernels, and the
+// weights come from the same rank-count code, so the output has the same
+// bits as the routed layer's.
 
-// The expert layer after routing in one persistent launch: every workgroup
-// dequeues units from one counter, first the gate_up units (item, quad),
-// then the down units (item, quad pair), until the queue is exhausted.  A
-// gate_up unit publishes its h rows (agent-coherent stores, completed)
-// before it counts itself done for its item; a down unit first waits until
-// all I/32 gate_up units of its item are done.  No wait can deadlock: the
-// units a down unit waits for were dequeued before it, by workgroups that
-// are running and never wait themselves.  The wait is bounded (wait_count)
-// and raises queue[kQueueError] if it ever gives up.
+// LDS of the weight pass: the logits, then the chosen ids and logits
+constexpr int kSelfLdsFloats = kSelfMaxPairs + 2 * kSelfMaxTok * kMaxTopK;
+
+// The rows of expert e for a self-routed GEMM workgroup: from its slot list
+// (one scalar load of m before any weight load; the slots are read after
+// the first weight loads are issued), or ranked here from the logits.
+template <bool LISTS>
+struct SelfRows;
+template <>
+struct SelfRows<true> {
+    static __device__ ListRows get(const GemmArgs& a, int e) {
+        const int32_t* list = a.slot_lists + e * kSlotListInts;
+        return ListRows{uniform(list[0]), list + 1};
+    }
+};
+template <>
+struct SelfRows<false> {
+    static __device__ SlotRows get(const GemmArgs& a, int e) {
+        int slot;
+        const int m = uniform(expert_slots(a.logits, a.T, a.E, a.k, e, &slot));
+        return SlotRows{m, slot};
+    }
+};
+
+// blockIdx.x = 0: the routing weights w[t, j] (and expert ids) of every
+// slot, for the combine.  blockIdx.x = 1 + e * (I/32) + quad: gate_up quad
+// `quad` of expert e, for the tokens that chose e, h rows by slot.
+template <bool LISTS>
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+self_gate_up_kernel(GemmArgs a) {
+    __shared__ __attribute__((aligned(16)))
+    float smem[kSelfLdsFloats > 4 * kRedGateUp ? kSelfLdsFloats : 4 * kRedGateUp];
+    if (blockIdx.x == 0) {
+        const int T = a.T, E = a.E;
+        for (int i = threadIdx.x; i < T * E; i += blockDim.x) smem[i] = a.logits[i];
+        __syncthreads();
+        float* sel_l = smem + T * E;
+        int* sel_id = reinterpret_cast<int*>(sel_l + T * a.k);
+        topk_tokens(smem, T, 0, E, a.k, sel_id, sel_l, a.route_ids, a.route_wts);
+        return;
+    }
+    const int quads = a.I / 32;
+    const int e = (blockIdx.x - 1) / quads, quad = (blockIdx.x - 1) % quads;
+    const auto rows = SelfRows<LISTS>::get(a, e);
+    if (rows.m == 0) return;  // no token chose e
+    gate_up_item<1>(a, quad, e, rows, reinterpret_cast<f32x4_t*>(smem));
+}
+
+// blockIdx.x = e * ceil(H/128) + pair: the down quads 2*pair, 2*pair+1 of
+// expert e for the tokens that chose it, y rows by slot.
+template <bool LISTS>
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+self_down_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[kRedDown];
+    const int pairs = (a.H / 64 + 1) / 2;
+    const int e = blockIdx.x / pairs, pair = blockIdx.x % pairs;
+    const auto rows = SelfRows<LISTS>::get(a, e);
+    if (rows.m == 0) return;
+    down_item<1, false>(a, pair, e, rows, red);
+}
+
 #ifndef MOE_FUSED_WAVES_PER_EU
 #define MOE_FUSED_WAVES_PER_EU 2
 #endif
@@ -348,7 +416,8 @@ mfma_fused_kernel(GemmArgs a) {
         if (u < n_gu) {
             const int item = u / gu_units;
             const int4 it = a.items[item];
-            gate_up_item<1>(a, u % gu_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
+            gate_up_item<1>(a, u % gu_units, uniform(it.x),
+                            SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
             if (threadIdx.x < kWave) {  // wave 0 stored the h rows
                 __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): they are complete
                 if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
@@ -358,7 +427,8 @@ mfma_fused_kernel(GemmArgs a) {
             const int4 it = a.items[item];
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
-            down_item<1, true>(a, v % dn_units, uniform(it.x), uniform(it.y), uniform(it.z), red[cur]);
+            down_item<1, true>(a, v % dn_units, uniform(it.x),
+                               SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
         }
     }
 }
@@ -374,6 +444,24 @@ hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int pairs = (a.H / 64 + 1) / 2;
     mfma_down_kernel<<<max_items * pairs, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_self_gate_up(const GemmArgs& a, bool lists, hipStream_t stream) {
+    const int grid = 1 + a.E * (a.I / 32);
+    if (lists)
+        self_gate_up_kernel<true><<<grid, kMfmaThreads, 0, stream>>>(a);
+    else
+        self_gate_up_kernel<false><<<grid, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_self_down(const GemmArgs& a, bool lists, hipStream_t stream) {
+    const int grid = a.E * ((a.H / 64 + 1) / 2);
+    if (lists)
+        self_down_kernel<true><<<grid, kMfmaThreads, 0, stream>>>(a);
+    else
+        self_down_kernel<false><<<grid, kMfmaThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -203,7 +203,7 @@ __device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int
     wide_mainloop<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
                       chunks, sm, acc);
     if (!live) return;
-    store_down_tile<NT, COMBINE>(a, quad, row0, m, acc);
+    store_down_tile<NT, COMBINE>(a, quad, SortedRows{row0, m}, acc);
 }
 
 // gate_up: blockIdx.x = item * (I / 128) + quad block (quads 4qb..4qb+3)

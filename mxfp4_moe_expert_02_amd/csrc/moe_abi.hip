@@ -6,7 +6,9 @@
 //   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine
 // (on the matrix-core paths the combine is its own kernel, or the
 // last-finisher step of the single-launch layer; the VALU path combines by
-// last finisher inside its down kernel).
+// last finisher inside its down kernel).  Layers of at most 16 tokens on
+// the bf16 matrix-core path skip the route: their GEMM workgroups rank
+// their own experts (the self-routed layer).
 // Every expert that received no token is absent from the active lists and
 // costs no weight bytes: the layer reads only the experts its tokens use,
 // the property the pages build the 4-bit expert format around (bjdmk.com.cn
@@ -63,6 +65,7 @@ size_t layout(Workspace* ws, char* base) {
     ws->max_items = (int)(ws->E + S / moe::kMfmaTok + 1);
     ws->queue = (int32_t*)take(moe::kQueueWords * 4);
     ws->gu_done = (int32_t*)take((size_t)ws->max_items * 4);
+    ws->slot_lists = (int32_t*)take((size_t)ws->E * moe::kSlotListInts * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
@@ -188,7 +191,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         return MOE_E_OPTION;
     if (o.num_events < 0 || o.num_events > 4 || (o.num_events > 0 && !o.events))
         return MOE_E_OPTION;
-    if (o.launch != MOE_LAUNCH_AUTO && o.launch != MOE_LAUNCH_SPLIT && o.launch != MOE_LAUNCH_FUSED)
+    if (o.launch != MOE_LAUNCH_AUTO && o.launch != MOE_LAUNCH_SPLIT &&
+        o.launch != MOE_LAUNCH_FUSED && o.launch != MOE_LAUNCH_SELF_ROUTED)
         return MOE_E_OPTION;
     if (num_tokens == 0) return MOE_OK;
     if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
@@ -221,15 +225,39 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     // tokens (an expert's weights are then read once per 64 tokens)
     const bool wide = (int64_t)T * k >= (int64_t)moe::kMfmaWideMeanTok * E;
     const int item_tok = mx8 ? moe::kMx8Tok : wide ? moe::kMfmaItemTok : moe::kMfmaTok;
+    // The self-routed layer (no sorting pass: the GEMM workgroups find their
+    // experts' tokens themselves) covers the bf16 matrix-core path with
+    // single-tile items of at most kSelfMaxTok tokens; AUTO takes it
+    // wherever it applies.
+    const bool self_ok = !mx8 && path == MOE_PATH_MFMA && !wide && T <= moe::kSelfMaxTok &&
+                         (int64_t)T * E <= moe::kSelfMaxPairs;
+    if (o.launch == MOE_LAUNCH_SELF_ROUTED && !self_ok) return MOE_E_OPTION;
+    const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO);
+    // the routing pass also runs for a self-routed layer when its results
+    // are asked for (it writes the same ids and weights the layer uses)
+    const bool want_route = o.ids || o.weights || o.counts || o.offsets || o.sorted;
     if (mx8) {  // x is encoded in the routing stage (events [0]..[1])
         err = moe::launch_quantize_x_mxfp8((const uint16_t*)x, T, H, ws->x_codes, ws->x_scales, st);
         if (err != hipSuccess) return hip_fail(err, "quantize x");
     }
-    err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, item_tok, st);
-    if (err != hipSuccess) return hip_fail(err, "route");
+    if (!self || want_route) {
+        err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, item_tok, st);
+        if (err != hipSuccess) return hip_fail(err, "route");
+    }
+    // a large self-routed layer ranks each expert once, in a pre-pass
+    const bool lists = self && (int64_t)E * (I / 32 + H / 128) >= moe::kSelfListUnits;
+    moe::GemmArgs a;
+    a.logits = router_logits;
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.slot_lists = ws->slot_lists;
+    if (lists) {
+        err = moe::launch_slot_lists(a, st);
+        if (err != hipSuccess) return hip_fail(err, "slot lists");
+    }
     if ((err = mark(1)) != hipSuccess) return hip_fail(err, "hipEventRecord");
 
-    moe::GemmArgs a;
     a.x = (const uint16_t*)x;
     a.wgu = W_gate_up;
     a.sgu = scales->gate_up;
@@ -243,10 +271,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.list_meta = moe::kMetaNumGemv;
     a.h = ws->h;
     a.y = ws->y;
-    a.T = T;
     a.H = H;
     a.I = I;
-    a.k = k;
     a.tile_done = ws->tile_done;
     a.items = ws->mfma_items;
     a.wts = ws->wts;
@@ -259,7 +285,18 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.hs = ws->h_scales;
     a.queue = ws->queue;
     a.gu_done = ws->gu_done;
-    if (mx8) {
+    a.route_ids = ws->ids;
+    a.route_wts = ws->wts;
+    if (self) {
+        a.pos = nullptr;  // h and y rows are the slots
+        err = moe::launch_self_gate_up(a, lists, st);
+        if (err != hipSuccess) return hip_fail(err, "gate_up");
+        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        err = moe::launch_self_down(a, lists, st);
+        if (err != hipSuccess) return hip_fail(err, "down");
+        err = moe::launch_combine(a, st);
+        if (err != hipSuccess) return hip_fail(err, "combine");
+    } else if (mx8) {
         const int max_items = max_active + S / moe::kMx8Tok + 1;
         err = moe::launch_mx8_gate_up(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");

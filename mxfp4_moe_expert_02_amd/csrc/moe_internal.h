@@ -58,6 +58,19 @@ constexpr int kMfmaWideMeanTok = MOE_WIDE_MEAN_TOK;
 // MXFP8 (prefill) path: items of up to kMx8Tok tokens (eight 16-token MFMA
 // column tiles), weights in the same tile layout.
 constexpr int kMx8Tok = 128;
+// Self-routed layer (no routing pass): up to kSelfMaxTok tokens (one MFMA
+// column tile per expert), whose logits [T, E] (T*E <= kSelfMaxPairs) the
+// weight pass holds in LDS.
+constexpr int kSelfMaxTok = 16;
+constexpr int kSelfMaxPairs = 4096;
+// Per-expert slot list of the self-routed layer: m, then the slots t*k + j
+// of its m tokens in ascending token order (one 128-byte line per expert).
+// Layers whose two GEMM grids hold at least kSelfListUnits workgroups
+// (E * (I/32 + H/128)) write the lists in a pre-pass (one wave per expert)
+// and the GEMM workgroups read them; smaller layers rank in every GEMM
+// workgroup (no pre-pass launch).
+constexpr int kSlotListInts = 32;
+constexpr int kSelfListUnits = 2048;
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaDownRows = 32;
 constexpr int kMfmaThreads = 256;
@@ -83,6 +96,7 @@ struct Workspace {
     int32_t* bhist = nullptr;      // [ceil(Tmax*kmax/kRouteSlotBlock) * E] per-block expert histograms
     int32_t* queue = nullptr;      // [kQueueWords] single-launch layer: next unit, error flag
     int32_t* gu_done = nullptr;    // [E + Tmax*kmax/kMfmaTok + 1] finished gate_up units per MFMA item
+    int32_t* slot_lists = nullptr; // [E * kSlotListInts] self-routed layer: per-expert slot lists
     int max_items = 0;             // entries of mfma_items / gu_done
     int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
@@ -118,12 +132,19 @@ struct GemmArgs {
     uint8_t* hq;                // [T*k, I] E4M3 codes of h (sorted rows)
     uint8_t* hs;                // [T*k, I/32] E8M0 scales of h
     const float* wts;           // [T*k] routing weights
-    const int32_t* pos;         // [T*k] slot -> row of y
+    const int32_t* pos;         // [T*k] slot -> row of y; null: row = slot (self-routed layer)
     uint16_t* out;              // [T, H] bf16
     int col_tiles;
     // single-launch layer (route, then one kernel for gate_up + down + combine)
     int32_t* queue;             // [kQueueWords], zeroed by the route
     int32_t* gu_done;           // [max items] finished gate_up units per item, zeroed by the route
+    // self-routed layer (no routing pass): each GEMM workgroup ranks its own
+    // expert for every token from the router logits
+    const float* logits;        // [T, E] fp32
+    int E;
+    int32_t* route_ids;         // [T*k] written by the weight pass (expert per slot)
+    float* route_wts;           // [T*k] written by the weight pass (= wts)
+    int32_t* slot_lists;        // [E * kSlotListInts] per-expert slot lists
 };
 
 // ---------------------------------------------------------------- launchers
@@ -146,10 +167,22 @@ hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t strea
 // launch_combine forms out.
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream);
+// Self-routed layer of at most kSelfMaxTok tokens (route_rank.h): no
+// sorting pass.  gate_up runs one workgroup per (expert, row tile), each of
+// which finds its expert's tokens (ranked from the logits, or from the slot
+// lists; experts with none exit), plus one workgroup that writes the
+// routing weights; down runs one per (expert, column tile pair).  h and y
+// rows are indexed by slot t*k + j, so launch_combine runs with pos = null.
+// lists: the GEMM workgroups read the slot lists written by
+// launch_slot_lists instead of ranking their experts themselves.
+hipError_t launch_slot_lists(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_self_gate_up(const GemmArgs& a, bool lists, hipStream_t stream);
+hipError_t launch_self_down(const GemmArgs& a, bool lists, hipStream_t stream);
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream);
 // out = the weighted sum of the k per-assignment rows of y per token, in
-// slot order (after a down kernel of the split launch).
+// slot order (after a down kernel of the split launch); the row of slot s
+// is pos[s], or s itself when pos is null.
 hipError_t launch_combine(const GemmArgs& a, hipStream_t stream);
 // The same two GEMMs (and the combine) in one persistent launch: workgroups
 // dequeue gate_up units (item, row tile), then down units, each of which

@@ -25,7 +25,7 @@
 #include <float.h>
 #include <limits.h>
 
-#include "moe_internal.h"
+#include "route_rank.h"
 
 namespace moe {
 namespace {
@@ -40,11 +40,6 @@ static_assert(kFusedMaxPairs <= kFusedPairs, "the single-workgroup route holds T
 constexpr int kSlotBlock = kRouteSlotBlock;
 constexpr int kTopkThreads = 256;
 constexpr int kSortLdsInts = 12288;   // per-range histograms
-
-// a beats b: larger logit, or equal logit and lower expert index
-__device__ inline bool beats(float av, int ai, float bv, int bi) {
-    return av > bv || (av == bv && ai < bi);
-}
 
 // Inclusive prefix sum over a wave64 with DPP row shifts and row broadcasts.
 __device__ inline int wave_incl_scan(int v) {
@@ -64,40 +59,6 @@ __device__ inline int wave_incl_scan(int v) {
     v += t;
     (void)lane;
     return v;
-}
-
-// Rank-count top-k of the tokens [t0, t0+nt) whose logits sit in LDS
-// (lg[i*E + e] for token t0+i).  sel_id/sel_l [nt*k] are LDS scratch.
-// Writes ids and weights of those tokens.  Uses every thread of the block.
-__device__ void topk_tokens(const float* lg, int nt, int t0, int E, int k, int* sel_id,
-                            float* sel_l, int32_t* ids, float* wts) {
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    for (int i = tid; i < nt * k; i += nthr) {
-        sel_id[i] = i % k;  // defined even if NaN logits leave a rank unfilled
-        sel_l[i] = -INFINITY;
-    }
-    __syncthreads();
-    for (int p = tid; p < nt * E; p += nthr) {
-        const int i = p / E, e = p % E;
-        const float* row = lg + i * E;
-        const float v = row[e];
-        int rank = 0;
-        for (int f = 0; f < E; f++) rank += beats(row[f], f, v, e) ? 1 : 0;
-        if (rank < k) {
-            sel_id[i * k + rank] = e;
-            sel_l[i * k + rank] = v;
-        }
-    }
-    __syncthreads();
-    for (int p = tid; p < nt * k; p += nthr) {
-        const int i = p / k, j = p % k;
-        const float top = sel_l[i * k];
-        float s = 0.f;
-        for (int q = 0; q < k; q++) s += __expf(sel_l[i * k + q] - top);
-        const int64_t o = (int64_t)(t0 + i) * k + j;
-        ids[o] = sel_id[p];
-        wts[o] = __expf(sel_l[p] - top) / s;
-    }
 }
 
 // s_off[e] = exclusive prefix sum of s_cnt over experts, s_off[E] = total
@@ -358,7 +319,26 @@ route_scatter_kernel(const int32_t* __restrict__ ids, int S, int E,
     }
 }
 
+// Slot lists of the self-routed layer: wave w of block b ranks expert
+// e = 4b + w for every token (expert_slots) and writes m and the slots.
+__global__ void __launch_bounds__(kWave * 4)
+slot_lists_kernel(const float* __restrict__ logits, int T, int E, int k,
+                  int32_t* __restrict__ lists) {
+    const int e = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (e >= E) return;
+    int slot;
+    const int m = expert_slots(logits, T, E, k, e, &slot);
+    int32_t* list = lists + e * kSlotListInts;
+    if (lane < m) list[1 + lane] = slot;
+    if (lane == 0) list[0] = m;
+}
+
 }  // namespace
+
+hipError_t launch_slot_lists(const GemmArgs& a, hipStream_t stream) {
+    slot_lists_kernel<<<(a.E + 3) / 4, kWave * 4, 0, stream>>>(a.logits, a.T, a.E, a.k, a.slot_lists);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const Workspace& ws,
                         int gemv_max_tokens, int path, int item_tok, hipStream_t stream) {

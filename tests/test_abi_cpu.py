@@ -111,12 +111,13 @@ def test_forward_validation_without_gpu(L):
     bad_layout.weight_layout = 5
     assert _fwd(L, opt=bad_layout) == L.MOE_E_OPTION
     bad_launch = L.moe_mxfp4_options(0, 0)
-    bad_launch.launch = 3
+    bad_launch.launch = 4
     assert _fwd(L, opt=bad_launch) == L.MOE_E_OPTION
-    fused = L.moe_mxfp4_options(0, L.MOE_PATH_MFMA)
-    fused.weight_layout = L.MOE_LAYOUT_TILES
-    fused.launch = L.MOE_LAUNCH_FUSED
-    assert _fwd(L, opt=fused) == L.MOE_E_NOT_INIT        # a valid request
+    for launch in (L.MOE_LAUNCH_FUSED, L.MOE_LAUNCH_SELF_ROUTED):
+        req = L.moe_mxfp4_options(0, L.MOE_PATH_MFMA)
+        req.weight_layout = L.MOE_LAYOUT_TILES
+        req.launch = launch
+        assert _fwd(L, opt=req) == L.MOE_E_NOT_INIT      # a valid request
     assert L.lib().moe_mxfp4_forward(0x1000, 0x2000, 9, 2, 0x3000, 0x4000, None, 0x7000,
                                      None) == L.MOE_E_NULL
 
