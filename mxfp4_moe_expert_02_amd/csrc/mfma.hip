@@ -74,10 +74,20 @@ struct XStep {
 
 // One wave: chunks [c_begin, c_end) of one quad against NT column tiles of
 // 16 tokens.  tiles/tscales point at the quad's chunk 0; rows_of(xrow)
-// fills this lane's token row (bf16) of every tile, or null for a zero
-// column, and is called only after the first weight loads are in flight
-// (it usually waits on an index load).  Each weight word is decoded once and
-// feeds the NT tiles' MFMAs.
+// fills this lane's token row (bf16) of every tile -- a real row for every
+// lane: lanes past the item's tokens repeat one of its rows, and their
+// output columns are never stored -- and is called only after the first
+// weight loads are in flight (it usually waits on an index load).  Each
+// weight word is decoded once and feeds the NT tiles' MFMAs.
+//
+// Per step (CPS chunks): the x loads of this step, then the weight loads of
+// the next step, then the MFMAs.  Loads complete in issue order, so the
+// wait for x leaves the next step's weights in flight during the MFMAs.
+// For that the loads must stay in this order (sched_barrier) and carry no
+// conditions: a load skipped on some path makes the wait conservative, a
+// full drain.  So every load is unconditional -- a partial last step loads
+// its last chunk again (in the same step: a cache hit) and skips that
+// chunk's MFMAs -- and the last step, which prefetches nothing, is peeled.
 template <int NT, typename RowsFn>
 __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowsFn rows_of,
                                  int c_begin, int c_end, f32x4_t (&acc)[kGroups][NT]) {
@@ -88,17 +98,16 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (c_begin >= c_end) return;
+    auto chunk_of = [&](int c0, int i) { return min(c0 + i, c_end - 1); };
     auto load_w = [&](int c0, WStep<CPS>& b) {
 #pragma unroll
         for (int i = 0; i < CPS; i++) {
-            const bool ok = c0 + i < c_end;
-            const uint8_t* t = tiles + (int64_t)(c0 + i) * 4096 + lane * 16;
+            const int ci = chunk_of(c0, i);
+            const uint8_t* t = tiles + (int64_t)ci * 4096 + lane * 16;
 #pragma unroll
-            for (int rg = 0; rg < kGroups; rg++)
-                b.w[i][rg] = ok ? load_stream16(t + rg * 1024) : make_uint4(0, 0, 0, 0);
-            b.s[i] = ok ? *reinterpret_cast<const uint32_t*>(tscales + (int64_t)(c0 + i) * 256 +
-                                                             lane * 4)
-                        : 0x7f7f7f7fu;
+            for (int rg = 0; rg < kGroups; rg++) b.w[i][rg] = load_stream16(t + rg * 1024);
+            b.s[i] = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
         }
     };
     auto load_x = [&](int c0, XStep<NT>& xb) {
@@ -106,16 +115,16 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
         for (int i = 0; i < CPS; i++)
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const bool ok = xrow[t] && (c0 + i < c_end);
-                const uint4* src =
-                    reinterpret_cast<const uint4*>(xrow[t] + (int64_t)(4 * (c0 + i) + g) * 32);
+                const uint4* src = reinterpret_cast<const uint4*>(
+                    xrow[t] + (int64_t)(4 * chunk_of(c0, i) + g) * 32);
 #pragma unroll
-                for (int q = 0; q < 4; q++) xb.x[i][t][q] = ok ? src[q] : make_uint4(0, 0, 0, 0);
+                for (int q = 0; q < 4; q++) xb.x[i][t][q] = src[q];
             }
     };
-    auto compute = [&](const WStep<CPS>& b, const XStep<NT>& xb) {
+    auto compute = [&](int c0, const WStep<CPS>& b, const XStep<NT>& xb) {
 #pragma unroll
         for (int i = 0; i < CPS; i++) {
+            if (c0 + i >= c_end) break;  // the repeated chunk of a partial step
 #pragma unroll
             for (int q = 0; q < 4; q++) {
 #pragma unroll
@@ -134,20 +143,33 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
     WStep<CPS> wa, wb;
     XStep<NT> xa;
     int c = c_begin;
-    if (c < c_end) load_w(c, wa);
+    int left = (c_end - c_begin + CPS - 1) / CPS;  // steps
+    load_w(c, wa);
     rows_of(xrow);
-    while (c < c_end) {
-        const int n1 = c + CPS;
-        if (n1 < c_end) load_w(n1, wb);  // prefetch the next step's weights
+    while (left >= 3) {  // two steps, each with a successor to prefetch
         load_x(c, xa);
-        compute(wa, xa);
-        c = n1;
-        if (c >= c_end) break;
-        const int n2 = c + CPS;
-        if (n2 < c_end) load_w(n2, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wb);
+        compute(c, wa, xa);
+        c += CPS;
         load_x(c, xa);
-        compute(wb, xa);
-        c = n2;
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wa);
+        compute(c, wb, xa);
+        c += CPS;
+        left -= 2;
+    }
+    if (left == 2) {
+        load_x(c, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wb);
+        compute(c, wa, xa);
+        c += CPS;
+        load_x(c, xa);
+        compute(c, wb, xa);
+    } else {
+        load_x(c, xa);
+        compute(c, wa, xa);
     }
 }
 
@@ -202,7 +224,7 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, const Ro
 #pragma unroll
                       for (int t = 0; t < NT; t++) {
                           const int j = 16 * t + c;
-                          xrow[t] = j < m ? a.x + (int64_t)(rows.slot(a, j) / a.k) * K : nullptr;
+                          xrow[t] = a.x + (int64_t)(rows.slot(a, min(j, m - 1)) / a.k) * K;
                       }
                   },
                   cb, ce, acc);
@@ -263,7 +285,7 @@ __device__ inline void down_item(const GemmArgs& a, int pair, int e, const Rows&
 #pragma unroll
                           for (int t = 0; t < NT; t++) {
                               const int j = 16 * t + c;
-                              xrow[t] = j < m ? a.h + (int64_t)rows.row(j) * K : nullptr;
+                              xrow[t] = a.h + (int64_t)rows.row(min(j, m - 1)) * K;
                           }
                       },
                       half ? hc : 0, half ? chunks : hc, acc);

@@ -10,8 +10,8 @@
 // into LDS and read by all four waves.  Wave w computes quad 4qb+w against
 // all NT column tiles:
 //   A: the quad's 4 KB tile of the chunk, 16 bytes per lane per row group,
-//      decoded with v_cvt_scalef32_pk_bf16_fp4 (block scale applied), two
-//      chunks of weights in flight ahead of the MFMAs;
+//      decoded with v_cvt_scalef32_pk_bf16_fp4 (block scale applied), the
+//      next chunk's weights loaded during the MFMAs;
 //   B: lane (c, g) reads elements 32g + 8q .. +7 of token row c from LDS
 //      (rows padded to 272 bytes: a quarter-wave's 16-byte reads then cover
 //      all banks once);
@@ -27,9 +27,6 @@ namespace {
 
 #ifndef MOE_WIDE_WAVES_PER_EU
 #define MOE_WIDE_WAVES_PER_EU 2
-#endif
-#ifndef MOE_WIDE_WBUF
-#define MOE_WIDE_WBUF 2
 #endif
 
 constexpr int kWThreads = 256;
@@ -101,56 +98,44 @@ __device__ inline void chunk_mfma(const WSmem& sm, int buf, const WChunk& b,
 }
 
 // Main loop of one workgroup over all `chunks` chunks.  live: this wave's
-// quad exists (all waves stage x and meet every barrier either way).
+// quad exists (all waves stage x and meet every barrier either way).  Two
+// weight buffers alternate: chunk s+1 is loaded into the buffer that chunk
+// s-1 just left while chunk s is computed.  (Written as a loop over two
+// unrolled steps with exits, which the compiler allocates in 164 VGPRs --
+// three workgroups per CU -- where other forms of the same loop take 242.)
 template <int NT>
 __device__ inline void wide_mainloop(const uint8_t* tiles, const uint8_t* tscales, bool live,
                                      const uint16_t* const (&rows)[NT], int chunks, WSmem& sm,
                                      f32x4_t (&acc)[kGroups][NT]) {
+    constexpr int WB = 2;
 #pragma unroll
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     XStage<NT> st;
     x_load<NT>(rows, 0, st);
-#if MOE_WIDE_WBUF == 3
-    WChunk w0, w1, w2;
+    WChunk w[WB];
     if (live) {
-        load_chunk(tiles, tscales, 0, w0);
-        if (chunks > 1) load_chunk(tiles, tscales, 1, w1);
+#pragma unroll
+        for (int i = 0; i < WB - 1; i++)
+            if (i < chunks) load_chunk(tiles, tscales, i, w[i]);
     }
-#else
-    WChunk w0, w1;
-    if (live) load_chunk(tiles, tscales, 0, w0);
-#endif
     x_store<NT>(sm, 0, st);
     __syncthreads();
-    // weight buffers in rotation: chunk s + WBUF - 1 is loaded while s computes
     auto step = [&](int s, WChunk& cur, WChunk& ahead) {
         const int nxt = s + 1 < chunks ? s + 1 : s;
         x_load<NT>(rows, nxt, st);
-        if (live && s + MOE_WIDE_WBUF - 1 < chunks)
-            load_chunk(tiles, tscales, s + MOE_WIDE_WBUF - 1, ahead);
+        if (live && s + WB - 1 < chunks) load_chunk(tiles, tscales, s + WB - 1, ahead);
         if (live) chunk_mfma<NT>(sm, s & 1, cur, acc);
         x_store<NT>(sm, (s & 1) ^ 1, st);
         __syncthreads();
     };
-    int s = 0;
-    while (true) {
-#if MOE_WIDE_WBUF == 3
-        if (s >= chunks) break;
-        step(s, w0, w2);
-        if (++s >= chunks) break;
-        step(s, w1, w0);
-        if (++s >= chunks) break;
-        step(s, w2, w1);
-        ++s;
-#else
-        if (s >= chunks) break;
-        step(s, w0, w1);
-        if (++s >= chunks) break;
-        step(s, w1, w0);
-        ++s;
-#endif
+    for (int s0 = 0; s0 < chunks; s0 += WB) {
+#pragma unroll
+        for (int i = 0; i < WB; i++) {
+            if (s0 + i >= chunks) break;
+            step(s0 + i, w[i], w[(i + WB - 1) % WB]);
+        }
     }
 }
 

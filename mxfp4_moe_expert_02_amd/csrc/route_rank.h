@@ -64,9 +64,9 @@ __device__ inline void topk_tokens(const float* lg, int nt, int t0, int E, int k
 // expert 64*chunk + l of the token's row (one coalesced load per pair) and
 // e's own logit, and a ballot counts the experts that beat e; the count
 // goes to lane t, which ends with the rank of e for token t.  Returns the
-// number m of tokens with rank < k; lane c (c = lane % 16 < m) gets in
-// *slot the slot t*k + rank of the c-th of them in ascending token order.
-// Every wave gets the same result.
+// number m of tokens with rank < k; lane c (c = lane % 16) gets in *slot
+// the slot t*k + rank of the c-th of them in ascending token order (lanes
+// c >= m: the last one's).  Every wave gets the same result.
 __device__ inline int expert_slots(const float* __restrict__ logits, int T, int E, int k, int e,
                                    int* slot) {
     const int lane = threadIdx.x % kWave;
@@ -101,13 +101,15 @@ __device__ inline int expert_slots(const float* __restrict__ logits, int T, int 
         }
     }
     const uint64_t chosen = __ballot(lane < T && my_rank < k);  // bit t: token t
-    // lane c: the c-th chosen token (the lowest set bit after dropping c)
+    const int m = __popcll(chosen);
+    // lane c: the c-th chosen token (the lowest set bit after dropping c);
+    // lanes c >= m take the last one, so every lane holds a real slot
     uint64_t rest = chosen;
-    for (int i = 0; i < lane % 16 && rest; i++) rest &= rest - 1;
+    for (int i = 0; i < min(lane % 16, m - 1); i++) rest &= rest - 1;
     const int src = rest ? __builtin_ctzll(rest) : 0;
     const int rank = __builtin_amdgcn_ds_bpermute(src * 4, my_rank);
     *slot = src * k + rank;
-    return __popcll(chosen);
+    return m;
 }
 
 }  // namespace moe
