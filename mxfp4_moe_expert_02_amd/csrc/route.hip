@@ -280,11 +280,18 @@ route_scan_kernel(int nblk, int E, Workspace ws, int32_t* __restrict__ bhist, in
     __shared__ int s_off[kMaxExperts + 1];
     const int tid = threadIdx.x, nthr = blockDim.x;
     for (int e = tid; e < E; e += nthr) {  // per expert: exclusive scan over blocks
+        // 16 blocks' counts at a time, loaded before any is rewritten: one
+        // memory latency per 16 blocks instead of one per block
         int run = 0;
-        for (int b = 0; b < nblk; b++) {
-            const int c = bhist[(int64_t)b * E + e];
-            bhist[(int64_t)b * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) c[i] = b0 + i < nblk ? bhist[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                if (b0 + i < nblk) bhist[(int64_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
         }
         s_cnt[e] = run;
         ws.counts[e] = run;
