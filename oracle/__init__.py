@@ -12,6 +12,8 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
   route ....................... pinned (brute-force sort, softmax identity)
   forward ..................... pinned (closed forms, scale identities,
                                   brute.py on tiny shapes)
+  router_logits ............... pinned (brute-force loop, unit-vector
+                                  closed form, exact power-of-two scaling)
 """
 from __future__ import annotations
 
@@ -105,6 +107,31 @@ def quantize_mxfp8(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     if rc:
         raise ValueError(f"oracle_quantize_mxfp8 failed ({rc})")
     return codes, scales
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> their exact values (a bf16 is the top half of
+    an IEEE binary32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to quiet NaNs
+        return b.view(np.float32).astype(np.float64)
+
+
+def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """Router logits [T, E] in fp64: logits[t, e] = sum_h x[t, h] * W[e, h]
+    over the exact bf16 values (the router linear layer upstream of top-k,
+    kept at the activations' precision).  Products of two bf16 are exact in
+    fp64; only the sum rounds."""
+    x = bf16_bits_to_f64(x_bf16)
+    w = bf16_bits_to_f64(w_bf16)
+    assert x.ndim == 2 and w.ndim == 2 and x.shape[1] == w.shape[1]
+    return x @ w.T
+
+
+def router_logits_abs(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """sum_h |x[t, h] * W[e, h]| -- the scale of the rounding error of any
+    summation order of the router products (for error bounds)."""
+    return np.abs(bf16_bits_to_f64(x_bf16)) @ np.abs(bf16_bits_to_f64(w_bf16)).T
 
 
 def route(logits: np.ndarray, k: int) -> dict:

@@ -30,6 +30,7 @@ import numpy as np
 
 # stream tags inside a SeedSequence
 _S_X, _S_LOGITS, _S_BIAS, _S_ZIPF_RANK, _S_GATE_UP, _S_DOWN = 1, 2, 3, 4, 10, 11
+_S_ROUTER = 12
 
 WEIGHT_STD = 0.02
 
@@ -123,6 +124,17 @@ def make_logits(cfg: Config, seed: int | None = None) -> np.ndarray:
         g = _rng(seed, _S_LOGITS).gumbel(size=shape)
         return (-1.1 * np.log(rank)[None, :] + g).astype(np.float32)
     raise ValueError(f"unknown logits recipe {cfg.logits!r}")
+
+
+def make_router_weight_bf16(cfg: Config, seed: int | None = None) -> np.ndarray:
+    """Router weight [E, H] as bfloat16 bit patterns (uint16), from
+    N(0, 1/sqrt(H)): with x ~ N(0, 1) the logits x . w_e are then about
+    N(0, 1), the configs' logit distribution."""
+    import torch  # conversion only; torch rounds float32 -> bfloat16 to nearest even
+    seed = cfg.seed if seed is None else seed
+    w = _rng(seed, _S_ROUTER).standard_normal((cfg.E, cfg.H), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(cfg.H))
+    return torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
 def weight_shape(cfg: Config, which: str) -> tuple[int, int]:
