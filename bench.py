@@ -58,6 +58,9 @@ def parse():
                    help="bf16 MFMA path: auto (the library's choice: self-routed for at most "
                         "16 tokens), split (routing kernel, then the GEMMs), self (no routing "
                         "kernel: each GEMM workgroup ranks its own expert)")
+    p.add_argument("--router", action="store_true",
+                   help="compute the router logits in the layer from a bf16 router weight [E, H] "
+                        "(x . W_router^T on the matrix cores) instead of taking them as input")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
@@ -193,12 +196,6 @@ def main():
     layout = M.MOE_LAYOUT_TILES if path == M.MOE_PATH_MFMA else M.MOE_LAYOUT_ROWS
     wgu, wdn, scales = layer.weights(layout)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
-                           gemm_path=path, weight_layout=layout, counts=counts, act_format=act)
-    torch.cuda.synchronize()
-    counts_np = counts.cpu().numpy()
-    gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
-    total_bytes = gu_bytes + dn_bytes
 
     launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
               "self": M.MOE_LAUNCH_SELF_ROUTED}[args.launch]
@@ -207,10 +204,24 @@ def main():
                and cfg.T * cfg.E <= 4096)
     self_routed = self_ok and launch in (M.MOE_LAUNCH_AUTO, M.MOE_LAUNCH_SELF_ROUTED)
 
+    router = None
+    if args.router:
+        from workloads import make_router_weight_bf16
+        router = torch.from_numpy(make_router_weight_bf16(cfg).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+
     def step(events=None):
-        M.moe_mxfp4_forward_ex(layer.x, layer.logits, cfg.k, wgu, wdn, scales, layer.out,
-                               gemm_path=path, weight_layout=layout, events=events,
-                               act_format=act, launch=launch)
+        M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, wgu,
+                               wdn, scales, layer.out, gemm_path=path, weight_layout=layout,
+                               events=events, act_format=act, launch=launch, router_weight=router)
+
+    M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, wgu, wdn,
+                           scales, layer.out, gemm_path=path, weight_layout=layout, counts=counts,
+                           act_format=act, router_weight=router)
+    torch.cuda.synchronize()
+    counts_np = counts.cpu().numpy()
+    gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
+    total_bytes = gu_bytes + dn_bytes
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -341,6 +352,8 @@ def main():
                        touched_weight_bytes=int(total_bytes),
                        gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
                        launch="self_routed" if self_routed else "split",
+                       router="computed in the layer from W_router [E,H] bf16" if router is not None
+                       else "logits given",
                        weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",
                        activations="mxfp8" if mx8 else "bf16"),
         "tflops": {"layer": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),

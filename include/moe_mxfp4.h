@@ -152,6 +152,18 @@ typedef struct moe_mxfp4_options {
      * million polls; a correct launch never reaches that.  0 in split
      * launches. */
     int32_t* wait_error;
+    /* Optional [E, H] bf16 router weight (device, row-major, 16-byte
+     * aligned).  When set, the layer computes its router logits itself,
+     * logits[t, e] = sum_h x[t, h] * W_router[e, h] -- bf16 products summed
+     * in fp32 on the matrix cores, split over K for small T with the
+     * partial sums added in a fixed order, so the same inputs give the same
+     * bits -- and routes on them; router_logits is then ignored (it may be
+     * NULL).  The pages keep routing at the model's original precision
+     * (sandbot 1000-TPS post, technical-breakdown section). */
+    const void* router_weight;
+    /* Optional [T, E] fp32 device output: the logits the layer routed on
+     * (the computed ones with router_weight, else a copy of router_logits). */
+    float* logits_out;
 } moe_mxfp4_options;
 
 /* Allocate the workspace on the current device for layers with at most

@@ -61,7 +61,8 @@ class moe_mxfp4_options(ctypes.Structure):
                 ("sorted", ctypes.c_void_p), ("x_codes", ctypes.c_void_p),
                 ("x_scales", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
                 ("num_events", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
-                ("launch", ctypes.c_int32), ("wait_error", ctypes.c_void_p)]
+                ("launch", ctypes.c_int32), ("wait_error", ctypes.c_void_p),
+                ("router_weight", ctypes.c_void_p), ("logits_out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -145,6 +146,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                          counts=None, offsets=None, sorted=None, x_codes=None,
                          x_scales=None, events=None, weight_layout: int = MOE_LAYOUT_ROWS,
                          launch: int = MOE_LAUNCH_AUTO, wait_error=None,
+                         router_weight=None, logits_out=None,
                          check: bool = True, validate: bool = True) -> int:
     """Enqueue one layer on ``stream`` (default: torch's current stream).
 
@@ -155,13 +157,21 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     ``events``: up to 4 torch.cuda.Event (timing enabled) recorded by the
     library at its stage boundaries.  ``launch``: MOE_LAUNCH_*;
     ``wait_error``: optional int32 [1] device tensor (see the header).
+    ``router_weight``: optional [E, H] bfloat16: the layer computes the
+    logits itself (``router_logits`` may then be None); ``logits_out``:
+    optional [T, E] float32 output of the logits routed on.
     """
     import torch
     if validate:
         T, H = x.shape
-        E = router_logits.shape[1]
+        E = router_weight.shape[0] if router_weight is not None else router_logits.shape[1]
         _expect(x, torch.bfloat16, (T, H), "x")
-        _expect(router_logits, torch.float32, (T, E), "router_logits")
+        if router_weight is not None:
+            _expect(router_weight, torch.bfloat16, (E, H), "router_weight")
+        else:
+            _expect(router_logits, torch.float32, (T, E), "router_logits")
+        if logits_out is not None:
+            _expect(logits_out, torch.float32, (T, E), "logits_out")
         I2 = W_gate_up.numel() * 2 // (E * H)  # 2I from the byte count (both layouts)
         for t, n, name in ((W_gate_up, E * I2 * H // 2, "W_gate_up"), (W_down, E * H * I2 // 4, "W_down"),
                            (scales[0], E * I2 * H // 32, "scales[0]"),
@@ -183,7 +193,8 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     opt = moe_mxfp4_options(act_format, gemm_path, _ptr(ids), _ptr(weights), _ptr(counts),
                             _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
                             ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
-                            n_ev, weight_layout, launch, _ptr(wait_error))
+                            n_ev, weight_layout, launch, _ptr(wait_error), _ptr(router_weight),
+                            _ptr(logits_out))
     T = x.shape[0] if x is not None else 0
     rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,

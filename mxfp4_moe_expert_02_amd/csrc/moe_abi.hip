@@ -66,6 +66,11 @@ size_t layout(Workspace* ws, char* base) {
     ws->queue = (int32_t*)take(moe::kQueueWords * 4);
     ws->gu_done = (int32_t*)take((size_t)ws->max_items * 4);
     ws->slot_lists = (int32_t*)take((size_t)ws->E * moe::kSlotListInts * 4);
+    const size_t TE = (size_t)ws->max_tokens * ws->E;
+    const size_t split_te = TE < (size_t)moe::kRouterWaves * 512 ? TE : (size_t)moe::kRouterWaves * 512;
+    ws->logits = (float*)take(TE * 4);
+    ws->router_partial = (float*)take((size_t)moe::kRouterMaxSplit * split_te * 4);
+    ws->router_cnt = (int32_t*)take((size_t)2 * moe::kRouterWaves * 4);
     ws->h = (uint16_t*)take(S * ws->I * 2);
     ws->y = (float*)take(S * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
@@ -195,10 +200,13 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         o.launch != MOE_LAUNCH_FUSED && o.launch != MOE_LAUNCH_SELF_ROUTED)
         return MOE_E_OPTION;
     if (num_tokens == 0) return MOE_OK;
-    if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
+    if (o.router_weight) router_logits = nullptr;  // ignored: the layer computes the logits
+    if (!x || (!router_logits && !o.router_weight) || !W_gate_up || !W_down || !scales || !out)
+        return MOE_E_NULL;
     if (!scales->gate_up || !scales->down) return MOE_E_NULL;
     if (top_k < 1) return MOE_E_TOPK;
-    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(W_gate_up) ||
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(o.router_weight) ||
+        !aligned16(W_gate_up) ||
         !aligned16(W_down) || !aligned16(scales->gate_up) || !aligned16(scales->down) ||
         !aligned16(out))
         return MOE_E_ALIGN;
@@ -219,6 +227,12 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     hipError_t err;
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    if (o.router_weight) {  // the router linear layer, ahead of the routing
+        err = moe::launch_router_gemm((const uint16_t*)x, (const uint16_t*)o.router_weight, T, E, H,
+                                      *ws, ws->logits, st);
+        if (err != hipSuccess) return hip_fail(err, "router");
+        router_logits = ws->logits;
+    }
     const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
     const bool mx8 = o.act_format == MOE_ACT_MXFP8;
     // bf16 MFMA items: 16 tokens, or up to 64 when experts average >= 8
@@ -346,6 +360,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         {mx8 ? o.x_codes : nullptr, ws->x_codes, (size_t)T * H},
         {mx8 ? o.x_scales : nullptr, ws->x_scales, (size_t)T * (H / 32)},
         {o.wait_error, ws->queue + moe::kQueueError, 4},
+        {o.logits_out, router_logits, (size_t)T * E * 4},
     };
     for (auto& c : copies) {
         if (!c.dst) continue;

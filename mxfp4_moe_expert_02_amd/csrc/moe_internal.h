@@ -71,6 +71,12 @@ constexpr int kSelfMaxPairs = 4096;
 // workgroup (no pre-pass launch).
 constexpr int kSlotListInts = 32;
 constexpr int kSelfListUnits = 2048;
+// router GEMM: K is split (at most kRouterMaxSplit ways, over tiles of 16
+// tokens x 16 experts) only for layers of fewer than kRouterWaves / 2 tiles
+// of 16 tokens x 64 experts, so then T*E < kRouterWaves * 512 and there are
+// fewer than kRouterWaves * 2 split tiles
+constexpr int kRouterWaves = 256;
+constexpr int kRouterMaxSplit = 16;
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaDownRows = 32;
 constexpr int kMfmaThreads = 256;
@@ -97,6 +103,9 @@ struct Workspace {
     int32_t* queue = nullptr;      // [kQueueWords] single-launch layer: next unit, error flag
     int32_t* gu_done = nullptr;    // [E + Tmax*kmax/kMfmaTok + 1] finished gate_up units per MFMA item
     int32_t* slot_lists = nullptr; // [E * kSlotListInts] self-routed layer: per-expert slot lists
+    float* logits = nullptr;       // [Tmax * E] logits computed from a router weight
+    float* router_partial = nullptr;  // [kRouterMaxSplit * min(Tmax*E, kRouterWaves*512)] split-K partials
+    int32_t* router_cnt = nullptr;    // [2 * kRouterWaves] finished splits per tile (split-K only)
     int max_items = 0;             // entries of mfma_items / gu_done
     int col_tiles = 0;             // H / kColTile
     uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
@@ -175,6 +184,9 @@ hipError_t launch_mfma_down(const GemmArgs& a, int max_items, hipStream_t stream
 // rows are indexed by slot t*k + j, so launch_combine runs with pos = null.
 // lists: the GEMM workgroups read the slot lists written by
 // launch_slot_lists instead of ranking their experts themselves.
+// logits [T, E] fp32 = x [T, H] bf16 . wr [E, H]^T bf16 (router.hip)
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wr, int T, int E, int H,
+                              const Workspace& ws, float* logits, hipStream_t stream);
 hipError_t launch_slot_lists(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_self_gate_up(const GemmArgs& a, bool lists, hipStream_t stream);
 hipError_t launch_self_down(const GemmArgs& a, bool lists, hipStream_t stream);

@@ -31,13 +31,15 @@ def get_layer(cfg: Config, logits=None):
     return _layers[key]
 
 
-def run(M, layer, path=0, debug=False, act=0, launch=0, init=True):
+def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None):
     """One forward through the C ABI on every token of the layer; returns
     the requested debug outputs (routing; with MXFP8 also the codes of x)
     as numpy arrays.  out is NaN-filled first, so every element it holds
     afterwards was written by this call.  launch: MOE_LAUNCH_* (the fused
     launch also returns its wait-error flag as "wait_error"); init=False
-    keeps the current workspace (and whatever an earlier call left in it)."""
+    keeps the current workspace (and whatever an earlier call left in it).
+    router: a [E, H] bf16 device router weight -- the layer then computes its
+    own logits (returned as "logits") and is given no router_logits."""
     import torch
     c = layer.cfg
     if init:
@@ -55,6 +57,10 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True):
             dbg["x_scales"] = torch.empty((c.T, c.H // 32), dtype=torch.uint8, device="cuda")
     if launch == M.MOE_LAUNCH_FUSED:
         dbg["wait_error"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    extra = {}
+    if router is not None:
+        dbg["logits_out"] = torch.full((c.T, c.E), float("nan"), dtype=torch.float32, device="cuda")
+        extra["router_weight"] = router
     layer.out.fill_(float("nan"))
     torch.cuda.synchronize()
     say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path} act={act} "
@@ -62,9 +68,9 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True):
     mfma = path == M.MOE_PATH_MFMA or act == M.MOE_ACT_MXFP8
     layout = M.MOE_LAYOUT_TILES if mfma else M.MOE_LAYOUT_ROWS
     wgu, wdn, scales = layer.weights(layout)
-    M.moe_mxfp4_forward_ex(layer.x, layer.logits, c.k, wgu, wdn, scales, layer.out,
-                           gemm_path=path, weight_layout=layout, act_format=act, launch=launch,
-                           **dbg)
+    M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, c.k, wgu, wdn,
+                           scales, layer.out, gemm_path=path, weight_layout=layout,
+                           act_format=act, launch=launch, **dbg, **extra)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in dbg.items()}
 
