@@ -39,8 +39,8 @@
  * Ownership: the caller owns every tensor and keeps it alive until the work
  * enqueued on `stream` has completed.  The library keeps no caller pointer.
  * It owns one workspace per device (routing arrays, h, per-assignment
- * outputs, queue counters), allocated by moe_mxfp4_init; the forward calls
- * never allocate.
+ * outputs, the shared expert's rows, queue counters), allocated by
+ * moe_mxfp4_init; the forward calls never allocate.
  *
  * Errors: arguments are validated synchronously before anything is
  * enqueued; a failed check returns a negative status, enqueues nothing and
@@ -164,6 +164,25 @@ typedef struct moe_mxfp4_options {
     /* Optional [T, E] fp32 device output: the logits the layer routed on
      * (the computed ones with router_weight, else a copy of router_logits). */
     float* logits_out;
+    /* Optional shared expert, all four set or all NULL (else MOE_E_NULL),
+     * each 16-byte aligned.  The pages store only the MoE experts in 4 bits
+     * and keep the rest of the model at FP8 (bjdmk.com.cn news page,
+     * co-design section; yifor-blog digest, selective FP4 quantisation); a
+     * shared expert is read as one more SiLU-gated FFN of the routed
+     * experts' shape (gate/up [2I, H], down [H, I]) whose weights are MXFP8
+     * -- E4M3 codes, one E8M0 scale per 32 along K -- applied to every token
+     * with weight 1:
+     *   out[t,:] += Ws_down ( SiLU(Ws_gate x_t) * (Ws_up x_t) )
+     * added in fp32 after the k routed terms, before the rounding to bf16.
+     * Its h follows the activation format (bf16, or MXFP8 with
+     * MOE_ACT_MXFP8).  The matrices are in the MXFP8 tile layout written by
+     * moe_mxfp8_prepack: shared_gate_up / shared_gate_up_scales from
+     * [2I, H] with gate_up_pairs = 1, shared_down / shared_down_scales from
+     * [H, I] with gate_up_pairs = 0.  Works with every path and launch. */
+    const uint8_t* shared_gate_up;
+    const uint8_t* shared_gate_up_scales;
+    const uint8_t* shared_down;
+    const uint8_t* shared_down_scales;
 } moe_mxfp4_options;
 
 /* Allocate the workspace on the current device for layers with at most
@@ -218,6 +237,31 @@ int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* pack
  * 16-byte aligned, tile_scales 4-byte aligned.  A one-time step at weight
  * load (not part of a forward call).  Enqueued on `stream`. */
 int moe_mxfp4_prepack(const uint8_t* packed, const uint8_t* scales, int64_t num_matrices,
+                      int64_t rows, int64_t cols, int32_t gate_up_pairs, uint8_t* tiles,
+                      uint8_t* tile_scales, void* stream);
+
+/* Encode a float32 matrix w [rows, cols] to MXFP8 along cols (the 8-bit
+ * weights beside the experts, e.g. the shared expert): E4M3 elements
+ * (OCP "FN": no infinities, 0x7F/0xFF NaN), one E8M0 scale per 32, the
+ * OCP MX block rule -- scale 2^(floor(log2 amax) - 8) with the exponent
+ * clamped to [-127, 127], amax == 0 -> scale code 0, elements rounded to
+ * the nearest E4M3 value with ties to the even code and saturating at 448;
+ * a block with a non-finite element gets scale 0xFF and element codes 0.
+ * codes [rows, cols] (one byte per element), scales [rows, cols/32], on the
+ * current device, enqueued on `stream`.  cols % 32 == 0; w and codes
+ * 16-byte aligned.  Returns MOE_OK, MOE_E_SHAPE, MOE_E_NULL, MOE_E_ALIGN or
+ * MOE_E_HIP. */
+int moe_mxfp8_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes,
+                       uint8_t* scales, void* stream);
+
+/* moe_mxfp4_prepack for MXFP8 matrices (codes [.., rows, cols], one byte
+ * per element; scales [.., rows, cols/32]): the same quads, chunks, lanes,
+ * gate/up pairing and scale order, with each 16-row group's codes split in
+ * two halves -- [group][half h][lane][16 bytes], lane r + 16 g holding
+ * bytes 16h..16h+15 of block g of row r -- so tiles holds rows*cols bytes
+ * per matrix (8 KB per quad and chunk) and tile_scales rows*cols/32.  Same
+ * constraints and status codes as moe_mxfp4_prepack. */
+int moe_mxfp8_prepack(const uint8_t* codes, const uint8_t* scales, int64_t num_matrices,
                       int64_t rows, int64_t cols, int32_t gate_up_pairs, uint8_t* tiles,
                       uint8_t* tile_scales, void* stream);
 

@@ -11,7 +11,8 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_MXFP8, MOE_E_ALIGN, MOE_E_HIP, MOE_E_NO
                    MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES, MOE_PATH_AUTO, MOE_PATH_GEMV,
                    MOE_PATH_MFMA, MoeError, lib, moe_mxfp4_prepack,
                    moe_mxfp4_finalize, moe_mxfp4_forward, moe_mxfp4_forward_ex, moe_mxfp4_init,
-                   moe_mxfp4_quantize, moe_mxfp4_status_string, moe_probe_copy,
+                   moe_mxfp4_quantize, moe_mxfp4_status_string, moe_mxfp8_prepack,
+                   moe_mxfp8_quantize, moe_probe_copy,
                    moe_probe_sink_words, moe_probe_stream_read)
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "lib"]

@@ -40,7 +40,7 @@ MOE_LAUNCH_SELF_ROUTED = 3
 
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
-            "moe_mxfp4_prepack",
+            "moe_mxfp4_prepack", "moe_mxfp8_quantize", "moe_mxfp8_prepack",
             "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy")
 
 
@@ -62,7 +62,9 @@ class moe_mxfp4_options(ctypes.Structure):
                 ("x_scales", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
                 ("num_events", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
                 ("launch", ctypes.c_int32), ("wait_error", ctypes.c_void_p),
-                ("router_weight", ctypes.c_void_p), ("logits_out", ctypes.c_void_p)]
+                ("router_weight", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
+                ("shared_gate_up", ctypes.c_void_p), ("shared_gate_up_scales", ctypes.c_void_p),
+                ("shared_down", ctypes.c_void_p), ("shared_down_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -91,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_status_string.argtypes = [ctypes.c_int]
         L.moe_mxfp4_prepack.restype = ctypes.c_int
         L.moe_mxfp4_prepack.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
+        L.moe_mxfp8_prepack.restype = ctypes.c_int
+        L.moe_mxfp8_prepack.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
+        L.moe_mxfp8_quantize.restype = ctypes.c_int
+        L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.moe_probe_stream_read.restype = ctypes.c_int
         L.moe_probe_stream_read.argtypes = [vp, i64, vp, vp]
         L.moe_probe_sink_words.restype = i64
@@ -146,7 +152,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                          counts=None, offsets=None, sorted=None, x_codes=None,
                          x_scales=None, events=None, weight_layout: int = MOE_LAYOUT_ROWS,
                          launch: int = MOE_LAUNCH_AUTO, wait_error=None,
-                         router_weight=None, logits_out=None,
+                         router_weight=None, logits_out=None, shared=None,
                          check: bool = True, validate: bool = True) -> int:
     """Enqueue one layer on ``stream`` (default: torch's current stream).
 
@@ -159,7 +165,9 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     ``wait_error``: optional int32 [1] device tensor (see the header).
     ``router_weight``: optional [E, H] bfloat16: the layer computes the
     logits itself (``router_logits`` may then be None); ``logits_out``:
-    optional [T, E] float32 output of the logits routed on.
+    optional [T, E] float32 output of the logits routed on.  ``shared``:
+    optional (gate_up tiles, gate_up tile scales, down tiles, down tile
+    scales) of an MXFP8 shared expert (moe_mxfp8_prepack layout, uint8).
     """
     import torch
     if validate:
@@ -180,6 +188,14 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                 raise ValueError(f"{name}: expected {n} contiguous uint8 bytes, got "
                                  f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
         _expect(out, torch.bfloat16, (T, H), "out")
+        if shared is not None:
+            I = I2 // 2
+            for t, n, name in ((shared[0], 2 * I * H, "shared[0]"), (shared[1], 2 * I * H // 32, "shared[1]"),
+                               (shared[2], H * I, "shared[2]"), (shared[3], H * I // 32, "shared[3]")):
+                if t.dtype != torch.uint8 or t.numel() != n or not t.is_contiguous():
+                    raise ValueError(f"{name}: expected {n} contiguous uint8 bytes, got "
+                                     f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+    sh = [None] * 4 if shared is None else [_ptr(t) for t in shared]
     sc = moe_mxfp4_scales(_ptr(scales[0]), _ptr(scales[1])) if scales is not None else None
     ev_arr, n_ev = None, 0
     if events:
@@ -194,7 +210,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                             _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
                             ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
                             n_ev, weight_layout, launch, _ptr(wait_error), _ptr(router_weight),
-                            _ptr(logits_out))
+                            _ptr(logits_out), *sh)
     T = x.shape[0] if x is not None else 0
     rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,
@@ -244,6 +260,33 @@ def moe_mxfp4_quantize(w, packed, scales, stream=None, check: bool = True) -> in
     _expect(scales, torch.uint8, (rows, cols // 32), "scales")
     rc = lib().moe_mxfp4_quantize(_ptr(w), rows, cols, _ptr(packed), _ptr(scales), _stream(stream))
     return _check(rc, "moe_mxfp4_quantize") if check else rc
+
+
+def moe_mxfp8_prepack(codes, scales, tiles, tile_scales, gate_up_pairs: bool,
+                      stream=None, check: bool = True) -> int:
+    """Rearrange row-major MXFP8 matrices codes [N, rows, cols] + scales
+    [N, rows, cols/32] into the MXFP8 tile layout (same byte sizes)."""
+    import torch
+    N, rows, cols = codes.shape
+    _expect(scales, torch.uint8, (N, rows, cols // 32), "scales")
+    if tiles.numel() != codes.numel() or tile_scales.numel() != scales.numel():
+        raise ValueError("moe_mxfp8_prepack: output sizes must equal input sizes")
+    rc = lib().moe_mxfp8_prepack(_ptr(codes), _ptr(scales), N, rows, cols,
+                                 1 if gate_up_pairs else 0, _ptr(tiles), _ptr(tile_scales),
+                                 _stream(stream))
+    return _check(rc, "moe_mxfp8_prepack") if check else rc
+
+
+def moe_mxfp8_quantize(w, codes, scales, stream=None, check: bool = True) -> int:
+    """Encode float32 w [rows, cols] to MXFP8 into codes [rows, cols] and
+    scales [rows, cols/32] (uint8 device tensors)."""
+    import torch
+    rows, cols = w.shape
+    _expect(w, torch.float32, (rows, cols), "w")
+    _expect(codes, torch.uint8, (rows, cols), "codes")
+    _expect(scales, torch.uint8, (rows, cols // 32), "scales")
+    rc = lib().moe_mxfp8_quantize(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _stream(stream))
+    return _check(rc, "moe_mxfp8_quantize") if check else rc
 
 
 def moe_probe_sink_words() -> int:

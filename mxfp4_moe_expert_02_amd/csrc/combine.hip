@@ -2,8 +2,9 @@
 // kernel after the down projection (the split launch of the bf16 matrix-core
 // path):
 //
-//   out[t, n] = sum_{j = 0 .. k-1} w[t, j] * y[pos[t, j], n],  fp32 in slot
-//   order j, rounded to bf16 (nearest even)
+//   out[t, n] = sum_{j = 0 .. k-1} w[t, j] * y[pos[t, j], n]  (+ y[sh_row0 + t, n]),
+//   fp32 in slot order j, the shared expert's row (if any) added last,
+//   rounded to bf16 (nearest even)
 //
 // (pos null: the self-routed layer, whose y rows are the slots t*k + j)
 //
@@ -65,6 +66,13 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(GemmArgs a) {
         case 6: combine_batch<6>(a, base, j0, c4, v); break;
         case 7: combine_batch<7>(a, base, j0, c4, v); break;
         default: break;
+    }
+    if (a.sh_wgu) {
+        const float4 s = *reinterpret_cast<const float4*>(a.y + (int64_t)(a.sh_row0 + t) * a.H + 4 * c4);
+        v.x += s.x;
+        v.y += s.y;
+        v.z += s.z;
+        v.w += s.w;
     }
     ushort4 o;
     o.x = f32_to_bf16_rne(v.x);

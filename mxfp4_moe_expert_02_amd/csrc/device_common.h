@@ -38,6 +38,17 @@ __device__ inline bf16x8_t decode8(uint32_t word, float scale) {
     return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 8 E4M3 codes (bytes of lo, then of hi; element i in byte i) -> 8 bf16,
+// block scale applied by the conversion (E4M3 * 2^k is exact in bf16 while
+// the result stays inside bf16's normal range)
+__device__ inline bf16x8_t decode8_e4m3(uint32_t lo, uint32_t hi, float scale) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ inline uint32_t word_of(const uint4& v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
@@ -79,7 +90,7 @@ __device__ inline void wait_count(const int32_t* count, int need, int32_t* err) 
 }
 
 // sum_j w[t,j] * y[pos[t,j], n] over the k slots of token t, in slot order
-// j = 0..k-1, fp32.  y is read with agent-coherent loads because other
+// j = 0..k-1, fp32, plus the shared expert's y[sh_row0 + t, n] if there is one.  y is read with agent-coherent loads because other
 // workgroups of the running kernel wrote it.  The slot indices and weights,
 // then the y values, are fetched 8 slots at a time with unconditional loads
 // (indices clamped to k-1), so each batch costs two memory latencies rather
@@ -104,6 +115,9 @@ __device__ inline float combine_column(const GemmArgs& a, int t, int n) {
         for (int u = 0; u < 8; u++)
             if (j0 + u < a.k) v = fmaf(w[u], yv[u], v);
     }
+    if (a.sh_wgu)  // the shared expert, weight 1, after the k routed terms
+        v += __hip_atomic_load(a.y + (int64_t)(a.sh_row0 + t) * a.H + n, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     return v;
 }
 
@@ -113,18 +127,27 @@ __device__ inline void combine_tile(const GemmArgs& a, int t, int n0, int width)
         a.out[(int64_t)t * a.H + n0 + c] = f32_to_bf16_rne(combine_column(a, t, n0 + c));
 }
 
-// The token rows of one MFMA item, for the lane's column j of a tile.
-// SortedRows: a routed item, rows row0 .. row0+m-1 of the sorted order
-// (its h and y rows), slot sorted[row0 + j].  SlotRows: a self-routed
-// expert of at most 16 tokens (one column tile), where lane c holds the slot
-// t*k + rank of its column's token, which is also its h and y row.
+// The token rows of one MFMA item, for the lane's column j of a tile:
+// row(j) is its h and y row, token(a, j) the token whose x it reads.
+// SortedRows: a routed item, rows row0 .. row0+m-1 of the sorted order,
+// slot sorted[row0 + j].  SlotRows: a self-routed expert of at most 16
+// tokens (one column tile), where lane c holds the slot t*k + rank of its
+// column's token, which is also its h and y row.  TokenRows: the shared
+// expert, tokens t0 .. t0+m-1 in order, rows base + t.
 struct SortedRows {
     int row0, m;
     __device__ int row(int j) const { return row0 + j; }
     __device__ int slot(const GemmArgs& a, int j) const { return a.sorted[row0 + j]; }
+    __device__ int token(const GemmArgs& a, int j) const { return a.sorted[row0 + j] / a.k; }
+};
+struct TokenRows {
+    int t0, m, base;
+    __device__ int row(int j) const { return base + t0 + j; }
+    __device__ int token(const GemmArgs&, int j) const { return t0 + j; }
 };
 struct SlotRows {
     int m, lane_slot;
+    __device__ int token(const GemmArgs& a, int) const { return lane_slot / a.k; }
     __device__ int row(int) const { return lane_slot; }
     __device__ int slot(const GemmArgs&, int) const { return lane_slot; }
 };
@@ -135,6 +158,7 @@ struct ListRows {
     const int32_t* slots;
     __device__ int row(int j) const { return slots[j]; }
     __device__ int slot(const GemmArgs&, int j) const { return slots[j]; }
+    __device__ int token(const GemmArgs& a, int j) const { return slots[j] / a.k; }
 };
 
 // One wave's share of a down-projection tile: acc[rg][t] holds rows 4g..4g+3

@@ -34,6 +34,7 @@
 // go to mfma_wide.hip).  The quad routine is written for NT column tiles;
 // these kernels use NT = 1.
 #include "device_common.h"
+#include "mx_encode.h"
 #include "route_rank.h"
 
 namespace moe {
@@ -50,35 +51,132 @@ constexpr int kWaves = kMfmaThreads / kWave;  // 4, split K
 constexpr int kChunksPerStep = MOE_MFMA_CHUNKS_PER_STEP;  // 128-column chunks per prefetch step
 constexpr int kGroups = 4;                    // 16-row groups per quad
 
-// chunks per prefetch step: kChunksPerStep for single-tile items, one for
-// wider ones (their x operands alone fill 16 VGPRs per tile and chunk)
+// ---- weight formats of the tile layout (one 64-row quad, one 128-k chunk)
+// W4, MXFP4: 4 KB of codes, [group][lane][16 bytes], lane (r, g) holding
+// the 32 codes of block g of row r.  W8, MXFP8 (the 8-bit weights beside
+// the experts): 8 KB, [group][half][lane][16 bytes], half h holding codes
+// 16h..16h+15 of the lane's block.  Both: 256 scale bytes [lane][group].
+// a(b, rg, q) is the bf16 A operand of step q (codes 8q..8q+7 of the
+// lane's block of group rg), block scale applied by the conversion.
+struct W4 {
+    static constexpr int kChunkBytes = 4096;
+    struct Chunk {
+        uint4 w[kGroups];
+        uint32_t s;
+    };
+    static __device__ void load(const uint8_t* tiles, const uint8_t* tscales, int ci, Chunk& b) {
+        const int lane = threadIdx.x % kWave;
+        const uint8_t* t = tiles + (int64_t)ci * kChunkBytes + lane * 16;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++) b.w[rg] = load_stream16(t + rg * 1024);
+        b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
+    }
+    static __device__ bf16x8_t a(const Chunk& b, int rg, int q) {
+        return decode8(word_of(b.w[rg], q), e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
+    }
+};
+struct W8 {
+    static constexpr int kChunkBytes = 8192;
+    struct Chunk {
+        uint4 w[kGroups][2];
+        uint32_t s;
+    };
+    static __device__ void load(const uint8_t* tiles, const uint8_t* tscales, int ci, Chunk& b) {
+        const int lane = threadIdx.x % kWave;
+        const uint8_t* t = tiles + (int64_t)ci * kChunkBytes + lane * 16;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) b.w[rg][h] = load_stream16(t + rg * 2048 + h * 1024);
+        b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
+    }
+    static __device__ bf16x8_t a(const Chunk& b, int rg, int q) {
+        const uint4& v = b.w[rg][q >> 1];
+        return decode8_e4m3((q & 1) ? v.z : v.x, (q & 1) ? v.w : v.y,
+                            e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
+    }
+};
+
+// ---- activation formats of the B operand (one token row, 128-k chunk):
+// lane (c, g) takes block g of the chunk; b(x, q) is the bf16 B operand of
+// step q (elements 8q..8q+7 of the block).  XB: bf16 rows.  X8: MXFP8 rows
+// (E4M3 codes and one E8M0 scale per block, the prefill format), decoded
+// to bf16 exactly.  row(a, token) is a token's x row, hrow(a, r) row r of h.
+struct XB {
+    static constexpr bool kMx8 = false;
+    struct Row {
+        const uint16_t* p;
+    };
+    struct Chunk {
+        uint4 x[4];
+    };
+    static __device__ Row row(const GemmArgs& a, int t) { return Row{a.x + (int64_t)t * a.H}; }
+    static __device__ Row hrow(const GemmArgs& a, int r) { return Row{a.h + (int64_t)r * a.I}; }
+    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
+        const uint4* src = reinterpret_cast<const uint4*>(r.p + (int64_t)(4 * chunk + g) * 32);
+#pragma unroll
+        for (int q = 0; q < 4; q++) c.x[q] = src[q];
+    }
+    static __device__ bf16x8_t b(const Chunk& c, int q) { return __builtin_bit_cast(bf16x8_t, c.x[q]); }
+};
+struct X8 {
+    static constexpr bool kMx8 = true;
+    struct Row {
+        const uint8_t* c;
+        const uint8_t* s;
+    };
+    struct Chunk {
+        uint4 x[2];
+        uint32_t s;
+    };
+    static __device__ Row row(const GemmArgs& a, int t) {
+        return Row{a.xq + (int64_t)t * a.H, a.xs + (int64_t)t * (a.H / 32)};
+    }
+    static __device__ Row hrow(const GemmArgs& a, int r) {
+        return Row{a.hq + (int64_t)r * a.I, a.hs + (int64_t)r * (a.I / 32)};
+    }
+    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
+        const uint4* src = reinterpret_cast<const uint4*>(r.c + (int64_t)(4 * chunk + g) * 32);
+        c.x[0] = src[0];
+        c.x[1] = src[1];
+        c.s = r.s[4 * chunk + g];
+    }
+    static __device__ bf16x8_t b(const Chunk& c, int q) {
+        const uint4& v = c.x[q >> 1];
+        return decode8_e4m3((q & 1) ? v.z : v.x, (q & 1) ? v.w : v.y, e8m0_as_scale(c.s));
+    }
+};
+
+// chunks per prefetch step: MXFP4 single-tile items kChunksPerStep, wider
+// ones one (their x operands alone fill 16 VGPRs per tile and chunk);
+// MXFP8 weights one (a chunk is already twice the bytes)
 #ifndef MOE_MFMA_WIDE_CPS
 #define MOE_MFMA_WIDE_CPS 1
 #endif
 
-template <int NT>
+template <int NT, typename W>
 struct Cps {
-    static constexpr int value = NT == 1 ? kChunksPerStep : NT == 2 ? MOE_MFMA_WIDE_CPS : 1;
+    static constexpr int value =
+        W::kChunkBytes != 4096 ? 1 : NT == 1 ? kChunksPerStep : NT == 2 ? MOE_MFMA_WIDE_CPS : 1;
 };
 
-template <int CPS>
+template <typename W, int CPS>
 struct WStep {
-    uint4 w[CPS][kGroups];
-    uint32_t s[CPS];
+    typename W::Chunk c[CPS];
 };
 
-template <int NT>
+template <typename X, int NT, int CPS>
 struct XStep {
-    uint4 x[Cps<NT>::value][NT][4];
+    typename X::Chunk x[CPS][NT];
 };
 
 // One wave: chunks [c_begin, c_end) of one quad against NT column tiles of
 // 16 tokens.  tiles/tscales point at the quad's chunk 0; rows_of(xrow)
-// fills this lane's token row (bf16) of every tile -- a real row for every
-// lane: lanes past the item's tokens repeat one of its rows, and their
-// output columns are never stored -- and is called only after the first
-// weight loads are in flight (it usually waits on an index load).  Each
-// weight word is decoded once and feeds the NT tiles' MFMAs.
+// fills this lane's token row of every tile -- a real row for every lane:
+// lanes past the item's tokens repeat one of its rows, and their output
+// columns are never stored -- and is called only after the first weight
+// loads are in flight (it usually waits on an index load).  Each weight
+// word is decoded once and feeds the NT tiles' MFMAs.
 //
 // Per step (CPS chunks): the x loads of this step, then the weight loads of
 // the next step, then the MFMAs.  Loads complete in issue order, so the
@@ -88,40 +186,29 @@ struct XStep {
 // full drain.  So every load is unconditional -- a partial last step loads
 // its last chunk again (in the same step: a cache hit) and skips that
 // chunk's MFMAs -- and the last step, which prefetches nothing, is peeled.
-template <int NT, typename RowsFn>
+template <int NT, typename W, typename X, typename RowsFn>
 __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowsFn rows_of,
                                  int c_begin, int c_end, f32x4_t (&acc)[kGroups][NT]) {
-    constexpr int CPS = Cps<NT>::value;
+    constexpr int CPS = Cps<NT, W>::value;
     const int lane = threadIdx.x % kWave, g = lane / 16;
-    const uint16_t* xrow[NT];
+    typename X::Row xrow[NT];
 #pragma unroll
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (c_begin >= c_end) return;
     auto chunk_of = [&](int c0, int i) { return min(c0 + i, c_end - 1); };
-    auto load_w = [&](int c0, WStep<CPS>& b) {
+    auto load_w = [&](int c0, WStep<W, CPS>& b) {
 #pragma unroll
-        for (int i = 0; i < CPS; i++) {
-            const int ci = chunk_of(c0, i);
-            const uint8_t* t = tiles + (int64_t)ci * 4096 + lane * 16;
-#pragma unroll
-            for (int rg = 0; rg < kGroups; rg++) b.w[i][rg] = load_stream16(t + rg * 1024);
-            b.s[i] = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
-        }
+        for (int i = 0; i < CPS; i++) W::load(tiles, tscales, chunk_of(c0, i), b.c[i]);
     };
-    auto load_x = [&](int c0, XStep<NT>& xb) {
+    auto load_x = [&](int c0, XStep<X, NT, CPS>& xb) {
 #pragma unroll
         for (int i = 0; i < CPS; i++)
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const uint4* src = reinterpret_cast<const uint4*>(
-                    xrow[t] + (int64_t)(4 * chunk_of(c0, i) + g) * 32);
-#pragma unroll
-                for (int q = 0; q < 4; q++) xb.x[i][t][q] = src[q];
-            }
+            for (int t = 0; t < NT; t++) X::load(xrow[t], chunk_of(c0, i), g, xb.x[i][t]);
     };
-    auto compute = [&](int c0, const WStep<CPS>& b, const XStep<NT>& xb) {
+    auto compute = [&](int c0, const WStep<W, CPS>& b, const XStep<X, NT, CPS>& xb) {
 #pragma unroll
         for (int i = 0; i < CPS; i++) {
             if (c0 + i >= c_end) break;  // the repeated chunk of a partial step
@@ -129,19 +216,17 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
             for (int q = 0; q < 4; q++) {
 #pragma unroll
                 for (int rg = 0; rg < kGroups; rg++) {
-                    const float sc = e8m0_as_scale((b.s[i] >> (8 * rg)) & 0xffu);
-                    const bf16x8_t A = decode8(word_of(b.w[i][rg], q), sc);
+                    const bf16x8_t A = W::a(b.c[i], rg, q);
 #pragma unroll
-                    for (int t = 0; t < NT; t++) {
-                        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, xb.x[i][t][q]);
-                        acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[rg][t], 0, 0, 0);
-                    }
+                    for (int t = 0; t < NT; t++)
+                        acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, X::b(xb.x[i][t], q),
+                                                                             acc[rg][t], 0, 0, 0);
                 }
             }
         }
     };
-    WStep<CPS> wa, wb;
-    XStep<NT> xa;
+    WStep<W, CPS> wa, wb;
+    XStep<X, NT, CPS> xa;
     int c = c_begin;
     int left = (c_end - c_begin + CPS - 1) / CPS;  // steps
     load_w(c, wa);
@@ -208,31 +293,31 @@ constexpr int kRedGateUp = (kWaves - 1) * kGroups * kWave;
 constexpr int kRedDown = 2 * kGroups * kWave;
 
 // gate_up body for items of NT column tiles, token rows from `rows`
-// (SortedRows or SlotRows)
-template <int NT, typename Rows>
-__device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, const Rows& rows,
-                                    f32x4_t* red) {
+// (SortedRows, SlotRows, ListRows or TokenRows); gu/gus: the expert's
+// gate_up tiles (format W), x and h in format X.
+template <int NT, typename W, typename X, typename Rows>
+__device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* gu,
+                                    const uint8_t* gus, const Rows& rows, f32x4_t* red) {
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int m = rows.m;
-    const int K = a.H, chunks = K / 128, quads = a.I / 32;
-    const int64_t quad_id = (int64_t)e * quads + quad;
+    const int chunks = a.H / 128;
     int cb, ce;
     wave_chunk_range(chunks, cb, ce);
     f32x4_t acc[kGroups][NT];
-    mfma_quad<NT>(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256,
-                  [&](const uint16_t* (&xrow)[NT]) {
+    mfma_quad<NT, W, X>(gu + (int64_t)quad * chunks * W::kChunkBytes,
+                        gus + (int64_t)quad * chunks * 256,
+                        [&](typename X::Row (&xrow)[NT]) {
 #pragma unroll
-                      for (int t = 0; t < NT; t++) {
-                          const int j = 16 * t + c;
-                          xrow[t] = a.x + (int64_t)(rows.slot(a, min(j, m - 1)) / a.k) * K;
-                      }
-                  },
-                  cb, ce, acc);
+                            for (int t = 0; t < NT; t++)
+                                xrow[t] = X::row(a, rows.token(a, min(16 * t + c, m - 1)));
+                        },
+                        cb, ce, acc);
     reduce_waves<NT>(acc, red);
-    if (threadIdx.x < kWave) {
+    if (threadIdx.x >= kWave) return;
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const int j = 16 * t + c;
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if constexpr (!X::kMx8) {
             if (j >= m) continue;
             uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
 #pragma unroll
@@ -243,6 +328,40 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, int e, const Ro
                 o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
                 o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
                 store_h4(hrow + 16 * rg, o);
+            }
+        } else {
+            // h of this quad and token = one MX block of 32, held by lanes
+            // (c, 0..3): they agree on its scale through two cross-lane
+            // maxima (every lane takes part), then write their codes
+            float hv[8];
+            uint32_t amax = 0;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float v = silu_mul(acc[h2][t][i], acc[h2 + 2][t][i]);
+                    hv[4 * h2 + i] = v;
+                    const uint32_t mb = __float_as_uint(v) & 0x7fffffffu;
+                    amax = mb > amax ? mb : amax;
+                }
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+            uint32_t code[2] = {0, 0};
+            uint32_t scale = 255;
+            if (amax < 0x7f800000u) {
+                const int se = mxfp8_scale_exp(amax);
+                scale = (uint32_t)(se + 127);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) code[h2] |= e4m3_code(hv[4 * h2 + i], se) << (8 * i);
+            }
+            if (j < m) {
+                const int r = rows.row(j);
+                uint8_t* hrow = a.hq + (int64_t)r * a.I + 32 * quad + 4 * g;
+                *reinterpret_cast<uint32_t*>(hrow) = code[0];       // h 32q + 4g + i
+                *reinterpret_cast<uint32_t*>(hrow + 16) = code[1];  // h 32q + 16 + 4g + i
+                if (g == 0) a.hs[(int64_t)r * (a.I / 32) + quad] = (uint8_t)scale;
             }
         }
     }
@@ -261,34 +380,34 @@ mfma_gate_up_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    gate_up_item<1>(a, quad, e, SortedRows{row0, m}, red);
+    gate_up_item<1, W4, XB>(a, quad, a.wgu + (int64_t)e * (a.I / 32) * (a.H / 128) * 4096,
+                            a.sgu + (int64_t)e * (a.I / 32) * (a.H / 128) * 256, SortedRows{row0, m}, red);
 }
 
 // down body for items of NT column tiles (see mfma_down_kernel), token rows
-// from `rows`; COMBINE: see store_down_tile
-template <int NT, bool COMBINE, typename Rows>
-__device__ inline void down_item(const GemmArgs& a, int pair, int e, const Rows& rows,
-                                 f32x4_t* red) {
+// from `rows`; dn/dns: the expert's down tiles (format W), h in format X;
+// COMBINE: see store_down_tile
+template <int NT, bool COMBINE, typename W, typename X, typename Rows>
+__device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
+                                 const uint8_t* dns, const Rows& rows, f32x4_t* red) {
     const int m = rows.m;
     const int quads = a.H / 64;
     const int w = threadIdx.x / kWave, half = w & 1;
     const int quad = pair * 2 + (w >> 1);
     const int lane = threadIdx.x % kWave, c = lane % 16;
-    const int K = a.I, chunks = K / 128;
+    const int chunks = a.I / 128;
     const bool live = quad < quads;
     f32x4_t acc[kGroups][NT];
     if (live) {
-        const int64_t quad_id = (int64_t)e * quads + quad;
         const int hc = (chunks + 1) / 2;
-        mfma_quad<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256,
-                      [&](const uint16_t* (&xrow)[NT]) {
+        mfma_quad<NT, W, X>(dn + (int64_t)quad * chunks * W::kChunkBytes,
+                            dns + (int64_t)quad * chunks * 256,
+                            [&](typename X::Row (&xrow)[NT]) {
 #pragma unroll
-                          for (int t = 0; t < NT; t++) {
-                              const int j = 16 * t + c;
-                              xrow[t] = a.h + (int64_t)rows.row(min(j, m - 1)) * K;
-                          }
-                      },
-                      half ? hc : 0, half ? chunks : hc, acc);
+                                for (int t = 0; t < NT; t++)
+                                    xrow[t] = X::hrow(a, rows.row(min(16 * t + c, m - 1)));
+                            },
+                            half ? hc : 0, half ? chunks : hc, acc);
         if (half) {
 #pragma unroll
             for (int rg = 0; rg < kGroups; rg++)
@@ -319,7 +438,9 @@ mfma_down_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    down_item<1, false>(a, pair, e, SortedRows{row0, m}, red);
+    down_item<1, false, W4, XB>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
+                                a.sdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 256,
+                                SortedRows{row0, m}, red);
 }
 
 // ---- self-routed layer (up to kSelfMaxTok tokens): no routing pass.  The
@@ -381,7 +502,9 @@ self_gate_up_kernel(GemmArgs a) {
     const int e = (blockIdx.x - 1) / quads, quad = (blockIdx.x - 1) % quads;
     const auto rows = SelfRows<LISTS>::get(a, e);
     if (rows.m == 0) return;  // no token chose e
-    gate_up_item<1>(a, quad, e, rows, reinterpret_cast<f32x4_t*>(smem));
+    gate_up_item<1, W4, XB>(a, quad, a.wgu + (int64_t)e * quads * (a.H / 128) * 4096,
+                            a.sgu + (int64_t)e * quads * (a.H / 128) * 256, rows,
+                            reinterpret_cast<f32x4_t*>(smem));
 }
 
 // blockIdx.x = e * ceil(H/128) + pair: the down quads 2*pair, 2*pair+1 of
@@ -395,7 +518,8 @@ self_down_kernel(GemmArgs a) {
     const int e = blockIdx.x / pairs, pair = blockIdx.x % pairs;
     const auto rows = SelfRows<LISTS>::get(a, e);
     if (rows.m == 0) return;
-    down_item<1, false>(a, pair, e, rows, red);
+    down_item<1, false, W4, XB>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
+                                a.sdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 256, rows, red);
 }
 
 #ifndef MOE_FUSED_WAVES_PER_EU
@@ -438,8 +562,10 @@ mfma_fused_kernel(GemmArgs a) {
         if (u < n_gu) {
             const int item = u / gu_units;
             const int4 it = a.items[item];
-            gate_up_item<1>(a, u % gu_units, uniform(it.x),
-                            SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
+            const int64_t e = uniform(it.x);
+            gate_up_item<1, W4, XB>(a, u % gu_units, a.wgu + e * gu_units * (a.H / 128) * 4096,
+                                    a.sgu + e * gu_units * (a.H / 128) * 256,
+                                    SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
             if (threadIdx.x < kWave) {  // wave 0 stored the h rows
                 __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): they are complete
                 if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
@@ -449,13 +575,73 @@ mfma_fused_kernel(GemmArgs a) {
             const int4 it = a.items[item];
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
-            down_item<1, true>(a, v % dn_units, uniform(it.x),
-                               SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
+            const int64_t e = uniform(it.x);
+            down_item<1, true, W4, XB>(a, v % dn_units, a.wdn + e * (a.H / 64) * (a.I / 128) * 4096,
+                                       a.sdn + e * (a.H / 64) * (a.I / 128) * 256,
+                                       SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
         }
     }
 }
 
+// ---- the shared expert: MXFP8 weights, every token.  The pages keep all
+// but the MoE experts at 8 bits (bjdmk.com.cn news page, co-design
+// section; yifor-blog digest, selective FP4 quantisation); a shared expert
+// beside the routed ones is such a part.  Same quads, split-K waves and
+// epilogues as the routed items, over 16-token tiles of all T tokens (h and
+// y rows sh_row0 + t).  Unit u of `units` row units (gate_up quads or down
+// quad pairs) and tile of `tiles`: blockIdx = x + 8 * (tile + tiles * g)
+// with unit 8g + x, so the tiles of one unit run on one XCD (blockIdx mod 8)
+// one after another, and its weights come from HBM about once.
+__device__ inline bool shared_unit(int units, int tiles, int& unit, int& tile) {
+    const int x = blockIdx.x % 8, r = blockIdx.x / 8;
+    tile = r % tiles;
+    unit = 8 * (r / tiles) + x;
+    return unit < units;
+}
+
+template <typename X>
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+shared_gate_up_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[kRedGateUp];
+    int quad, tile;
+    if (!shared_unit(a.I / 32, (a.T + 15) / 16, quad, tile)) return;
+    const int t0 = 16 * tile;
+    gate_up_item<1, W8, X>(a, quad, a.sh_wgu, a.sh_sgu, TokenRows{t0, min(16, a.T - t0), a.sh_row0},
+                           red);
+}
+
+template <typename X>
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+shared_down_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[kRedDown];
+    int pair, tile;
+    if (!shared_unit((a.H / 64 + 1) / 2, (a.T + 15) / 16, pair, tile)) return;
+    const int t0 = 16 * tile;
+    down_item<1, false, W8, X>(a, pair, a.sh_wdn, a.sh_sdn, TokenRows{t0, min(16, a.T - t0), a.sh_row0},
+                               red);
+}
+
 }  // namespace
+
+hipError_t launch_shared_gate_up(const GemmArgs& a, bool mx8, hipStream_t stream) {
+    const int grid = 8 * ((a.T + 15) / 16) * ((a.I / 32 + 7) / 8);
+    if (mx8)
+        shared_gate_up_kernel<X8><<<grid, kMfmaThreads, 0, stream>>>(a);
+    else
+        shared_gate_up_kernel<XB><<<grid, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_down(const GemmArgs& a, bool mx8, hipStream_t stream) {
+    const int grid = 8 * ((a.T + 15) / 16) * (((a.H / 64 + 1) / 2 + 7) / 8);
+    if (mx8)
+        shared_down_kernel<X8><<<grid, kMfmaThreads, 0, stream>>>(a);
+    else
+        shared_down_kernel<XB><<<grid, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int quads = a.I / 32;

@@ -4,6 +4,8 @@
 // Launch sequence of a forward on `stream` (no host synchronisation):
 //   route (top-k + stable sort by expert + active-expert lists)
 //   -> gate_up GEMM with the SiLU * up epilogue -> down GEMM -> combine
+// (with a shared expert, its gate_up and down kernels run ahead of the
+// routed ones in the same stages, and the combine adds its rows)
 // (on the matrix-core paths the combine is its own kernel, or the
 // last-finisher step of the single-launch layer; the VALU path combines by
 // last finisher inside its down kernel).  Layers of at most 16 tokens on
@@ -71,12 +73,13 @@ size_t layout(Workspace* ws, char* base) {
     ws->logits = (float*)take(TE * 4);
     ws->router_partial = (float*)take((size_t)moe::kRouterMaxSplit * split_te * 4);
     ws->router_cnt = (int32_t*)take((size_t)2 * moe::kRouterWaves * 4);
-    ws->h = (uint16_t*)take(S * ws->I * 2);
-    ws->y = (float*)take(S * ws->H * 4);
+    const size_t R = S + (size_t)ws->max_tokens;  // routed rows, then the shared expert's
+    ws->h = (uint16_t*)take(R * ws->I * 2);
+    ws->y = (float*)take(R * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
     ws->x_scales = (uint8_t*)take((size_t)ws->max_tokens * (ws->H / 32));
-    ws->h_codes = (uint8_t*)take(S * ws->I);
-    ws->h_scales = (uint8_t*)take(S * (ws->I / 32));
+    ws->h_codes = (uint8_t*)take(R * ws->I);
+    ws->h_scales = (uint8_t*)take(R * (ws->I / 32));
     return off;
 }
 
@@ -205,6 +208,15 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         return MOE_E_NULL;
     if (!scales->gate_up || !scales->down) return MOE_E_NULL;
     if (top_k < 1) return MOE_E_TOPK;
+    // the shared expert comes whole or not at all
+    const bool shared = o.shared_gate_up || o.shared_gate_up_scales || o.shared_down ||
+                        o.shared_down_scales;
+    if (shared && !(o.shared_gate_up && o.shared_gate_up_scales && o.shared_down &&
+                    o.shared_down_scales))
+        return MOE_E_NULL;
+    if (!aligned16(o.shared_gate_up) || !aligned16(o.shared_gate_up_scales) ||
+        !aligned16(o.shared_down) || !aligned16(o.shared_down_scales))
+        return MOE_E_ALIGN;
     if (!aligned16(x) || !aligned16(router_logits) || !aligned16(o.router_weight) ||
         !aligned16(W_gate_up) ||
         !aligned16(W_down) || !aligned16(scales->gate_up) || !aligned16(scales->down) ||
@@ -301,11 +313,28 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.gu_done = ws->gu_done;
     a.route_ids = ws->ids;
     a.route_wts = ws->wts;
+    a.sh_wgu = shared ? o.shared_gate_up : nullptr;
+    a.sh_sgu = o.shared_gate_up_scales;
+    a.sh_wdn = o.shared_down;
+    a.sh_sdn = o.shared_down_scales;
+    a.sh_row0 = S;
+    // The shared expert needs no routing: its gate_up runs ahead of the
+    // routed gate_up, its down ahead of the routed down (which, on the VALU
+    // path and in the single-launch layer, also combines), both in the
+    // stages of the routed ones.
+    auto shared_gate_up = [&]() -> hipError_t {
+        return shared ? moe::launch_shared_gate_up(a, mx8, st) : hipSuccess;
+    };
+    auto shared_down = [&]() -> hipError_t {
+        return shared ? moe::launch_shared_down(a, mx8, st) : hipSuccess;
+    };
+    if ((err = shared_gate_up()) != hipSuccess) return hip_fail(err, "shared gate_up");
     if (self) {
         a.pos = nullptr;  // h and y rows are the slots
         err = moe::launch_self_gate_up(a, lists, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
         err = moe::launch_self_down(a, lists, st);
         if (err != hipSuccess) return hip_fail(err, "down");
         err = moe::launch_combine(a, st);
@@ -315,6 +344,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         err = moe::launch_mx8_gate_up(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
         err = moe::launch_mx8_down(a, max_items, st);
         if (err != hipSuccess) return hip_fail(err, "down");
         err = moe::launch_combine(a, st);
@@ -323,6 +353,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         err = moe::launch_gemv_gate_up(a, max_active, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
         if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
         err = moe::launch_gemv_down(a, max_active, st);
         if (err != hipSuccess) return hip_fail(err, "down");
     } else {
@@ -331,6 +362,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         const int max_items = max_active + S / item_tok + 1;
         if (o.launch == MOE_LAUNCH_FUSED) {
             // one kernel: event [2] marks its end as well as [3]
+            if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
             err = wide ? moe::launch_wide_fused(a, max_items, st)
                        : moe::launch_mfma_fused(a, max_items, st);
             if (err != hipSuccess) return hip_fail(err, "fused expert layer");
@@ -340,6 +372,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
                        : moe::launch_mfma_gate_up(a, max_items, st);
             if (err != hipSuccess) return hip_fail(err, "gate_up");
             if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+            if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
             err = wide ? moe::launch_wide_down(a, max_items, st) : moe::launch_mfma_down(a, max_items, st);
             if (err != hipSuccess) return hip_fail(err, "down");
             err = moe::launch_combine(a, st);
@@ -375,6 +408,17 @@ int moe_mxfp4_forward(const void* x, const float* router_logits, int64_t num_tok
                       const moe_mxfp4_scales* scales, void* out, void* stream) {
     return moe_mxfp4_forward_ex(x, router_logits, num_tokens, top_k, W_gate_up, W_down, scales,
                                 out, stream, nullptr);
+}
+
+int moe_mxfp8_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+    if (rows < 0 || cols < 0 || cols % 32) return MOE_E_SHAPE;
+    if (rows == 0 || cols == 0) return MOE_OK;
+    if (!w || !codes || !scales) return MOE_E_NULL;
+    if (!aligned16(w) || !aligned16(codes)) return MOE_E_ALIGN;
+    hipError_t err = moe::launch_quantize_mxfp8(w, rows, cols, codes, scales, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "quantize");
+    return MOE_OK;
 }
 
 int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* packed,

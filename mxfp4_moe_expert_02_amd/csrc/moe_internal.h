@@ -108,12 +108,14 @@ struct Workspace {
     int32_t* router_cnt = nullptr;    // [2 * kRouterWaves] finished splits per tile (split-K only)
     int max_items = 0;             // entries of mfma_items / gu_done
     int col_tiles = 0;             // H / kColTile
-    uint16_t* h = nullptr;      // [Tmax*kmax, I] bf16, rows in sorted order
-    float* y = nullptr;         // [Tmax*kmax, H] fp32, rows in sorted order
+    // h and y: Tmax*kmax rows of the routed assignments (sorted order, or
+    // slot order in a self-routed layer), then Tmax rows of the shared expert
+    uint16_t* h = nullptr;      // [Tmax*(kmax+1), I] bf16
+    float* y = nullptr;         // [Tmax*(kmax+1), H] fp32
     uint8_t* x_codes = nullptr;   // [Tmax, H] E4M3 codes of x (MXFP8 path)
     uint8_t* x_scales = nullptr;  // [Tmax, H/32] E8M0
-    uint8_t* h_codes = nullptr;   // [Tmax*kmax, I] E4M3 codes of h, rows in sorted order
-    uint8_t* h_scales = nullptr;  // [Tmax*kmax, I/32] E8M0
+    uint8_t* h_codes = nullptr;   // [Tmax*(kmax+1), I] E4M3 codes of h, rows as h
+    uint8_t* h_scales = nullptr;  // [Tmax*(kmax+1), I/32] E8M0
 };
 
 // Arguments common to the expert GEMM kernels.
@@ -154,6 +156,13 @@ struct GemmArgs {
     int32_t* route_ids;         // [T*k] written by the weight pass (expert per slot)
     float* route_wts;           // [T*k] written by the weight pass (= wts)
     int32_t* slot_lists;        // [E * kSlotListInts] per-expert slot lists
+    // optional shared expert: MXFP8 weights in the tile layout (null: none),
+    // applied to every token; its h and y rows are sh_row0 + t (sh_row0 = T*k)
+    const uint8_t* sh_wgu;      // [2I, H] as gate/up quads
+    const uint8_t* sh_sgu;
+    const uint8_t* sh_wdn;      // [H, I]
+    const uint8_t* sh_sdn;
+    int sh_row0;
 };
 
 // ---------------------------------------------------------------- launchers
@@ -211,5 +220,13 @@ hipError_t launch_mx8_gate_up(const GemmArgs& a, int max_items, hipStream_t stre
 hipError_t launch_mx8_down(const GemmArgs& a, int max_items, hipStream_t stream);
 hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                                  uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_mxfp8(const float* w, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
+// The shared expert (MXFP8 weights) over all T tokens in tiles of 16, on
+// the bf16 matrix cores; mx8: x and h in MXFP8 (the prefill format) instead
+// of bf16.  gate_up writes h rows sh_row0 + t, down writes y rows
+// sh_row0 + t; the combine adds them with weight 1.
+hipError_t launch_shared_gate_up(const GemmArgs& a, bool mx8, hipStream_t stream);
+hipError_t launch_shared_down(const GemmArgs& a, bool mx8, hipStream_t stream);
 
 }  // namespace moe

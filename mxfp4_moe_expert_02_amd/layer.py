@@ -3,7 +3,9 @@
 Weights are drawn as float32 by ``workloads`` (host, thread pool), copied to
 the GPU one expert at a time and encoded to MXFP4 there by the library's own
 ``moe_mxfp4_quantize``.  The result holds exactly the tensors the C ABI
-takes, laid out as include/moe_mxfp4.h describes.
+takes, laid out as include/moe_mxfp4.h describes.  ``build_shared`` does
+the same for the optional MXFP8 shared expert (``moe_mxfp8_quantize``,
+``moe_mxfp8_prepack``).
 """
 from __future__ import annotations
 
@@ -11,7 +13,8 @@ import dataclasses
 
 import numpy as np
 
-from workloads import Config, iter_weights_fp32, make_logits, make_x_bf16
+from workloads import (Config, iter_weights_fp32, make_logits, make_shared_weight_fp32,
+                       make_x_bf16)
 
 from . import _lib
 
@@ -92,3 +95,48 @@ def build_layer(cfg: Config, device: str = "cuda", workers: int | None = None,
         _lib.moe_mxfp4_prepack(wdn, sdn, layer.wdn_t, layer.sdn_t, gate_up_pairs=False)
     torch.cuda.synchronize(dev)
     return layer
+
+
+@dataclasses.dataclass
+class SharedExpert:
+    """The MXFP8 shared expert: row-major codes and scales, and the tile
+    layout the layer reads."""
+    gu: "torch.Tensor"       # [2I, H] uint8 E4M3 codes
+    gus: "torch.Tensor"      # [2I, H/32] uint8 E8M0
+    dn: "torch.Tensor"       # [H, I]
+    dns: "torch.Tensor"      # [H, I/32]
+    gu_t: "torch.Tensor"
+    gus_t: "torch.Tensor"
+    dn_t: "torch.Tensor"
+    dns_t: "torch.Tensor"
+
+    @property
+    def tiles(self):
+        """The four tensors of the ``shared`` argument of forward_ex."""
+        return (self.gu_t, self.gus_t, self.dn_t, self.dns_t)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.gu, self.gus, self.dn, self.dns))
+
+
+def build_shared(cfg: Config, device: str = "cuda", fp32: dict | None = None) -> SharedExpert:
+    """The shared expert of ``cfg`` encoded on the device.  ``fp32``: optional
+    {"gate_up": [2I, H], "down": [H, I]} float32 matrices to encode instead
+    of the seeded draws."""
+    import torch
+    dev = torch.device(device)
+    mats = []
+    for which in ("gate_up", "down"):
+        w = make_shared_weight_fp32(cfg, which) if fp32 is None else fp32[which]
+        rows, cols = w.shape
+        wd = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(dev)
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        _lib.moe_mxfp8_quantize(wd, codes, scales)
+        tiles, tscales = torch.empty_like(codes), torch.empty_like(scales)
+        _lib.moe_mxfp8_prepack(codes.view(1, rows, cols), scales.view(1, rows, cols // 32),
+                               tiles, tscales, gate_up_pairs=which == "gate_up")
+        mats.append((codes, scales, tiles, tscales))
+    (gu, gus, gu_t, gus_t), (dn, dns, dn_t, dns_t) = mats
+    torch.cuda.synchronize(dev)
+    return SharedExpert(gu, gus, dn, dns, gu_t, gus_t, dn_t, dns_t)

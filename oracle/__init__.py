@@ -14,6 +14,9 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
                                   brute.py on tiny shapes)
   router_logits ............... pinned (brute-force loop, unit-vector
                                   closed form, exact power-of-two scaling)
+  forward(shared=...) ......... pinned (brute.py on tiny shapes, an MXFP8
+                                  copy of an MXFP4 expert gives the same
+                                  result, closed forms, scale identities)
 """
 from __future__ import annotations
 
@@ -65,6 +68,9 @@ def lib():
         L.oracle_forward.restype = i32
         L.oracle_forward.argtypes = [vp, vp, i64, i64, i64, i64, i32,
                                      vp, vp, vp, vp, i32, vp, i64, vp]
+        L.oracle_forward_ex.restype = i32
+        L.oracle_forward_ex.argtypes = [vp, vp, i64, i64, i64, i64, i32,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -153,11 +159,13 @@ def route(logits: np.ndarray, k: int) -> dict:
 
 def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
             experts: Mapping[int, Sequence[np.ndarray]], tokens: Sequence[int] | None = None,
-            act_mxfp8: bool = False) -> np.ndarray:
+            act_mxfp8: bool = False, shared: Sequence[np.ndarray] | None = None) -> np.ndarray:
     """Layer output (fp64) for ``tokens`` (default: all).
 
     ``experts[e] = (gu_packed [2I,H/2], gu_scales [2I,H/32], dn_packed [H,I/2],
     dn_scales [H,I/32])`` for every expert the listed tokens are routed to.
+    ``shared = (gu_codes [2I,H], gu_scales [2I,H/32], dn_codes [H,I],
+    dn_scales [H,I/32])``: the MXFP8 shared expert added with weight 1.
     """
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -172,11 +180,20 @@ def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
             m = np.ascontiguousarray(m, dtype=np.uint8)
             keep.append(m)
             arrays[i][e] = m.ctypes.data
+    sh = [None] * 4
+    if shared is not None:
+        shapes = [(2 * I, H), (2 * I, H // 32), (H, I), (H, I // 32)]
+        for i, m in enumerate(shared):
+            m = np.ascontiguousarray(m, dtype=np.uint8)
+            assert m.shape == shapes[i], (m.shape, shapes[i])
+            keep.append(m)
+            sh[i] = m.ctypes.data
     out = np.zeros((len(toks), H), np.float64)
-    rc = lib().oracle_forward(_p(x_bf16), _p(logits), T, E, H, I, k,
-                              ctypes.addressof(arrays[0]), ctypes.addressof(arrays[1]),
-                              ctypes.addressof(arrays[2]), ctypes.addressof(arrays[3]),
-                              1 if act_mxfp8 else 0, _p(toks), len(toks), _p(out))
+    rc = lib().oracle_forward_ex(_p(x_bf16), _p(logits), T, E, H, I, k,
+                                 ctypes.addressof(arrays[0]), ctypes.addressof(arrays[1]),
+                                 ctypes.addressof(arrays[2]), ctypes.addressof(arrays[3]),
+                                 sh[0], sh[1], sh[2], sh[3],
+                                 1 if act_mxfp8 else 0, _p(toks), len(toks), _p(out))
     if rc == -2:
         raise KeyError("oracle_forward: a routed expert's weights were not given")
     if rc:

@@ -48,6 +48,10 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
 
 
+def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=1)
+
+
 def mxfp4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     vals = e2m1_decode(unpack_nibbles(packed))
     return vals * np.repeat(e8m0_decode(scales), 32, axis=1)
@@ -103,14 +107,28 @@ def route(logits: np.ndarray, k: int):
     return ids, w
 
 
+def _ffn(wgu: np.ndarray, wdn: np.ndarray, xt: np.ndarray, I: int, act_mxfp8: bool) -> np.ndarray:
+    g = wgu[:I] @ xt
+    u = wgu[I:] @ xt
+    h = np.array([gi / (1.0 + math.exp(-gi)) for gi in g]) * u
+    if act_mxfp8:
+        h = mxfp8_encode_values(h[None, :])[0][0]
+    return wdn @ h
+
+
 def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
-            experts: Mapping[int, Sequence[np.ndarray]], act_mxfp8: bool = False) -> np.ndarray:
+            experts: Mapping[int, Sequence[np.ndarray]], act_mxfp8: bool = False,
+            shared: Sequence[np.ndarray] | None = None) -> np.ndarray:
     xf = (x_bf16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     T = xf.shape[0]
     ids, w = route(logits, k)
     dense = {}
     for e, (gp, gs, dp, ds) in experts.items():
         dense[e] = (mxfp4_dequant(gp, gs), mxfp4_dequant(dp, ds))
+    sh = None
+    if shared is not None:
+        sgc, sgs, sdc, sds = shared
+        sh = (mxfp8_dequant(sgc, sgs), mxfp8_dequant(sdc, sds))
     out = np.zeros((T, H))
     for t in range(T):
         xt = xf[t:t + 1]
@@ -118,10 +136,7 @@ def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
             xt, _ = mxfp8_encode_values(xt)
         for j in range(k):
             wgu, wdn = dense[int(ids[t, j])]
-            g = wgu[:I] @ xt[0]
-            u = wgu[I:] @ xt[0]
-            h = np.array([gi / (1.0 + math.exp(-gi)) for gi in g]) * u
-            if act_mxfp8:
-                h = mxfp8_encode_values(h[None, :])[0][0]
-            out[t] += w[t, j] * (wdn @ h)
+            out[t] += w[t, j] * _ffn(wgu, wdn, xt[0], I, act_mxfp8)
+        if sh is not None:
+            out[t] += _ffn(sh[0], sh[1], xt[0], I, act_mxfp8)
     return out

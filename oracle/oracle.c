@@ -22,6 +22,14 @@
  *  - The prefill workload feeds the GEMMs MXFP8 (E4M3 elements, E8M0 block
  *    scales) activations: x is encoded per token along H and the intermediate
  *    h per assignment along I, by the same block rule as the weights.
+ *  - The pages keep the parts of the model other than the MoE experts at FP8
+ *    (bjdmk.com.cn news page, co-design section; yifor-blog digest, on
+ *    selective FP4 quantisation).  The optional shared expert is read that
+ *    way: one SiLU-gated FFN of the routed experts' shape, applied to every
+ *    token with weight 1 and added to the routed sum, whose weights are
+ *    MXFP8 (E4M3 elements, one E8M0 scale per 32 along the reduction
+ *    dimension: the OCP MX block structure of the experts, with 8-bit
+ *    elements).
  *
  * Rounding: the only rounding is the encoding step itself (round to nearest,
  * ties to the even code, saturating at the largest finite element).  All
@@ -264,6 +272,24 @@ static void mxfp4_matvec(const uint8_t* packed, const uint8_t* scales, int64_t N
     }
 }
 
+/* decoded weight W[n][kk] of an MXFP8 matrix with K columns: codes [N, K]
+ * E4M3, scales [N, K/32] E8M0 */
+static double mxfp8_weight(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t n,
+                           int64_t kk) {
+    return oracle_e4m3_value(codes[n * K + kk]) * oracle_e8m0_value(scales[n * (K / 32) + kk / 32]);
+}
+
+/* y[n] = sum_kk W[n][kk] * v[kk] for n in [0, N), W in MXFP8 */
+static void mxfp8_matvec(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                         const double* v, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; kk++) acc += mxfp8_weight(codes, scales, K, n, kk) * v[kk];
+        y[n] = acc;
+    }
+}
+
 /* replace v[0..n) by its MXFP8 (E4M3) encode-then-decode */
 static void mxfp8_roundtrip(double* v, int64_t n) {
     uint8_t codes[32], sc;
@@ -277,20 +303,28 @@ static void mxfp8_roundtrip(double* v, int64_t n) {
 
 /* The layer output for the tokens listed in `tokens` (n_tok of them):
  *   out[i][:] = sum_j w[t][j] * W_down[e_j] ( silu(W_gate[e_j] x_t) * (W_up[e_j] x_t) )
+ *             + Ws_down ( silu(Ws_gate x_t) * (Ws_up x_t) )     (shared expert, if given)
  * with t = tokens[i], (e_j, w[t][j]) from oracle_route over all T tokens.
  * x [T,H] bf16 bits; logits [T,E] fp32.  Expert e's matrices come through
  * the per-expert pointer arrays: gu_packed[e] [2I, H/2], gu_scales[e]
  * [2I, H/32], dn_packed[e] [H, I/2], dn_scales[e] [H, I/32].  Pointers of
  * experts that no listed token uses may be NULL; a NULL that is needed
- * returns OR_EMISSING.  act_mxfp8 != 0 encodes x_t (along H) and h (along I)
- * to MXFP8 before the products that consume them.  out [n_tok, H] fp64. */
-int oracle_forward(const uint16_t* x, const float* logits, int64_t T, int64_t E,
-                   int64_t H, int64_t I, int k,
-                   const uint8_t* const* gu_packed, const uint8_t* const* gu_scales,
-                   const uint8_t* const* dn_packed, const uint8_t* const* dn_scales,
-                   int act_mxfp8, const int32_t* tokens, int64_t n_tok, double* out) {
+ * returns OR_EMISSING.  The shared expert is MXFP8: sh_gu [2I, H] E4M3
+ * codes (rows 0..I-1 gate, I..2I-1 up), sh_gus [2I, H/32], sh_dn [H, I],
+ * sh_dns [H, I/32]; all four NULL = no shared expert.  act_mxfp8 != 0
+ * encodes x_t (along H) and every h (along I) to MXFP8 before the products
+ * that consume them.  out [n_tok, H] fp64. */
+int oracle_forward_ex(const uint16_t* x, const float* logits, int64_t T, int64_t E,
+                      int64_t H, int64_t I, int k,
+                      const uint8_t* const* gu_packed, const uint8_t* const* gu_scales,
+                      const uint8_t* const* dn_packed, const uint8_t* const* dn_scales,
+                      const uint8_t* sh_gu, const uint8_t* sh_gus, const uint8_t* sh_dn,
+                      const uint8_t* sh_dns, int act_mxfp8, const int32_t* tokens,
+                      int64_t n_tok, double* out) {
     if (T < 0 || E <= 0 || H <= 0 || I <= 0 || H % 32 || I % 32 || k < 1 || k > E)
         return OR_EINVAL;
+    const int shared = sh_gu || sh_gus || sh_dn || sh_dns;
+    if (shared && !(sh_gu && sh_gus && sh_dn && sh_dns)) return OR_EMISSING;
     int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
     double* w = (double*)malloc(sizeof(double) * (size_t)(T * k + 1));
     double* xt = (double*)malloc(sizeof(double) * (size_t)H);
@@ -323,8 +357,28 @@ int oracle_forward(const uint16_t* x, const float* logits, int64_t T, int64_t E,
             mxfp4_matvec(dn_packed[e], dn_scales[e], H, I, h, y);
             for (int64_t n = 0; n < H; n++) out[i * H + n] += w[t * k + j] * y[n];
         }
+        if (shared) { /* the same FFN with MXFP8 weights, weight 1 */
+            mxfp8_matvec(sh_gu, sh_gus, 2 * I, H, xt, gu);
+            for (int64_t n = 0; n < I; n++) {
+                double g = gu[n], u = gu[I + n];
+                h[n] = g / (1.0 + exp(-g)) * u;
+            }
+            if (act_mxfp8) mxfp8_roundtrip(h, I);
+            mxfp8_matvec(sh_dn, sh_dns, H, I, h, y);
+            for (int64_t n = 0; n < H; n++) out[i * H + n] += y[n];
+        }
     }
 done:
     free(ids); free(w); free(xt); free(gu); free(h); free(y);
     return rc;
+}
+
+/* oracle_forward_ex without a shared expert */
+int oracle_forward(const uint16_t* x, const float* logits, int64_t T, int64_t E,
+                   int64_t H, int64_t I, int k,
+                   const uint8_t* const* gu_packed, const uint8_t* const* gu_scales,
+                   const uint8_t* const* dn_packed, const uint8_t* const* dn_scales,
+                   int act_mxfp8, const int32_t* tokens, int64_t n_tok, double* out) {
+    return oracle_forward_ex(x, logits, T, E, H, I, k, gu_packed, gu_scales, dn_packed,
+                             dn_scales, NULL, NULL, NULL, NULL, act_mxfp8, tokens, n_tok, out);
 }

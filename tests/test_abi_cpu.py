@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward", "moe_mxfp4_forward_ex",
         "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_mxfp4_prepack",
-        "moe_probe_stream_read",
+        "moe_mxfp8_quantize", "moe_mxfp8_prepack", "moe_probe_stream_read",
         "moe_probe_sink_words", "moe_probe_copy"])
 
 
@@ -120,6 +120,16 @@ def test_forward_validation_without_gpu(L):
         assert _fwd(L, opt=req) == L.MOE_E_NOT_INIT      # a valid request
     assert L.lib().moe_mxfp4_forward(0x1000, 0x2000, 9, 2, 0x3000, 0x4000, None, 0x7000,
                                      None) == L.MOE_E_NULL
+    # the shared expert comes whole or not at all, 16-byte aligned
+    part = L.moe_mxfp4_options(0, 0)
+    part.shared_gate_up, part.shared_gate_up_scales, part.shared_down = 0x8000, 0x9000, 0xA000
+    assert _fwd(L, opt=part) == L.MOE_E_NULL
+    whole = L.moe_mxfp4_options(0, 0)
+    whole.shared_gate_up, whole.shared_gate_up_scales = 0x8000, 0x9000
+    whole.shared_down, whole.shared_down_scales = 0xA000, 0xB000
+    assert _fwd(L, opt=whole) == L.MOE_E_NOT_INIT         # a valid request
+    whole.shared_down_scales = 0xB004
+    assert _fwd(L, opt=whole) == L.MOE_E_ALIGN
 
 
 def test_quantize_validation(L):
@@ -131,8 +141,17 @@ def test_quantize_validation(L):
     assert q(0x1000, 0, 64, 0x2000, 0x3000, None) == L.MOE_OK
 
 
-def test_prepack_validation(L):
-    p = L.lib().moe_mxfp4_prepack
+def test_mxfp8_quantize_validation(L):
+    q = L.lib().moe_mxfp8_quantize
+    assert q(0x1000, 4, 48, 0x2000, 0x3000, None) == L.MOE_E_SHAPE
+    assert q(0x1000, 4, 64, 0, 0x3000, None) == L.MOE_E_NULL
+    assert q(0x1000, 4, 64, 0x2008, 0x3000, None) == L.MOE_E_ALIGN
+    assert q(0x1000, 0, 64, 0x2000, 0x3000, None) == L.MOE_OK
+
+
+@pytest.mark.parametrize("fn", ["moe_mxfp4_prepack", "moe_mxfp8_prepack"])
+def test_prepack_validation(L, fn):
+    p = getattr(L.lib(), fn)
     assert p(0x1000, 0x2000, 2, 96, 256, 0, 0x3000, 0x4000, None) == L.MOE_E_SHAPE   # rows % 64
     assert p(0x1000, 0x2000, 2, 128, 192, 0, 0x3000, 0x4000, None) == L.MOE_E_SHAPE  # cols % 128
     assert p(0, 0x2000, 2, 128, 256, 0, 0x3000, 0x4000, None) == L.MOE_E_NULL

@@ -7,8 +7,8 @@ method code.
 """
 from .synth import (CONFIGS, Config, get_config, make_x_bf16, make_logits,
                     make_router_weight_bf16, make_weight_fp32, iter_weights_fp32,
-                    bf16_bits_to_f32)
+                    bf16_bits_to_f32, make_shared_weight_fp32)
 
 __all__ = ["CONFIGS", "Config", "get_config", "make_x_bf16", "make_logits",
            "make_router_weight_bf16", "make_weight_fp32", "iter_weights_fp32",
-           "bf16_bits_to_f32"]
+           "bf16_bits_to_f32", "make_shared_weight_fp32"]

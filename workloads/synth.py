@@ -18,6 +18,8 @@ Recipe (all draws from numpy's PCG64 ``default_rng`` seeded by a
   (expert, matrix).  gate_up is [2I, H] (rows 0..I-1 gate, I..2I-1 up),
   down is [H, I].  Quantisation to MXFP4 is *not* done here: each side
   (the HIP library and the oracle) encodes these float32 values itself.
+* shared expert weights (optional): the same shapes and distribution from
+  streams of their own; each side encodes them to MXFP8 itself.
 """
 from __future__ import annotations
 
@@ -31,6 +33,7 @@ import numpy as np
 # stream tags inside a SeedSequence
 _S_X, _S_LOGITS, _S_BIAS, _S_ZIPF_RANK, _S_GATE_UP, _S_DOWN = 1, 2, 3, 4, 10, 11
 _S_ROUTER = 12
+_S_SHARED_GATE_UP, _S_SHARED_DOWN = 13, 14
 
 WEIGHT_STD = 0.02
 
@@ -151,6 +154,16 @@ def make_weight_fp32(cfg: Config, which: str, expert: int,
     seed = cfg.seed if seed is None else seed
     stream = _S_GATE_UP if which == "gate_up" else _S_DOWN
     w = _rng(seed, stream, expert).standard_normal(weight_shape(cfg, which), dtype=np.float32)
+    w *= np.float32(WEIGHT_STD)
+    return w
+
+
+def make_shared_weight_fp32(cfg: Config, which: str, seed: int | None = None) -> np.ndarray:
+    """The shared expert's float32 matrix (gate_up [2I, H] or down [H, I]),
+    N(0, 0.02), before any encoding."""
+    seed = cfg.seed if seed is None else seed
+    stream = _S_SHARED_GATE_UP if which == "gate_up" else _S_SHARED_DOWN
+    w = _rng(seed, stream).standard_normal(weight_shape(cfg, which), dtype=np.float32)
     w *= np.float32(WEIGHT_STD)
     return w
 
