@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--router", action="store_true",
                    help="compute the router logits in the layer from a bf16 router weight [E, H] "
                         "(x . W_router^T on the matrix cores) instead of taking them as input")
+    p.add_argument("--shared", action="store_true",
+                   help="add an MXFP8 shared expert (gate_up [2I,H], down [H,I]) applied to every "
+                        "token; its bytes count in the touched bytes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the HBM streaming-read probe")
@@ -132,7 +135,7 @@ def probe_bandwidth(M, torch, nbytes: int = 4 << 30, reps: int = 20) -> float:
     return gbs
 
 
-def cpu_baseline(cfg, gbytes_total: float) -> dict:
+def cpu_baseline(cfg, gbytes_total: float, shared: bool = False) -> dict:
     """The oracle as it stands, on the host cores: the whole layer when it
     has at most CPU_SAMPLE_TOKENS tokens, else that many evenly spaced
     tokens with the time scaled by T / sample (the oracle's cost is per
@@ -155,10 +158,15 @@ def cpu_baseline(cfg, gbytes_total: float) -> dict:
 
     with ThreadPoolExecutor(4) as ex:
         weights = dict(ex.map(prep, experts))
+    sh = None
+    if shared:
+        from workloads import make_shared_weight_fp32
+        sh = (*oracle.quantize_mxfp8(make_shared_weight_fp32(cfg, "gate_up").astype(np.float64)),
+              *oracle.quantize_mxfp8(make_shared_weight_fp32(cfg, "down").astype(np.float64)))
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     oracle.forward(x, lg, cfg.k, cfg.H, cfg.I, weights, tokens=tokens,
-                   act_mxfp8=cfg.act == "mxfp8")
+                   act_mxfp8=cfg.act == "mxfp8", shared=sh)
     dt = (time.perf_counter() - t0) * cfg.T / len(tokens)
     what = (f"whole layer: all {cfg.T} tokens" if len(tokens) == cfg.T else
             f"{len(tokens)} of {cfg.T} tokens evenly spaced, time scaled by {cfg.T}/{len(tokens)}")
@@ -210,17 +218,27 @@ def main():
         router = torch.from_numpy(make_router_weight_bf16(cfg).view(np.int16)).view(
             torch.bfloat16).to("cuda")
 
+    shared = None
+    if args.shared:
+        from mxfp4_moe_expert_02_amd.layer import build_shared
+        shared = build_shared(cfg)
+
     def step(events=None):
         M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, wgu,
                                wdn, scales, layer.out, gemm_path=path, weight_layout=layout,
-                               events=events, act_format=act, launch=launch, router_weight=router)
+                               events=events, act_format=act, launch=launch, router_weight=router,
+                               shared=None if shared is None else shared.tiles)
 
     M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, wgu, wdn,
                            scales, layer.out, gemm_path=path, weight_layout=layout, counts=counts,
-                           act_format=act, router_weight=router)
+                           act_format=act, router_weight=router,
+                           shared=None if shared is None else shared.tiles)
     torch.cuda.synchronize()
     counts_np = counts.cpu().numpy()
     gu_bytes, dn_bytes = touched_bytes(counts_np, cfg.H, cfg.I)
+    if shared is not None:  # MXFP8: one byte per weight plus one scale byte per 32
+        gu_bytes += 2 * cfg.I * cfg.H + 2 * cfg.I * cfg.H // 32
+        dn_bytes += cfg.H * cfg.I + cfg.H * cfg.I // 32
     total_bytes = gu_bytes + dn_bytes
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -310,8 +328,9 @@ def main():
     gu_ms = stage_ms["gate_up"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     S = cfg.T * cfg.k
-    gu_flops = 2.0 * S * 2 * cfg.I * cfg.H
-    dn_flops = 2.0 * S * cfg.H * cfg.I
+    S_all = S + (cfg.T if shared is not None else 0)  # rows through the FFN
+    gu_flops = 2.0 * S_all * 2 * cfg.I * cfg.H
+    dn_flops = 2.0 * S_all * cfg.H * cfg.I
     if mx8:
         gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma",
@@ -355,6 +374,8 @@ def main():
                        router="computed in the layer from W_router [E,H] bf16" if router is not None
                        else "logits given",
                        weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",
+                       shared_expert="MXFP8 gate_up [2I,H] + down [H,I], every token"
+                       if shared is not None else "none",
                        activations="mxfp8" if mx8 else "bf16"),
         "tflops": {"layer": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
                    "gate_up": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
@@ -371,7 +392,7 @@ def main():
         result["cold_GBps"] = round(total_bytes / (cold * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, total_bytes / 1e9)
+        result["cpu_baseline"] = cpu_baseline(cfg, total_bytes / 1e9, shared=shared is not None)
     print(json.dumps(result), flush=True)
 
 

@@ -1,0 +1,425 @@
+// mfma_items.h -- the split-K expert GEMM bodies on the bf16 matrix cores
+// (weight formats of the tile layout, activation formats, the per-wave quad
+// loop, the gate_up and down item bodies, and the shared expert's blocks),
+// used by the kernels of mfma.hip and, for the shared expert's blocks, by
+// the wide and prefill kernels.  See mfma.hip for the tile layout and the
+// MFMA operand mapping.
+#pragma once
+
+#include "device_common.h"
+#include "mx_encode.h"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_MFMA_CHUNKS_PER_STEP
+#define MOE_MFMA_CHUNKS_PER_STEP 2
+#endif
+#ifndef MOE_MFMA_WAVES_PER_EU
+#define MOE_MFMA_WAVES_PER_EU 2
+#endif
+
+constexpr int kWaves = kMfmaThreads / kWave;  // 4, split K
+constexpr int kChunksPerStep = MOE_MFMA_CHUNKS_PER_STEP;  // 128-column chunks per prefetch step
+constexpr int kGroups = 4;                    // 16-row groups per quad
+
+// ---- weight formats of the tile layout (one 64-row quad, one 128-k chunk)
+// W4, MXFP4: 4 KB of codes, [group][lane][16 bytes], lane (r, g) holding
+// the 32 codes of block g of row r.  W8, MXFP8 (the 8-bit weights beside
+// the experts): 8 KB, [group][half][lane][16 bytes], half h holding codes
+// 16h..16h+15 of the lane's block.  Both: 256 scale bytes [lane][group].
+// a(b, rg, q) is the bf16 A operand of step q (codes 8q..8q+7 of the
+// lane's block of group rg), block scale applied by the conversion.
+struct W4 {
+    static constexpr int kChunkBytes = 4096;
+    struct Chunk {
+        uint4 w[kGroups];
+        uint32_t s;
+    };
+    static __device__ void load(const uint8_t* tiles, const uint8_t* tscales, int ci, Chunk& b) {
+        const int lane = threadIdx.x % kWave;
+        const uint8_t* t = tiles + (int64_t)ci * kChunkBytes + lane * 16;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++) b.w[rg] = load_stream16(t + rg * 1024);
+        b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
+    }
+    static __device__ bf16x8_t a(const Chunk& b, int rg, int q) {
+        return decode8(word_of(b.w[rg], q), e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
+    }
+};
+struct W8 {
+    static constexpr int kChunkBytes = 8192;
+    struct Chunk {
+        uint4 w[kGroups][2];
+        uint32_t s;
+    };
+    static __device__ void load(const uint8_t* tiles, const uint8_t* tscales, int ci, Chunk& b) {
+        const int lane = threadIdx.x % kWave;
+        const uint8_t* t = tiles + (int64_t)ci * kChunkBytes + lane * 16;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) b.w[rg][h] = load_stream16(t + rg * 2048 + h * 1024);
+        b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
+    }
+    static __device__ bf16x8_t a(const Chunk& b, int rg, int q) {
+        const uint4& v = b.w[rg][q >> 1];
+        return decode8_e4m3((q & 1) ? v.z : v.x, (q & 1) ? v.w : v.y,
+                            e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
+    }
+};
+
+// ---- activation formats of the B operand (one token row, 128-k chunk):
+// lane (c, g) takes block g of the chunk; b(x, q) is the bf16 B operand of
+// step q (elements 8q..8q+7 of the block).  XB: bf16 rows.  X8: MXFP8 rows
+// (E4M3 codes and one E8M0 scale per block, the prefill format), decoded
+// to bf16 exactly.  row(a, token) is a token's x row, hrow(a, r) row r of h.
+struct XB {
+    static constexpr bool kMx8 = false;
+    struct Row {
+        const uint16_t* p;
+    };
+    struct Chunk {
+        uint4 x[4];
+    };
+    static __device__ Row row(const GemmArgs& a, int t) { return Row{a.x + (int64_t)t * a.H}; }
+    static __device__ Row hrow(const GemmArgs& a, int r) { return Row{a.h + (int64_t)r * a.I}; }
+    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
+        const uint4* src = reinterpret_cast<const uint4*>(r.p + (int64_t)(4 * chunk + g) * 32);
+#pragma unroll
+        for (int q = 0; q < 4; q++) c.x[q] = src[q];
+    }
+    static __device__ bf16x8_t b(const Chunk& c, int q) { return __builtin_bit_cast(bf16x8_t, c.x[q]); }
+};
+struct X8 {
+    static constexpr bool kMx8 = true;
+    struct Row {
+        const uint8_t* c;
+        const uint8_t* s;
+    };
+    struct Chunk {
+        uint4 x[2];
+        uint32_t s;
+    };
+    static __device__ Row row(const GemmArgs& a, int t) {
+        return Row{a.xq + (int64_t)t * a.H, a.xs + (int64_t)t * (a.H / 32)};
+    }
+    static __device__ Row hrow(const GemmArgs& a, int r) {
+        return Row{a.hq + (int64_t)r * a.I, a.hs + (int64_t)r * (a.I / 32)};
+    }
+    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
+        const uint4* src = reinterpret_cast<const uint4*>(r.c + (int64_t)(4 * chunk + g) * 32);
+        c.x[0] = src[0];
+        c.x[1] = src[1];
+        c.s = r.s[4 * chunk + g];
+    }
+    static __device__ bf16x8_t b(const Chunk& c, int q) {
+        const uint4& v = c.x[q >> 1];
+        return decode8_e4m3((q & 1) ? v.z : v.x, (q & 1) ? v.w : v.y, e8m0_as_scale(c.s));
+    }
+};
+
+// chunks per prefetch step: MXFP4 single-tile items kChunksPerStep, wider
+// ones one (their x operands alone fill 16 VGPRs per tile and chunk);
+// MXFP8 weights one (a chunk is already twice the bytes)
+#ifndef MOE_MFMA_WIDE_CPS
+#define MOE_MFMA_WIDE_CPS 1
+#endif
+
+template <int NT, typename W>
+struct Cps {
+    static constexpr int value =
+        W::kChunkBytes != 4096 ? 1 : NT == 1 ? kChunksPerStep : NT == 2 ? MOE_MFMA_WIDE_CPS : 1;
+};
+
+template <typename W, int CPS>
+struct WStep {
+    typename W::Chunk c[CPS];
+};
+
+template <typename X, int NT, int CPS>
+struct XStep {
+    typename X::Chunk x[CPS][NT];
+};
+
+// One wave: chunks [c_begin, c_end) of one quad against NT column tiles of
+// 16 tokens.  tiles/tscales point at the quad's chunk 0; rows_of(xrow)
+// fills this lane's token row of every tile -- a real row for every lane:
+// lanes past the item's tokens repeat one of its rows, and their output
+// columns are never stored -- and is called only after the first weight
+// loads are in flight (it usually waits on an index load).  Each weight
+// word is decoded once and feeds the NT tiles' MFMAs.
+//
+// Per step (CPS chunks): the x loads of this step, then the weight loads of
+// the next step, then the MFMAs.  Loads complete in issue order, so the
+// wait for x leaves the next step's weights in flight during the MFMAs.
+// For that the loads must stay in this order (sched_barrier) and carry no
+// conditions: a load skipped on some path makes the wait conservative, a
+// full drain.  So every load is unconditional -- a partial last step loads
+// its last chunk again (in the same step: a cache hit) and skips that
+// chunk's MFMAs -- and the last step, which prefetches nothing, is peeled.
+template <int NT, typename W, typename X, typename RowsFn>
+__device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowsFn rows_of,
+                                 int c_begin, int c_end, f32x4_t (&acc)[kGroups][NT]) {
+    constexpr int CPS = Cps<NT, W>::value;
+    const int lane = threadIdx.x % kWave, g = lane / 16;
+    typename X::Row xrow[NT];
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (c_begin >= c_end) return;
+    auto chunk_of = [&](int c0, int i) { return min(c0 + i, c_end - 1); };
+    auto load_w = [&](int c0, WStep<W, CPS>& b) {
+#pragma unroll
+        for (int i = 0; i < CPS; i++) W::load(tiles, tscales, chunk_of(c0, i), b.c[i]);
+    };
+    auto load_x = [&](int c0, XStep<X, NT, CPS>& xb) {
+#pragma unroll
+        for (int i = 0; i < CPS; i++)
+#pragma unroll
+            for (int t = 0; t < NT; t++) X::load(xrow[t], chunk_of(c0, i), g, xb.x[i][t]);
+    };
+    auto compute = [&](int c0, const WStep<W, CPS>& b, const XStep<X, NT, CPS>& xb) {
+#pragma unroll
+        for (int i = 0; i < CPS; i++) {
+            if (c0 + i >= c_end) break;  // the repeated chunk of a partial step
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+#pragma unroll
+                for (int rg = 0; rg < kGroups; rg++) {
+                    const bf16x8_t A = W::a(b.c[i], rg, q);
+#pragma unroll
+                    for (int t = 0; t < NT; t++)
+                        acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, X::b(xb.x[i][t], q),
+                                                                             acc[rg][t], 0, 0, 0);
+                }
+            }
+        }
+    };
+    WStep<W, CPS> wa, wb;
+    XStep<X, NT, CPS> xa;
+    int c = c_begin;
+    int left = (c_end - c_begin + CPS - 1) / CPS;  // steps
+    load_w(c, wa);
+    rows_of(xrow);
+    while (left >= 3) {  // two steps, each with a successor to prefetch
+        load_x(c, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wb);
+        compute(c, wa, xa);
+        c += CPS;
+        load_x(c, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wa);
+        compute(c, wb, xa);
+        c += CPS;
+        left -= 2;
+    }
+    if (left == 2) {
+        load_x(c, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(c + CPS, wb);
+        compute(c, wa, xa);
+        c += CPS;
+        load_x(c, xa);
+        compute(c, wb, xa);
+    } else {
+        load_x(c, xa);
+        compute(c, wa, xa);
+    }
+}
+
+// Sum the 4 waves' accumulators (split K) through LDS; wave 0 gets the total.
+template <int NT>
+__device__ inline void reduce_waves(f32x4_t (&acc)[kGroups][NT], f32x4_t* red) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    if (w > 0) {
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                red[(((w - 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int v = 1; v < kWaves; v++)
+#pragma unroll
+            for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    acc[rg][t] += red[(((v - 1) * kGroups + rg) * NT + t) * kWave + lane];
+    }
+}
+
+__device__ inline void wave_chunk_range(int chunks, int& c_begin, int& c_end) {
+    const int per = (chunks + kWaves - 1) / kWaves;
+    const int w = threadIdx.x / kWave;
+    c_begin = min(chunks, w * per);
+    c_end = min(chunks, c_begin + per);
+}
+
+// LDS for the cross-wave sums of single-tile items
+constexpr int kRedGateUp = (kWaves - 1) * kGroups * kWave;
+constexpr int kRedDown = 2 * kGroups * kWave;
+
+// gate_up body for items of NT column tiles, token rows from `rows`
+// (SortedRows, SlotRows, ListRows or TokenRows); gu/gus: the expert's
+// gate_up tiles (format W), x and h in format X.
+template <int NT, typename W, typename X, typename Rows>
+__device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* gu,
+                                    const uint8_t* gus, const Rows& rows, f32x4_t* red) {
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int m = rows.m;
+    const int chunks = a.H / 128;
+    int cb, ce;
+    wave_chunk_range(chunks, cb, ce);
+    f32x4_t acc[kGroups][NT];
+    mfma_quad<NT, W, X>(gu + (int64_t)quad * chunks * W::kChunkBytes,
+                        gus + (int64_t)quad * chunks * 256,
+                        [&](typename X::Row (&xrow)[NT]) {
+#pragma unroll
+                            for (int t = 0; t < NT; t++)
+                                xrow[t] = X::row(a, rows.token(a, min(16 * t + c, m - 1)));
+                        },
+                        cb, ce, acc);
+    reduce_waves<NT>(acc, red);
+    if (threadIdx.x >= kWave) return;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        if constexpr (!X::kMx8) {
+            if (j >= m) continue;
+            uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
+#pragma unroll
+            for (int rg = 0; rg < 2; rg++) {
+                ushort4 o;
+                o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
+                o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
+                o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
+                o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
+                store_h4(hrow + 16 * rg, o);
+            }
+        } else {
+            // h of this quad and token = one MX block of 32, held by lanes
+            // (c, 0..3): they agree on its scale through two cross-lane
+            // maxima (every lane takes part), then write their codes
+            float hv[8];
+            uint32_t amax = 0;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float v = silu_mul(acc[h2][t][i], acc[h2 + 2][t][i]);
+                    hv[4 * h2 + i] = v;
+                    const uint32_t mb = __float_as_uint(v) & 0x7fffffffu;
+                    amax = mb > amax ? mb : amax;
+                }
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+            uint32_t code[2] = {0, 0};
+            uint32_t scale = 255;
+            if (amax < 0x7f800000u) {
+                const int se = mxfp8_scale_exp(amax);
+                scale = (uint32_t)(se + 127);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) code[h2] |= e4m3_code(hv[4 * h2 + i], se) << (8 * i);
+            }
+            if (j < m) {
+                const int r = rows.row(j);
+                uint8_t* hrow = a.hq + (int64_t)r * a.I + 32 * quad + 4 * g;
+                *reinterpret_cast<uint32_t*>(hrow) = code[0];       // h 32q + 4g + i
+                *reinterpret_cast<uint32_t*>(hrow + 16) = code[1];  // h 32q + 16 + 4g + i
+                if (g == 0) a.hs[(int64_t)r * (a.I / 32) + quad] = (uint8_t)scale;
+            }
+        }
+    }
+}
+
+// down body for items of NT column tiles (see mfma_down_kernel), token rows
+// from `rows`; dn/dns: the expert's down tiles (format W), h in format X;
+// COMBINE: see store_down_tile
+template <int NT, bool COMBINE, typename W, typename X, typename Rows>
+__device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
+                                 const uint8_t* dns, const Rows& rows, f32x4_t* red) {
+    const int m = rows.m;
+    const int quads = a.H / 64;
+    const int w = threadIdx.x / kWave, half = w & 1;
+    const int quad = pair * 2 + (w >> 1);
+    const int lane = threadIdx.x % kWave, c = lane % 16;
+    const int chunks = a.I / 128;
+    const bool live = quad < quads;
+    f32x4_t acc[kGroups][NT];
+    if (live) {
+        const int hc = (chunks + 1) / 2;
+        mfma_quad<NT, W, X>(dn + (int64_t)quad * chunks * W::kChunkBytes,
+                            dns + (int64_t)quad * chunks * 256,
+                            [&](typename X::Row (&xrow)[NT]) {
+#pragma unroll
+                                for (int t = 0; t < NT; t++)
+                                    xrow[t] = X::hrow(a, rows.row(min(16 * t + c, m - 1)));
+                            },
+                            half ? hc : 0, half ? chunks : hc, acc);
+        if (half) {
+#pragma unroll
+            for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane] = acc[rg][t];
+        }
+    }
+    __syncthreads();
+    if (!live || half) return;
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
+    store_down_tile<NT, COMBINE>(a, quad, rows, acc);
+}
+
+// ---- the shared expert: MXFP8 weights, every token.  The pages keep all
+// but the MoE experts at 8 bits (bjdmk.com.cn news page, co-design
+// section; yifor-blog digest, selective FP4 quantisation); a shared expert
+// beside the routed ones is such a part.  Same quads, split-K waves and
+// epilogues as the routed items, over tiles of 16 * NT of the T tokens (h
+// and y rows sh_row0 + t).  Block b of the shared blocks takes unit u of
+// `units` row units (gate_up quads or down quad pairs) and tile `tile`:
+// b = x + 8 * (tile + tiles * g) with u = 8g + x, so the tiles of one unit
+// run on one XCD (block index mod 8) one after another, and its weights
+// come from HBM about once.  The shared blocks are a multiple of 8 and come
+// ahead of the routed blocks of the same launch (the split launch of the
+// single-tile kernels), or form a launch of their own.
+__device__ inline bool shared_unit(int b, int units, int tiles, int& unit, int& tile) {
+    const int x = b % 8, r = b / 8;
+    tile = r % tiles;
+    unit = 8 * (r / tiles) + x;
+    return unit < units;
+}
+
+__host__ __device__ inline int shared_blocks(int units, int tiles) { return 8 * tiles * ((units + 7) / 8); }
+
+template <int NT, typename X>
+__device__ inline void shared_gate_up_block(const GemmArgs& a, int b, f32x4_t* red) {
+    const int tok = 16 * NT;
+    int quad, tile;
+    if (!shared_unit(b, a.I / 32, (a.T + tok - 1) / tok, quad, tile)) return;
+    const int t0 = tok * tile;
+    gate_up_item<NT, W8, X>(a, quad, a.sh_wgu, a.sh_sgu, TokenRows{t0, min(tok, a.T - t0), a.sh_row0},
+                            red);
+}
+
+template <int NT, typename X>
+__device__ inline void shared_down_block(const GemmArgs& a, int b, f32x4_t* red) {
+    const int tok = 16 * NT;
+    int pair, tile;
+    if (!shared_unit(b, (a.H / 64 + 1) / 2, (a.T + tok - 1) / tok, pair, tile)) return;
+    const int t0 = tok * tile;
+    down_item<NT, false, W8, X>(a, pair, a.sh_wdn, a.sh_sdn,
+                                TokenRows{t0, min(tok, a.T - t0), a.sh_row0}, red);
+}
+
+}  // namespace
+}  // namespace moe

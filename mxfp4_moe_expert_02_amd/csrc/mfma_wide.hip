@@ -20,7 +20,7 @@
 // unconditional loads (rows past the item repeat its last token: they only
 // feed output columns that are never stored).  No cross-wave reduction is
 // needed: each wave ends with its quad's complete sums.
-#include "device_common.h"
+#include "mfma_items.h"
 
 namespace moe {
 namespace {
@@ -33,7 +33,6 @@ constexpr int kWThreads = 256;
 constexpr int kWQuads = 4;                     // quads per workgroup (one per wave)
 constexpr int kWMaxTiles = kMfmaItemTok / 16;  // 4
 constexpr int kXRow = 272;                     // LDS bytes per staged token row (256 + 16)
-constexpr int kGroups = 4;
 
 struct WSmem {
     alignas(16) uint8_t x[2][kWMaxTiles * 16 * kXRow];  // [buffer][token row][272]
@@ -194,8 +193,18 @@ __device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int
 // gate_up: blockIdx.x = item * (I / 128) + quad block (quads 4qb..4qb+3)
 __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_gate_up_kernel(GemmArgs a) {
     __shared__ WSmem sm;
+    static_assert(sizeof(WSmem) >= sizeof(f32x4_t) * kRedGateUp * 2, "LDS of the shared blocks");
     const int qblocks = a.I / 128;
-    const int item = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
+    int b = blockIdx.x;
+    if (a.sh_wgu) {  // the shared expert's blocks first (32-token tiles, split-K)
+        const int nb = shared_blocks(a.I / 32, (a.T + 31) / 32);
+        if (b < nb) {
+            shared_gate_up_block<2, XB>(a, b, reinterpret_cast<f32x4_t*>(&sm));
+            return;
+        }
+        b -= nb;
+    }
+    const int item = b / qblocks, qb = b % qblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
@@ -215,8 +224,18 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_gate_up
 // combine tile (the last finisher of a token's k experts combines it)
 __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_kernel(GemmArgs a) {
     __shared__ WSmem sm;
+    static_assert(sizeof(WSmem) >= sizeof(f32x4_t) * kRedDown * 2, "LDS of the shared blocks");
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
-    const int item = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
+    int b = blockIdx.x;
+    if (a.sh_wdn) {  // the shared expert's blocks first
+        const int nb = shared_blocks((a.H / 64 + 1) / 2, (a.T + 31) / 32);
+        if (b < nb) {
+            shared_down_block<2, XB>(a, b, reinterpret_cast<f32x4_t*>(&sm));
+            return;
+        }
+        b -= nb;
+    }
+    const int item = b / qblocks, qb = b % qblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
@@ -293,13 +312,15 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_k
 }  // namespace
 
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
-    wide_gate_up_kernel<<<max_items * (a.I / 128), kWThreads, 0, stream>>>(a);
+    const int sh = a.sh_wgu ? shared_blocks(a.I / 32, (a.T + 31) / 32) : 0;
+    wide_gate_up_kernel<<<sh + max_items * (a.I / 128), kWThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
-    wide_down_kernel<<<max_items * qblocks, kWThreads, 0, stream>>>(a);
+    const int sh = a.sh_wdn ? shared_blocks((a.H / 64 + 1) / 2, (a.T + 31) / 32) : 0;
+    wide_down_kernel<<<sh + max_items * qblocks, kWThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -321,12 +321,15 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     // The shared expert needs no routing: its gate_up runs ahead of the
     // routed gate_up, its down ahead of the routed down (which, on the VALU
     // path and in the single-launch layer, also combines), both in the
-    // stages of the routed ones.
+    // stages of the routed ones.  The matrix-core GEMM kernels of the split
+    // launch run its workgroups themselves, ahead of the routed ones; the
+    // VALU path and the single-launch layer launch them on their own.
+    const bool shared_inside = path == MOE_PATH_MFMA && (mx8 || o.launch != MOE_LAUNCH_FUSED);
     auto shared_gate_up = [&]() -> hipError_t {
-        return shared ? moe::launch_shared_gate_up(a, mx8, st) : hipSuccess;
+        return shared && !shared_inside ? moe::launch_shared_gate_up(a, st) : hipSuccess;
     };
     auto shared_down = [&]() -> hipError_t {
-        return shared ? moe::launch_shared_down(a, mx8, st) : hipSuccess;
+        return shared && !shared_inside ? moe::launch_shared_down(a, st) : hipSuccess;
     };
     if ((err = shared_gate_up()) != hipSuccess) return hip_fail(err, "shared gate_up");
     if (self) {

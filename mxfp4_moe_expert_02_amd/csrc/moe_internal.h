@@ -222,11 +222,12 @@ hipError_t launch_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uin
                                  uint8_t* scales, hipStream_t stream);
 hipError_t launch_quantize_mxfp8(const float* w, int64_t rows, int64_t cols, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream);
-// The shared expert (MXFP8 weights) over all T tokens in tiles of 16, on
-// the bf16 matrix cores; mx8: x and h in MXFP8 (the prefill format) instead
-// of bf16.  gate_up writes h rows sh_row0 + t, down writes y rows
+// The shared expert (MXFP8 weights) over all T tokens, on the bf16 matrix
+// cores, as launches of its own (the VALU path and the single-launch layer;
+// the other GEMM kernels run its blocks ahead of their routed ones when
+// sh_wgu is set).  gate_up writes h rows sh_row0 + t, down writes y rows
 // sh_row0 + t; the combine adds them with weight 1.
-hipError_t launch_shared_gate_up(const GemmArgs& a, bool mx8, hipStream_t stream);
-hipError_t launch_shared_down(const GemmArgs& a, bool mx8, hipStream_t stream);
+hipError_t launch_shared_gate_up(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_shared_down(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace moe

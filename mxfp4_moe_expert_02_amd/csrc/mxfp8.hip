@@ -35,8 +35,7 @@
 // XOR-swizzled so that operand reads are free of bank conflicts.  The token
 // rows of x are gathered through the routing order; h rows are already in
 // that order.
-#include "device_common.h"
-#include "mx_encode.h"
+#include "mfma_items.h"
 
 namespace moe {
 namespace {
@@ -251,9 +250,22 @@ __device__ inline int wave_tiles(int m, int wt) {
 // two cross-lane maxima.
 __global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
 mx8_gate_up_kernel(GemmArgs a) {
-    __shared__ PfSmem sm;
+    __shared__ union {
+        PfSmem pf;
+        f32x4_t red[kRedGateUp * 4];  // the shared expert's blocks
+    } lds;
+    PfSmem& sm = lds.pf;
     const int rowblocks = a.I / 64;
-    const int item = blockIdx.x / rowblocks, rb = blockIdx.x % rowblocks;
+    int b = blockIdx.x;
+    if (a.sh_wgu) {  // the shared expert's blocks first (64-token tiles, split-K)
+        const int nb = shared_blocks(a.I / 32, (a.T + 63) / 64);
+        if (b < nb) {
+            shared_gate_up_block<4, X8>(a, b, lds.red);
+            return;
+        }
+        b -= nb;
+    }
+    const int item = b / rowblocks, rb = b % rowblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
@@ -314,9 +326,22 @@ mx8_gate_up_kernel(GemmArgs a) {
 // combine runs as its own kernel after this one (combine.hip).
 __global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
 mx8_down_kernel(GemmArgs a) {
-    __shared__ PfSmem sm;
+    __shared__ union {
+        PfSmem pf;
+        f32x4_t red[kRedDown * 4];  // the shared expert's blocks
+    } lds;
+    PfSmem& sm = lds.pf;
     const int rowblocks = a.H / 128;
-    const int item = blockIdx.x / rowblocks, rb = blockIdx.x % rowblocks;
+    int b = blockIdx.x;
+    if (a.sh_wdn) {  // the shared expert's blocks first
+        const int nb = shared_blocks((a.H / 64 + 1) / 2, (a.T + 63) / 64);
+        if (b < nb) {
+            shared_down_block<4, X8>(a, b, lds.red);
+            return;
+        }
+        b -= nb;
+    }
+    const int item = b / rowblocks, rb = b % rowblocks;
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
@@ -362,12 +387,14 @@ hipError_t launch_quantize_x_mxfp8(const uint16_t* x, int T, int H, uint8_t* cod
 }
 
 hipError_t launch_mx8_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
-    mx8_gate_up_kernel<<<max_items * (a.I / 64), kPfThreads, 0, stream>>>(a);
+    const int sh = a.sh_wgu ? shared_blocks(a.I / 32, (a.T + 63) / 64) : 0;
+    mx8_gate_up_kernel<<<sh + max_items * (a.I / 64), kPfThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_mx8_down(const GemmArgs& a, int max_items, hipStream_t stream) {
-    mx8_down_kernel<<<max_items * (a.H / 128), kPfThreads, 0, stream>>>(a);
+    const int sh = a.sh_wdn ? shared_blocks((a.H / 64 + 1) / 2, (a.T + 63) / 64) : 0;
+    mx8_down_kernel<<<sh + max_items * (a.H / 128), kPfThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

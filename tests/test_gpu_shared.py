@@ -188,6 +188,11 @@ CASES = {  # name: (config, path, act, launch, sampled tokens or None = all)
     "t40_wide": (("t", 40, 4), 2, 0, 0, None),
     "t33_mx8": (("t", 33), 0, 1, 0, None),
     "t50_gemv": (("t", 50), 1, 0, 0, None),
+    "t70_wide": (("t", 70, 4), 2, 0, 0, None),      # 64-token shared tiles, a ragged one
+    "t100_mx8": (("t", 100), 0, 1, 0, None),
+    "t130_split": (("t", 130, 64), 2, 0, 0, None),   # shared blocks inside the split kernels
+    "t80_gemv": (("t", 80), 1, 0, 0, None),          # own launches, 64-token tiles
+    "t70_fused": (("t", 70, 64), 2, 0, 2, None),
     "c2_self": ("c2", 2, 0, 0, [0, 4, 8]),
     "c3_split": ("c3", 2, 0, 0, [0, 35, 71]),
     "c4_wide": ("c4", 2, 0, 0, [0, 143, 287]),
@@ -200,7 +205,7 @@ def _cfg(spec, act):
         return get_config(spec)
     T = spec[1]
     E = spec[2] if len(spec) > 2 else 8
-    return _small(T, 50 + T, E=E, act="mxfp8" if act else "bf16")
+    return _small(T, 50 + T, E=E, k=min(2, E), act="mxfp8" if act else "bf16")
 
 
 @pytest.mark.parametrize("name", list(CASES))
