@@ -28,13 +28,12 @@
 // waves form a 2 x 2 grid: wave (wr, wt) owns quad wr and the token tiles
 // wt, wt+2, wt+4, wt+6 of 16 tokens (4 row groups x 4 column tiles = 16
 // MFMAs per 128-k chunk).
-// A comes straight from global memory in operand order (one 1 KB wave load
-// per row group); B, shared by the two waves of a token half, goes from
-// global memory directly into double-buffered LDS (global_load_lds, 16
-// bytes per lane, lane l at byte 16l of the wave's 1 KB destination),
-// XOR-swizzled so that operand reads are free of bank conflicts.  The token
-// rows of x are gathered through the routing order; h rows are already in
-// that order.
+// Both operands go from global memory straight into LDS (direct global ->
+// LDS loads, 16 bytes per lane), three chunks deep: A (the two quads' tiles,
+// already in operand order) and B (XOR-swizzled rows, so that operand reads
+// are free of bank conflicts); each wave then reads its A and B operands of
+// the chunk from LDS.  The token rows of x are gathered through the routing
+// order; h rows are already in that order.
 #include "mfma_items.h"
 
 namespace moe {
@@ -42,9 +41,6 @@ namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-#ifndef MOE_PF_SCHED_BARRIERS
-#define MOE_PF_SCHED_BARRIERS 0
-#endif
 #ifndef MOE_PF_WAVES_PER_EU
 #define MOE_PF_WAVES_PER_EU 2
 #endif
@@ -94,54 +90,120 @@ quantize_x_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
     scales[b] = s;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Staged B of one chunk: 128 token rows of 128 code bytes, 16-byte piece p
-// of row r stored in slot p ^ ((r >> 1) & 7).  A 16-lane quarter of an
-// operand read (rows c = 0..15, one piece) then covers the 64 banks once.
+// Staged operands of one 128-k chunk, three chunks deep:
+//   B: 128 token rows of 128 code bytes, 16-byte piece p of row r in slot
+//      p ^ ((r >> 1) & 7) (a 16-lane quarter of an operand read then covers
+//      the 64 banks once), and the chunk's 4 block scales per token;
+//   A: the two quads' 4 KB weight tiles (the global tile layout as is) and
+//      their 256 scale bytes.
+constexpr int kPfStages = 3;
 struct PfSmem {
-    alignas(16) uint8_t b[2][kMx8Tok * 128];
-    alignas(16) uint32_t bs[2][kMx8Tok];  // the chunk's 4 block scales per token
+    alignas(16) uint8_t b[kPfStages][kMx8Tok * 128];
+    alignas(16) uint8_t a[kPfStages][2][4096];
+    alignas(16) uint32_t bs[kPfStages][kMx8Tok];
+    alignas(16) uint32_t as[kPfStages][2][kWave];
 };
 
 __device__ inline int b_slot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
-// Where this lane's direct-to-LDS loads come from.  Wave w fills LDS rows
-// 32w .. 32w+31 of a chunk with four 1 KB loads (lane l: row 32w + 8i +
-// l/8, slot l % 8); waves 0 and 1 also load the scale words of tokens
-// 64w + l.  Rows past the item's m tokens repeat row m-1: they only feed
-// output columns that are never stored.
+// Direct global -> LDS loads (16 or 4 bytes per lane; lane l's bytes land
+// at lds + 16 l, or 4 l).  Written as inline asm so that the compiler does
+// not treat every later LDS read as depending on them (it would wait for all
+// of them, a full drain, before each read); the main loop waits for them
+// itself.  M0 (the LDS base) is saved and restored inside the block.
+typedef __attribute__((address_space(3))) const void lds_cvoid_t;
+__device__ inline uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_cvoid_t*)p);
+}
+__device__ inline void dma16(const uint8_t* src, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+__device__ inline void dma4(const uint8_t* src, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+
+// Where this lane's loads of a chunk come from.  Wave w fills B rows
+// 32w .. 32w+31 with four 1 KB loads (lane l: row 32w + 8i + l/8, slot
+// l % 8); waves 0, 1 load the scale words of tokens 64w + l, waves 2, 3 the
+// scale dword of lane l of quad w - 2; and wave w loads row groups
+// 2(w & 1), 2(w & 1) + 1 of quad w >> 1.  Seven loads per wave per chunk.
+// Rows past the item's m tokens repeat row m-1: they only feed output
+// columns that are never stored.
 struct StageSrc {
     const uint8_t* row[4];  // code bytes of the row's piece for this lane, chunk 0
-    const uint8_t* srow;    // scale bytes of this lane's token, chunk 0 (waves 0, 1)
+    const uint8_t* sc;      // this lane's scale bytes, chunk 0 (B or A scales)
+    int sc_step;            // bytes per chunk of sc: 4 (B) or 256 (A)
+    const uint8_t* a[2];    // this wave's two A row groups, chunk 0 (lane offset included)
 };
+constexpr int kPfLoadsPerChunk = 7;  // the vmcnt(7) of pf_mainloop
 
 __device__ inline void stage_issue(const StageSrc& src, int chunk, PfSmem& sm, int buf) {
     const int w = threadIdx.x / kWave;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-        __builtin_amdgcn_global_load_lds(src.row[i] + chunk * 128,
-                                         (lds_void_t*)&sm.b[buf][(32 * w + 8 * i) * 128], 16, 0, 0);
-    if (w < 2)
-        __builtin_amdgcn_global_load_lds(src.srow + chunk * 4, (lds_void_t*)&sm.bs[buf][64 * w], 4,
-                                         0, 0);
+    for (int i = 0; i < 4; i++) dma16(src.row[i] + chunk * 128, lds_addr(&sm.b[buf][(32 * w + 8 * i) * 128]));
+    dma4(src.sc + chunk * src.sc_step,
+         lds_addr(w < 2 ? (const void*)&sm.bs[buf][64 * w] : (const void*)&sm.as[buf][w - 2][0]));
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+        dma16(src.a[j] + (int64_t)chunk * 4096,
+              lds_addr(&sm.a[buf][w >> 1][(2 * (w & 1) + j) * 1024]));
 }
 
 // lane's LDS row for staging load i of wave w, and the piece it carries
 __device__ inline int stage_row(int i) { return 32 * (threadIdx.x / kWave) + 8 * i + (threadIdx.x % kWave) / 8; }
 __device__ inline int stage_piece(int i) { return b_slot(stage_row(i), threadIdx.x % 8); }
 
+// The loads of a workgroup's chunks: B rows from `rows`, this lane's scale
+// bytes, and the A tiles of quads 2rb, 2rb + 1 (tiles/tscales at quad 2rb).
+template <typename RowFn>
+__device__ inline StageSrc stage_src(RowFn code_row, const uint8_t* scale_row, const uint8_t* tiles,
+                                     const uint8_t* tscales, int chunks) {
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    StageSrc src;
+#pragma unroll
+    for (int i = 0; i < 4; i++) src.row[i] = code_row(stage_row(i)) + 16 * stage_piece(i);
+    if (w < 2) {
+        src.sc = scale_row;
+        src.sc_step = 4;
+    } else {
+        src.sc = tscales + (int64_t)(w - 2) * chunks * 256 + lane * 4;
+        src.sc_step = 256;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+        src.a[j] = tiles + (int64_t)(w >> 1) * chunks * 4096 + (2 * (w & 1) + j) * 1024 + lane * 16;
+    return src;
+}
+
 struct AOperand {
     uint4 w[4];  // row groups 0..3 of the quad
     uint32_t s;  // their four scale bytes
 };
 
-__device__ inline void load_a(const uint8_t* tiles, const uint8_t* tscales, int chunk, AOperand& a) {
-    const int lane = threadIdx.x % kWave;
-    const uint8_t* t = tiles + (int64_t)chunk * 4096 + lane * 16;
+// this wave's A operand (quad wr) of the chunk in LDS buffer `buf`
+__device__ inline void read_a(const PfSmem& sm, int buf, AOperand& a) {
+    const int lane = threadIdx.x % kWave, wr = (threadIdx.x / kWave) & 1;
 #pragma unroll
-    for (int rg = 0; rg < 4; rg++) a.w[rg] = *reinterpret_cast<const uint4*>(t + rg * 1024);
-    a.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)chunk * 256 + lane * 4);
+    for (int rg = 0; rg < 4; rg++) a.w[rg] = *reinterpret_cast<const uint4*>(&sm.a[buf][wr][rg * 1024 + lane * 16]);
+    a.s = sm.as[buf][wr][lane];
 }
 
 // Column tile t of wave (wr, wt) is token tile 2t + wt of the item
@@ -186,53 +248,50 @@ __device__ inline void chunk_mfma(const AOperand& ac, const BOperands<NT>& b,
     }
 }
 
-// The main loop of one workgroup: acc[rg][t] = quad rows (group rg) x
-// column tile t of this wave (t < NT), summed over all `chunks` 128-k
-// chunks.  tiles/tscales point at this wave's quad.
+// The main loop of one workgroup: acc[rg][t] = this wave's quad (group rg)
+// x column tile t (t < NT), summed over all `chunks` 128-k chunks.
 //
-// Step s: wait for this wave's loads (its share of chunk s in LDS buffer
-// s%2, A of chunk s) and meet the other waves at a barrier; read the B
-// operands of chunk s; issue A of chunk s+1 and the direct-to-LDS loads of
-// chunk s+1 into the other buffer (whose readers all passed this barrier);
-// run the MFMAs.  The loads of chunk s+1 thus fly during the MFMAs of chunk
-// s, and no staging registers are needed.  Every wave runs the same number
-// of barriers whatever its NT.
+// Chunks are staged three deep: step s waits for this wave's loads of chunk
+// s (vmcnt: only chunk s+1's seven loads may still be in flight) and meets
+// the other waves at a barrier (without a fence: only LDS is exchanged);
+// then it issues chunk s+2's loads into the buffer chunk s-1 left (every
+// wave finished reading it before this barrier), reads chunk s's operands
+// from LDS and runs its MFMAs.  A load thus has two steps of MFMAs to land.
+// Every wave runs the same number of barriers whatever its NT.
 template <int NT>
-__device__ inline void pf_mainloop(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
-                                   int chunks, PfSmem& sm, f32x4_t (&acc)[4][kPfTiles]) {
+__device__ inline void pf_mainloop(const StageSrc& src, int chunks, PfSmem& sm,
+                                   f32x4_t (&acc)[4][kPfTiles]) {
 #pragma unroll
     for (int rg = 0; rg < 4; rg++)
 #pragma unroll
         for (int t = 0; t < kPfTiles; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    AOperand a0, a1;
     stage_issue(src, 0, sm, 0);
-    load_a(tiles, tscales, 0, a0);
-    auto step = [&](int s, const AOperand& acur, AOperand& anext) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of chunk s
-        __syncthreads();                      // everyone's
+    if (chunks > 1) stage_issue(src, 1, sm, 1);
+    int buf = 0;
+    for (int s = 0; s < chunks; s++) {
+        static_assert(kPfLoadsPerChunk == 7, "the wait below counts a chunk's loads");
+        if (s + 1 < chunks)
+            asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + 2 < chunks) stage_issue(src, s + 2, sm, buf == 0 ? 2 : buf - 1);
+        AOperand ac;
+        read_a(sm, buf, ac);
         BOperands<NT> b;
-        read_b<NT>(sm, s & 1, b);
-        if (s + 1 < chunks) {
-            load_a(tiles, tscales, s + 1, anext);
-            stage_issue(src, s + 1, sm, (s & 1) ^ 1);
-        }
-        chunk_mfma<NT>(acur, b, acc);
-    };
-    for (int s = 0; s < chunks; s += 2) {
-        step(s, a0, a1);
-        if (s + 1 >= chunks) break;
-        step(s + 1, a1, a0);
+        read_b<NT>(sm, buf, b);
+        chunk_mfma<NT>(ac, b, acc);
+        buf = buf == 2 ? 0 : buf + 1;
     }
 }
 
-__device__ inline void pf_gemm(const uint8_t* tiles, const uint8_t* tscales, const StageSrc& src,
-                               int chunks, int ntile, PfSmem& sm, f32x4_t (&acc)[4][kPfTiles]) {
+__device__ inline void pf_gemm(const StageSrc& src, int chunks, int ntile, PfSmem& sm,
+                               f32x4_t (&acc)[4][kPfTiles]) {
     switch (ntile) {
-        case 4: pf_mainloop<4>(tiles, tscales, src, chunks, sm, acc); break;
-        case 3: pf_mainloop<3>(tiles, tscales, src, chunks, sm, acc); break;
-        case 2: pf_mainloop<2>(tiles, tscales, src, chunks, sm, acc); break;
-        case 1: pf_mainloop<1>(tiles, tscales, src, chunks, sm, acc); break;
-        default: pf_mainloop<0>(tiles, tscales, src, chunks, sm, acc); break;
+        case 4: pf_mainloop<4>(src, chunks, sm, acc); break;
+        case 3: pf_mainloop<3>(src, chunks, sm, acc); break;
+        case 2: pf_mainloop<2>(src, chunks, sm, acc); break;
+        case 1: pf_mainloop<1>(src, chunks, sm, acc); break;
+        default: pf_mainloop<0>(src, chunks, sm, acc); break;
     }
 }
 
@@ -274,17 +333,14 @@ mx8_gate_up_kernel(GemmArgs a) {
     const int K = a.H, chunks = K / 128, quads = a.I / 32;
     const int quad = 2 * rb + wr;
     const int64_t quad_id = (int64_t)e * quads + quad;
-    StageSrc src;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int j = min(stage_row(i), m - 1);
-        src.row[i] = a.xq + (int64_t)(a.sorted[row0 + j] / a.k) * K + 16 * stage_piece(i);
-    }
-    src.srow = a.xs + (int64_t)(a.sorted[row0 + min(64 * (w & 1) + lane, m - 1)] / a.k) * (K / 32);
+    const int64_t pair_id = (int64_t)e * quads + 2 * rb;
+    const StageSrc src = stage_src(
+        [&](int r) { return a.xq + (int64_t)(a.sorted[row0 + min(r, m - 1)] / a.k) * K; },
+        a.xs + (int64_t)(a.sorted[row0 + min(64 * (w & 1) + lane, m - 1)] / a.k) * (K / 32),
+        a.wgu + pair_id * chunks * 4096, a.sgu + pair_id * chunks * 256, chunks);
     const int ntile = uniform(wave_tiles(m, wt));
     f32x4_t acc[4][kPfTiles];
-    pf_gemm(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, src, chunks, ntile, sm,
-            acc);
+    pf_gemm(src, chunks, ntile, sm, acc);
 #pragma unroll
     for (int t = 0; t < kPfTiles; t++) {
         if (t >= ntile) break;
@@ -350,17 +406,14 @@ mx8_down_kernel(GemmArgs a) {
     const int K = a.I, chunks = K / 128, quads = a.H / 64;
     const int quad = 2 * rb + wr;
     const int64_t quad_id = (int64_t)e * quads + quad;
-    StageSrc src;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int j = min(stage_row(i), m - 1);
-        src.row[i] = a.hq + (int64_t)(row0 + j) * K + 16 * stage_piece(i);
-    }
-    src.srow = a.hs + (int64_t)(row0 + min(64 * (w & 1) + lane, m - 1)) * (K / 32);
+    const int64_t pair_id = (int64_t)e * quads + 2 * rb;
+    const StageSrc src = stage_src(
+        [&](int r) { return a.hq + (int64_t)(row0 + min(r, m - 1)) * K; },
+        a.hs + (int64_t)(row0 + min(64 * (w & 1) + lane, m - 1)) * (K / 32),
+        a.wdn + pair_id * chunks * 4096, a.sdn + pair_id * chunks * 256, chunks);
     const int ntile = uniform(wave_tiles(m, wt));
     f32x4_t acc[4][kPfTiles];
-    pf_gemm(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, src, chunks, ntile, sm,
-            acc);
+    pf_gemm(src, chunks, ntile, sm, acc);
     const int n0 = 64 * quad;
 #pragma unroll
     for (int t = 0; t < kPfTiles; t++) {
