@@ -322,7 +322,7 @@ gemv_down_kernel(GemmArgs a) {
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's y stores done
         __syncthreads();
-        if (threadIdx.x < m) {
+        if ((int)threadIdx.x < m) {
             const int token = a.sorted[off + t0 + threadIdx.x] / a.k;
             const int old = atomicAdd(&a.tile_done[token * td + tile], 1);
             s_combine[threadIdx.x] = (old == a.k - 1) ? token : -1;

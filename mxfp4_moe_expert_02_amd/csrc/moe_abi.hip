@@ -85,13 +85,13 @@ size_t layout(Workspace* ws, char* base) {
 
 void free_ws(Workspace* ws) {
     if (!ws) return;
-    if (ws->base) {
+    if (ws->base) {  // best effort: nothing to report to from here
         int cur = 0;
-        hipGetDevice(&cur);
-        hipSetDevice(ws->device);
-        hipDeviceSynchronize();
-        hipFree(ws->base);
-        hipSetDevice(cur);
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(ws->device);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(ws->base);
+        (void)hipSetDevice(cur);
     }
     delete ws;
 }

@@ -332,7 +332,6 @@ mx8_gate_up_kernel(GemmArgs a) {
     const int wr = w & 1, wt = w >> 1;
     const int K = a.H, chunks = K / 128, quads = a.I / 32;
     const int quad = 2 * rb + wr;
-    const int64_t quad_id = (int64_t)e * quads + quad;
     const int64_t pair_id = (int64_t)e * quads + 2 * rb;
     const StageSrc src = stage_src(
         [&](int r) { return a.xq + (int64_t)(a.sorted[row0 + min(r, m - 1)] / a.k) * K; },
@@ -405,7 +404,6 @@ mx8_down_kernel(GemmArgs a) {
     const int wr = w & 1, wt = w >> 1;
     const int K = a.I, chunks = K / 128, quads = a.H / 64;
     const int quad = 2 * rb + wr;
-    const int64_t quad_id = (int64_t)e * quads + quad;
     const int64_t pair_id = (int64_t)e * quads + 2 * rb;
     const StageSrc src = stage_src(
         [&](int r) { return a.hq + (int64_t)(row0 + min(r, m - 1)) * K; },
