@@ -2,12 +2,11 @@
 // (weight formats of the tile layout, activation formats, the per-wave quad
 // loop, the gate_up and down item bodies, and the shared expert's blocks),
 // used by the kernels of mfma.hip and, for the shared expert's blocks, by
-// the wide and prefill kernels.  See mfma.hip for the tile layout and the
+// the wide kernels.  See mfma.hip for the tile layout and the
 // MFMA operand mapping.
 #pragma once
 
 #include "device_common.h"
-#include "mx_encode.h"
 
 namespace moe {
 namespace {
@@ -69,13 +68,11 @@ struct W8 {
     }
 };
 
-// ---- activation formats of the B operand (one token row, 128-k chunk):
-// lane (c, g) takes block g of the chunk; b(x, q) is the bf16 B operand of
-// step q (elements 8q..8q+7 of the block).  XB: bf16 rows.  X8: MXFP8 rows
-// (E4M3 codes and one E8M0 scale per block, the prefill format), decoded
-// to bf16 exactly.  row(a, token) is a token's x row, hrow(a, r) row r of h.
+// ---- the activation format of the B operand (one token row, 128-k
+// chunk): lane (c, g) takes block g of the chunk; b(x, q) is the bf16 B
+// operand of step q (elements 8q..8q+7 of the block).  XB: bf16 rows;
+// row(a, token) is a token's x row, hrow(a, r) row r of h.
 struct XB {
-    static constexpr bool kMx8 = false;
     struct Row {
         const uint16_t* p;
     };
@@ -91,34 +88,6 @@ struct XB {
     }
     static __device__ bf16x8_t b(const Chunk& c, int q) { return __builtin_bit_cast(bf16x8_t, c.x[q]); }
 };
-struct X8 {
-    static constexpr bool kMx8 = true;
-    struct Row {
-        const uint8_t* c;
-        const uint8_t* s;
-    };
-    struct Chunk {
-        uint4 x[2];
-        uint32_t s;
-    };
-    static __device__ Row row(const GemmArgs& a, int t) {
-        return Row{a.xq + (int64_t)t * a.H, a.xs + (int64_t)t * (a.H / 32)};
-    }
-    static __device__ Row hrow(const GemmArgs& a, int r) {
-        return Row{a.hq + (int64_t)r * a.I, a.hs + (int64_t)r * (a.I / 32)};
-    }
-    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
-        const uint4* src = reinterpret_cast<const uint4*>(r.c + (int64_t)(4 * chunk + g) * 32);
-        c.x[0] = src[0];
-        c.x[1] = src[1];
-        c.s = r.s[4 * chunk + g];
-    }
-    static __device__ bf16x8_t b(const Chunk& c, int q) {
-        const uint4& v = c.x[q >> 1];
-        return decode8_e4m3((q & 1) ? v.z : v.x, (q & 1) ? v.w : v.y, e8m0_as_scale(c.s));
-    }
-};
-
 // chunks per prefetch step: MXFP4 single-tile items kChunksPerStep, wider
 // ones one (their x operands alone fill 16 VGPRs per tile and chunk);
 // MXFP8 weights one (a chunk is already twice the bytes)
@@ -289,52 +258,16 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* 
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         const int j = 16 * t + c;
-        if constexpr (!X::kMx8) {
-            if (j >= m) continue;
-            uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
+        if (j >= m) continue;
+        uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
 #pragma unroll
-            for (int rg = 0; rg < 2; rg++) {
-                ushort4 o;
-                o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
-                o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
-                o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
-                o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
-                store_h4(hrow + 16 * rg, o);
-            }
-        } else {
-            // h of this quad and token = one MX block of 32, held by lanes
-            // (c, 0..3): they agree on its scale through two cross-lane
-            // maxima (every lane takes part), then write their codes
-            float hv[8];
-            uint32_t amax = 0;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const float v = silu_mul(acc[h2][t][i], acc[h2 + 2][t][i]);
-                    hv[4 * h2 + i] = v;
-                    const uint32_t mb = __float_as_uint(v) & 0x7fffffffu;
-                    amax = mb > amax ? mb : amax;
-                }
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
-            uint32_t code[2] = {0, 0};
-            uint32_t scale = 255;
-            if (amax < 0x7f800000u) {
-                const int se = mxfp8_scale_exp(amax);
-                scale = (uint32_t)(se + 127);
-#pragma unroll
-                for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) code[h2] |= e4m3_code(hv[4 * h2 + i], se) << (8 * i);
-            }
-            if (j < m) {
-                const int r = rows.row(j);
-                uint8_t* hrow = a.hq + (int64_t)r * a.I + 32 * quad + 4 * g;
-                *reinterpret_cast<uint32_t*>(hrow) = code[0];       // h 32q + 4g + i
-                *reinterpret_cast<uint32_t*>(hrow + 16) = code[1];  // h 32q + 16 + 4g + i
-                if (g == 0) a.hs[(int64_t)r * (a.I / 32) + quad] = (uint8_t)scale;
-            }
+        for (int rg = 0; rg < 2; rg++) {
+            ushort4 o;
+            o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
+            o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
+            o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
+            o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
+            store_h4(hrow + 16 * rg, o);
         }
     }
 }
