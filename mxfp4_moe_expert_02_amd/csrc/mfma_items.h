@@ -322,9 +322,10 @@ __device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
 // `units` row units (gate_up quads or down quad pairs) and tile `tile`:
 // b = x + 8 * (tile + tiles * g) with u = 8g + x, so the tiles of one unit
 // run on one XCD (block index mod 8) one after another, and its weights
-// come from HBM about once.  The shared blocks are a multiple of 8 and come
-// ahead of the routed blocks of the same launch (the split launch of the
-// single-tile kernels), or form a launch of their own.
+// come from HBM about once (the prefill kernels map their one-quad blocks
+// the same way).  The shared blocks are a multiple of 8 and come ahead of
+// the routed blocks of the same launch (self-routed, split and wide
+// kernels), or form a launch of their own (mfma.hip).
 __device__ inline bool shared_unit(int b, int units, int tiles, int& unit, int& tile) {
     const int x = b % 8, r = b / 8;
     tile = r % tiles;
