@@ -252,3 +252,30 @@ def test_shared_deterministic_and_plain_after_shared(M):
     run(M, layer, path=2)
     assert torch.equal(plain.view(torch.int16), layer.out.view(torch.int16))
     assert not torch.equal(a.view(torch.int16), plain.view(torch.int16))
+
+
+@pytest.mark.parametrize("key", ["c2", "mx8"])
+def test_shared_expert_with_router_weight(M, oracle_lib, key):
+    """Both options together: the layer computes its logits from a bf16
+    router weight and adds the shared expert.  The routing is checked on
+    the GPU's fp32 logits (the decision in the same precision on both
+    sides), the output against the oracle on those logits."""
+    import torch
+    from workloads import make_router_weight_bf16
+    cfg = get_config("c2") if key == "c2" else _small(40, 77, E=8, act="mxfp8")
+    act = M.MOE_ACT_MXFP8 if cfg.act == "mxfp8" else M.MOE_ACT_BF16
+    layer = get_layer(cfg)
+    sh = get_shared(cfg)
+    w = make_router_weight_bf16(cfg)
+    w_dev = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to("cuda")
+    dbg = run(M, layer, path=0 if act else 2, act=act, debug=True, router=w_dev, shared=sh.tiles)
+    lg = dbg["logits_out"]
+    r = oracle_lib.route(lg, cfg.k)
+    np.testing.assert_array_equal(dbg["ids"], r["ids"])
+    tokens = sorted({0, cfg.T // 2, cfg.T - 1})
+    ex = oracle_experts(oracle_lib, cfg, r["ids"][tokens].ravel())
+    ref = oracle_lib.forward(make_x_bf16(cfg), lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens,
+                             act_mxfp8=bool(act), shared=oracle_shared(oracle_lib, cfg))
+    ratio = parity_ratio(bf16_tensor_to_f64(layer.out)[tokens], ref)
+    say(f"shared + router parity {cfg.name}: max|d|/rms = {ratio:.3e}")
+    assert ratio <= TOL
