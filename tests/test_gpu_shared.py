@@ -279,3 +279,20 @@ def test_shared_expert_with_router_weight(M, oracle_lib, key):
     ratio = parity_ratio(bf16_tensor_to_f64(layer.out)[tokens], ref)
     say(f"shared + router parity {cfg.name}: max|d|/rms = {ratio:.3e}")
     assert ratio <= TOL
+
+
+@pytest.mark.parametrize("path", [2, 0])
+def test_shared_nan_scales_reach_every_token(M, path):
+    """A NaN block scale (E8M0 0xFF) throughout the shared expert's down
+    matrix makes every output NaN (the shared expert is applied to every
+    token); the same layer without it stays finite."""
+    import torch
+    act = M.MOE_ACT_MXFP8 if path == 0 else M.MOE_ACT_BF16
+    cfg = _small(20, 91, act="mxfp8" if act else "bf16")
+    layer = get_layer(cfg)
+    sh = get_shared(cfg)
+    bad = (sh.gu_t, sh.gus_t, sh.dn_t, torch.full_like(sh.dns_t, 255))
+    run(M, layer, path=path, act=act)
+    assert torch.isfinite(layer.out.float()).all()
+    run(M, layer, path=path, act=act, shared=bad, init=False)
+    assert torch.isnan(layer.out.float()).all()
