@@ -51,7 +51,10 @@
  *
  * Concurrency: one workspace per device, shared by every call on that
  * device; calls whose work overlaps on one device (e.g. on two streams)
- * race.  Calls on different devices are independent.
+ * race.  Calls on different devices are independent.  moe_mxfp4_init and
+ * moe_mxfp4_finalize replace or free workspaces: no other host thread may
+ * be inside a call of this library meanwhile (they synchronise the device
+ * first, so work already enqueued is safe).
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
