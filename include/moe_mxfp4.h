@@ -186,6 +186,13 @@ typedef struct moe_mxfp4_options {
     const uint8_t* shared_gate_up_scales;
     const uint8_t* shared_down;
     const uint8_t* shared_down_scales;
+    /* Optional copies of h on the MOE_ACT_MXFP8 path (NULL: not copied;
+     * ignored on the other paths): h_codes [T*k, I] E4M3 codes and h_scales
+     * [T*k, I/32] E8M0 scales of the routed assignments, row p holding the
+     * assignment at position p of the expert-sorted order (`sorted`).  They
+     * expose the encoding decision of h, taken on fp32 values, for tests. */
+    uint8_t* h_codes;
+    uint8_t* h_scales;
 } moe_mxfp4_options;
 
 /* Allocate the workspace on the current device for layers with at most

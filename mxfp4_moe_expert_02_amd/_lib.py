@@ -64,7 +64,8 @@ class moe_mxfp4_options(ctypes.Structure):
                 ("launch", ctypes.c_int32), ("wait_error", ctypes.c_void_p),
                 ("router_weight", ctypes.c_void_p), ("logits_out", ctypes.c_void_p),
                 ("shared_gate_up", ctypes.c_void_p), ("shared_gate_up_scales", ctypes.c_void_p),
-                ("shared_down", ctypes.c_void_p), ("shared_down_scales", ctypes.c_void_p)]
+                ("shared_down", ctypes.c_void_p), ("shared_down_scales", ctypes.c_void_p),
+                ("h_codes", ctypes.c_void_p), ("h_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -153,6 +154,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                          x_scales=None, events=None, weight_layout: int = MOE_LAYOUT_ROWS,
                          launch: int = MOE_LAUNCH_AUTO, wait_error=None,
                          router_weight=None, logits_out=None, shared=None,
+                         h_codes=None, h_scales=None,
                          check: bool = True, validate: bool = True) -> int:
     """Enqueue one layer on ``stream`` (default: torch's current stream).
 
@@ -168,6 +170,8 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
     optional [T, E] float32 output of the logits routed on.  ``shared``:
     optional (gate_up tiles, gate_up tile scales, down tiles, down tile
     scales) of an MXFP8 shared expert (moe_mxfp8_prepack layout, uint8).
+    ``h_codes`` [T*k, I] / ``h_scales`` [T*k, I/32] uint8: optional copies of
+    h's MXFP8 encoding on the MXFP8 path, rows in expert-sorted order.
     """
     import torch
     if validate:
@@ -188,6 +192,10 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                 raise ValueError(f"{name}: expected {n} contiguous uint8 bytes, got "
                                  f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
         _expect(out, torch.bfloat16, (T, H), "out")
+        if h_codes is not None:
+            _expect(h_codes, torch.uint8, (T * top_k, I2 // 2), "h_codes")
+        if h_scales is not None:
+            _expect(h_scales, torch.uint8, (T * top_k, I2 // 64), "h_scales")
         if shared is not None:
             I = I2 // 2
             for t, n, name in ((shared[0], 2 * I * H, "shared[0]"), (shared[1], 2 * I * H // 32, "shared[1]"),
@@ -210,7 +218,7 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                             _ptr(offsets), _ptr(sorted), _ptr(x_codes), _ptr(x_scales),
                             ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
                             n_ev, weight_layout, launch, _ptr(wait_error), _ptr(router_weight),
-                            _ptr(logits_out), *sh)
+                            _ptr(logits_out), *sh, _ptr(h_codes), _ptr(h_scales))
     T = x.shape[0] if x is not None else 0
     rc = lib().moe_mxfp4_forward_ex(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,

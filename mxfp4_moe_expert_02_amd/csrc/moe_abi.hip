@@ -395,6 +395,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         {o.sorted, ws->sorted, (size_t)S * 4},
         {mx8 ? o.x_codes : nullptr, ws->x_codes, (size_t)T * H},
         {mx8 ? o.x_scales : nullptr, ws->x_scales, (size_t)T * (H / 32)},
+        {mx8 ? o.h_codes : nullptr, ws->h_codes, (size_t)S * I},
+        {mx8 ? o.h_scales : nullptr, ws->h_scales, (size_t)S * (I / 32)},
         {o.wait_error, ws->queue + moe::kQueueError, 4},
         {o.logits_out, router_logits, (size_t)T * E * 4},
     };

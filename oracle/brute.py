@@ -140,3 +140,52 @@ def forward(x_bf16: np.ndarray, logits: np.ndarray, k: int, H: int, I: int,
         if sh is not None:
             out[t] += _ffn(sh[0], sh[1], xt[0], I, act_mxfp8)
     return out
+
+
+def _silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    return np.array([gi / (1.0 + math.exp(-gi)) for gi in g]) * u
+
+
+def hidden_mxfp8_rows(x_bf16: np.ndarray, k: int, I: int,
+                      experts: Mapping[int, Sequence[np.ndarray]], ids: np.ndarray,
+                      sorted_slots: np.ndarray) -> np.ndarray:
+    """h of the MXFP8 path before its own MXFP8 encoding, in fp64, one row per
+    position p of the expert-sorted order: slot s = sorted_slots[p] = t*k + j
+    gives SiLU(Wg x_t) * (Wu x_t) of expert ids[t, j], x_t being the MXFP8
+    encoding of token t.  The encoding decision of h is then taken from these
+    values (by a caller)."""
+    xf = (x_bf16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gate_up = {}
+    rows = np.zeros((len(sorted_slots), I))
+    for p, s in enumerate(sorted_slots):
+        t, j = divmod(int(s), k)
+        e = int(ids[t, j])
+        if e not in gate_up:
+            gp, gs = experts[e][0], experts[e][1]
+            gate_up[e] = mxfp4_dequant(gp, gs)
+        xt = mxfp8_encode_values(xf[t:t + 1])[0][0]
+        w = gate_up[e]
+        rows[p] = _silu_mul(w[:I] @ xt, w[I:] @ xt)
+    return rows
+
+
+def down_from_h(h_codes: np.ndarray, h_scales: np.ndarray, k: int,
+                experts: Mapping[int, Sequence[np.ndarray]], ids: np.ndarray, w: np.ndarray,
+                pos: np.ndarray) -> np.ndarray:
+    """The rest of the layer on a given MXFP8 h (rows in expert-sorted order,
+    pos[t*k + j] = the row of slot t*k + j): out[t] = sum_j w[t, j] *
+    Wdown[ids[t, j]] @ dequant(h row pos[t*k + j]), in fp64, slots in order."""
+    T = ids.shape[0]
+    h = mxfp8_dequant(h_codes, h_scales)
+    down = {}
+    out = None
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e not in down:
+                down[e] = mxfp4_dequant(experts[e][2], experts[e][3])
+            term = w[t, j] * (down[e] @ h[int(pos[t * k + j])])
+            if out is None:
+                out = np.zeros((T, term.shape[0]))
+            out[t] += term
+    return out

@@ -76,6 +76,8 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, 
         if act == M.MOE_ACT_MXFP8:
             dbg["x_codes"] = torch.empty((c.T, c.H), dtype=torch.uint8, device="cuda")
             dbg["x_scales"] = torch.empty((c.T, c.H // 32), dtype=torch.uint8, device="cuda")
+            dbg["h_codes"] = torch.empty((S, c.I), dtype=torch.uint8, device="cuda")
+            dbg["h_scales"] = torch.empty((S, c.I // 32), dtype=torch.uint8, device="cuda")
     if launch == M.MOE_LAUNCH_FUSED:
         dbg["wait_error"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     extra = {}
@@ -116,3 +118,35 @@ def parity_ratio(gpu: np.ndarray, ref: np.ndarray) -> float:
     """max |gpu - ref| / rms(ref): the acceptance quantity (bar: <= 2e-2)."""
     rms = float(np.sqrt(np.mean(ref ** 2)))
     return float(np.abs(gpu - ref).max() / rms)
+
+
+def check_mxfp8_h(oracle, cfg: Config, x_bf16, experts, route, dbg, rel: float = 1e-4):
+    """The encoding decision of h on the MXFP8 path, taken from fp32 values on
+    the GPU and fp64 ones in the oracle, may differ where a value sits on a
+    decision boundary.  Checks that every difference is such a case -- a block
+    scale that differs only where the block's largest |h| is within `rel` of a
+    power of two, an element code that differs only where the GPU's code is a
+    nearest one up to rel * (block max) -- and returns the oracle's output
+    finished from the GPU's own h codes (fp64, [T, H])."""
+    from oracle import brute
+    rows = brute.hidden_mxfp8_rows(x_bf16, cfg.k, cfg.I, experts, route["ids"], route["sorted"])
+    codes, scales = oracle.quantize_mxfp8(rows)
+    hq, hs = dbg["h_codes"], dbg["h_scales"]
+    S, I = rows.shape
+    blocks = np.abs(rows).reshape(S, I // 32, 32).max(axis=2)
+    bad_scale = hs != scales
+    for p, b in zip(*np.nonzero(bad_scale)):
+        a = blocks[p, b]
+        assert abs(int(hs[p, b]) - int(scales[p, b])) == 1, (p, b)
+        assert a > 0 and abs(a / 2.0 ** np.round(np.log2(a)) - 1.0) <= rel, (p, b, a)
+    gpu_v = brute.mxfp8_dequant(hq, hs)
+    ora_v = brute.mxfp8_dequant(codes, scales)
+    same_scale = np.repeat(~bad_scale, 32, axis=1)
+    diff = (hq != codes) & same_scale
+    slack = 2 * rel * np.repeat(blocks, 32, axis=1)
+    d_gpu = np.abs(rows - gpu_v)
+    d_ora = np.abs(rows - ora_v)
+    assert np.all(d_gpu[diff] <= d_ora[diff] + slack[diff])
+    say(f"h codes: {int(diff.sum())} of {diff.size} differ at a boundary, "
+        f"{int(bad_scale.sum())} block scales")
+    return brute.down_from_h(hq, hs, cfg.k, experts, route["ids"], route["w"], route["pos"])

@@ -7,7 +7,10 @@ matrix cores) against the CPU oracle run with the same MXFP8 rule.
 * routing bit-exact (the prefill path groups 64 tokens per work item)
 * layer output: max |out - ref| <= 2e-2 * rms(ref); h is encoded from fp32
   on the GPU and from fp64 in the oracle, so a code of h may differ where
-  the value sits on a rounding boundary -- far below the bar
+  the value sits on a rounding boundary.  At the fixed shapes here that
+  stays within the bar; where one flipped code matters more (small I),
+  the seed sweep checks each difference and compares the output with the
+  oracle finished from the GPU's own h codes
 """
 import numpy as np
 import pytest

@@ -1,0 +1,97 @@
+"""GPU: the whole layer over a sweep of seeds, every path and launch form.
+
+Eight seeds, each with its own small shape (1 to 130 tokens, 8 to 32
+experts, top-1 to top-8; ragged token tiles, wide items where the experts
+average 8 or more tokens), each run through the C ABI on the VALU GEMV path,
+the automatic matrix-core launch (self-routed where it applies), the split
+launch, the single launch and the MXFP8 path.  On every case the routing
+(ids, counts, offsets, sorted order) equals the oracle's bit for bit, the weights agree
+within 1e-6, and every token's output is within the bar of the fp64 oracle.
+On the MXFP8 path the x codes are bit-exact; the codes of h are a decision
+taken on fp32 values, so every code that differs from the oracle's must sit
+on a rounding or scale boundary, and the output is compared with the oracle
+finished from the GPU's own h (the decision taken in the kernel's precision).
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_common import (bf16_tensor_to_f64, check_mxfp8_h, get_layer, oracle_experts,
+                              parity_ratio, run, say)
+from workloads import Config, bf16_bits_to_f32, make_logits, make_x_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+SHAPES = {  # seed: (T, E, k)
+    201: (3, 8, 2),
+    202: (16, 12, 3),
+    203: (37, 8, 2),
+    204: (64, 16, 4),    # wide items (T*k >= 8E)
+    205: (100, 12, 6),   # wide, experts with more than 64 tokens
+    206: (9, 16, 8),
+    207: (130, 32, 4),   # wide, ragged last tile
+    208: (1, 8, 1),
+}
+
+PATHS = {  # name: (gemm path, activation format, launch)
+    "gemv": (1, 0, 0),
+    "auto": (2, 0, 0),
+    "split": (2, 0, 1),
+    "fused": (2, 0, 2),
+    "mx8": (0, 1, 0),
+}
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    import mxfp4_moe_expert_02_amd as M
+    return M
+
+
+def bf16_to_f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _cfg(seed, act):
+    T, E, k = SHAPES[seed]
+    name = f"sweep_s{seed}_t{T}_e{E}_h256_i128_k{k}_{'mxfp8' if act else 'bf16'}"
+    return Config("sweep", name, T, E, 256, 128, k, "normal", "mxfp8" if act else "bf16", seed)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("seed", list(SHAPES))
+def test_seed_sweep_vs_oracle(M, oracle_lib, seed, path):
+    gemm, act, launch = PATHS[path]
+    cfg = _cfg(seed, act)
+    layer = get_layer(cfg)
+    dbg = run(M, layer, path=gemm, act=act, launch=launch, debug=True)
+    if launch == M.MOE_LAUNCH_FUSED:
+        assert int(dbg["wait_error"][0]) == 0
+    lg = make_logits(cfg)
+    r = oracle_lib.route(lg, cfg.k)
+    np.testing.assert_array_equal(dbg["ids"], r["ids"])
+    np.testing.assert_array_equal(dbg["counts"], r["counts"])
+    np.testing.assert_array_equal(dbg["offsets"], r["offsets"])
+    np.testing.assert_array_equal(dbg["sorted"], r["sorted"])
+    np.testing.assert_allclose(dbg["weights"], r["w"], rtol=0, atol=1e-6)
+    full = bf16_tensor_to_f64(layer.out)
+    assert np.isfinite(full).all()
+    ex = oracle_experts(oracle_lib, cfg, r["ids"].ravel())
+    x = make_x_bf16(cfg)
+    if act:
+        # the x codes are exact (bf16 in, exact arithmetic); h's codes are a
+        # decision on fp32 values, so the oracle checks them and then finishes
+        # the layer from the GPU's own h
+        xc, xs = oracle_lib.quantize_mxfp8(bf16_to_f64(x))
+        np.testing.assert_array_equal(dbg["x_codes"], xc)
+        np.testing.assert_array_equal(dbg["x_scales"], xs)
+        ref = check_mxfp8_h(oracle_lib, cfg, x, ex, r, dbg)
+    else:
+        ref = oracle_lib.forward(x, lg, cfg.k, cfg.H, cfg.I, ex)
+    ratio = parity_ratio(full, ref)
+    say(f"seed sweep {cfg.name} {path}: max|d|/rms = {ratio:.3e}")
+    assert ratio <= TOL
