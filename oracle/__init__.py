@@ -17,6 +17,10 @@ Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
   forward(shared=...) ......... pinned (brute.py on tiny shapes, an MXFP8
                                   copy of an MXFP4 expert gives the same
                                   result, closed forms, scale identities)
+  brute.hidden_mxfp8_rows /
+  brute.down_from_h ........... pinned (together they reproduce the C
+                                  oracle's whole MXFP8 layer; one h code
+                                  moves only its own token)
 """
 from __future__ import annotations
 
