@@ -195,6 +195,8 @@ def main():
         print("bench.py: MXFP8 activations run on the matrix cores only (--path 0 or 2)",
               file=sys.stderr)
         sys.exit(2)
+    lib_path = os.path.abspath(M.lib()._name)
+    print(f"[bench] library {lib_path}", file=sys.stderr, flush=True)
     print(f"[bench] building {cfg.name}", file=sys.stderr, flush=True)
     layer = build_layer(cfg)
     M.moe_mxfp4_init(cfg.T, cfg.E, cfg.H, cfg.I, cfg.k)
@@ -207,8 +209,8 @@ def main():
 
     launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
               "self": M.MOE_LAUNCH_SELF_ROUTED}[args.launch]
-    wide = cfg.T * cfg.k >= 8 * cfg.E  # the library's wide items (experts average >= 8 tokens)
-    self_ok = (path == M.MOE_PATH_MFMA and not mx8 and not wide and cfg.T <= 16
+    wide = cfg.T * cfg.k >= 4 * cfg.E  # the library's wide items (experts average >= 4 tokens)
+    self_ok = (path == M.MOE_PATH_MFMA and not mx8 and cfg.T * cfg.k < 8 * cfg.E and cfg.T <= 16
                and cfg.T * cfg.E <= 4096)
     self_routed = self_ok and launch in (M.MOE_LAUNCH_AUTO, M.MOE_LAUNCH_SELF_ROUTED)
 
@@ -310,7 +312,7 @@ def main():
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
     # the gate_up kernel the library runs for this layer (the wide bf16
-    # kernels when the experts average >= 8 tokens each; the self-routed one
+    # kernels when the experts average >= 4 tokens each; the self-routed one
     # for at most 16 tokens unless the split launch is asked for)
     kname = ("mx8_gate_up_kernel" if mx8 else
              "self_gate_up_kernel" if self_routed else
@@ -380,6 +382,7 @@ def main():
         "tflops": {"layer": round((gu_flops + dn_flops) / (ms_per_step * 1e-3) / 1e12, 2),
                    "gate_up": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
                    "down_combine": round(dn_flops / (dn_ms * 1e-3) / 1e12, 2)},
+        "library": lib_path,
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},

@@ -1,7 +1,10 @@
 // device_common.h -- small device helpers shared by the expert GEMM kernels.
 #pragma once
 
+#include <utility>
+
 #include "moe_internal.h"
+#include "mx_encode.h"
 
 namespace moe {
 
@@ -9,6 +12,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // 16-byte streaming load (expert weights are read exactly once)
 __device__ inline uint4 load_stream16(const uint8_t* p) {
@@ -65,13 +69,136 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Four bf16 of h through an agent-coherent 8-byte store: in the
-// single-launch layer the down unit that reads them may run on another XCD
-// in the same launch (its L2 never held these lines in this launch).
-__device__ inline void store_h4(uint16_t* dst, ushort4 v) {
-    const uint64_t u = (uint64_t)v.x | ((uint64_t)v.y << 16) | ((uint64_t)v.z << 32) |
-                       ((uint64_t)v.w << 48);
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (for builtin operands
+// that must be constants)
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One v_mfma_scale_f32_16x16x128_f8f6f4: A in format FA (4: FP4 E2M1, 0: FP8
+// E4M3), B FP8 E4M3; the scales are byte SA of sa and byte SB of sb (the
+// instruction's op_sel picks them, so packed scale dwords need no unpacking)
+template <int FA, int SA, int SB>
+__device__ inline f32x4_t mfma_scaled(const i32x8_t& A, const i32x8_t& B, const f32x4_t& c, uint32_t sa,
+                                      uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, FA, 0, SA, (int)sa, SB, (int)sb);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// v -> (hi, lo) = (bf16(v), bf16(v - hi)) (v - hi is exact in fp32); a
+// non-finite remainder (v infinite or NaN, or hi rounded to infinity) gives
+// lo = 0, so hi alone carries the special value.
+__device__ inline void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_rne(v);
+    const float d = v - bf16_to_f32(hi);
+    lo = __builtin_isfinite(d) ? f32_to_bf16_rne(d) : (uint16_t)0;
+}
+
+// ---- h between the GEMMs on the matrix-core paths with bf16 activations.
+// A single bf16 rounding of h costs up to 2^-9 relative per element, and
+// stacked on the bf16 rounding of out it can exceed the layer's error
+// budget.  So h is carried as three MXFP8 terms, h ~ t0 + t1 + t2: t0 is
+// an MXFP8 encoding of h (E4M3 elements, one E8M0 scale per block of 32),
+// t1 that of the remainder h - t0, t2 that of h - t0 - t1; each term leaves
+// at most 2^-4 of what it encodes, so the three hold h to about 2^-12
+// relative (8 times closer than bf16).  The down
+// GEMM then runs on the scaled FP4 x FP8 matrix cores: per 128-k chunk and
+// 16-row group, one v_mfma_scale_f32_16x16x128_f8f6f4 per term, the
+// weights' FP4 codes and E8M0 scales taken as they are (no decode).
+//
+// Layout of row r of h (I values): codes h3q + r * 3I, scales h3s + r * I/8.
+// The B operand of one scaled MFMA gives lane (c, g) the 32 codes of
+// k = 16g .. 16g+15 and 64+16g .. 64+16g+15 of the chunk, with the scale
+// of MX block g (see mxfp8.hip), so a chunk's codes are stored per lane:
+// [chunk][g][term][32 bytes] (96 contiguous bytes per lane and chunk), and
+// its scales as [chunk][block g][term 0, 1, 2, 0] (one dword per lane).
+constexpr int kHTerms = 3;
+
+// Encode, as three MXFP8 terms, the h values a lane holds for one token:
+// v[rg][i] = element 16*rg + 4*g + i of h block `blk` (elements 32*blk ..
+// 32*blk+31 of the row), the 32 values of the block spread over the lanes
+// (c, 0..3) of the 16x16 MFMA D layout, which agree on each term's scale
+// through two cross-lane maxima (every lane of the wave takes part; only
+// lanes with `live` store, and the four lanes of a block agree on it).
+// Each term's scale is 2^(floor(log2 amax) - 7), one above the OCP MX rule,
+// so the scaled values stay below 256 and v_cvt_scalef32_pk_fp8_f32 (two
+// values per instruction, rounding to nearest even, not saturating) never
+// overflows; the same instruction's inverse gives the rounded values for
+// the remainder.  A block holding a NaN or an infinity gets term 0 scale
+// 0xFF (NaN) and zero codes.  Agent-coherent stores: in the single-launch
+// layer the down unit that reads them may run on another XCD in the same
+// launch (its L2 never held these lines in this launch).
+__device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const float (&v)[2][4],
+                                bool live) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const int g = (threadIdx.x % kWave) / 16;
+    const int chunk = blk >> 2, b = blk & 3;
+    float r[2][4];
+#pragma unroll
+    for (int rg = 0; rg < 2; rg++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[rg][i] = v[rg][i];
+    uint32_t code[kHTerms][2] = {};
+    uint32_t scales = 0;
+    bool special = false;  // a NaN or an infinity in the block (seen by term 0 only)
+#pragma unroll
+    for (int tm = 0; tm < kHTerms; tm++) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int rg = 0; rg < 2; rg++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t mb = __float_as_uint(r[rg][i]) & 0x7fffffffu;
+                amax = mb > amax ? mb : amax;  // NaN bits order above every finite value
+            }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        if (tm == 0) special = amax >= 0x7f800000u;
+        const int se = special || amax == 0 ? -127 : min(floor_log2_bits(amax) - 7, 127);
+        scales |= (uint32_t)(se + 127) << (8 * tm);
+#pragma unroll
+        for (int rg = 0; rg < 2; rg++) {
+            float q[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) q[i] = special ? 0.f : ldexpf(r[rg][i], -se);
+            s16x2_t w = {0, 0};
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q[0], q[1], 1.0f, false);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q[2], q[3], 1.0f, true);
+            const uint32_t c = (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
+            code[tm][rg] = c;
+            if (tm + 1 < kHTerms) {
+                const f32x2_t d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+                const f32x2_t d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, true);
+                r[rg][0] -= ldexpf(d0[0], se);
+                r[rg][1] -= ldexpf(d0[1], se);
+                r[rg][2] -= ldexpf(d1[0], se);
+                r[rg][3] -= ldexpf(d1[1], se);
+            }
+        }
+    }
+    if (special) scales = 0xffu;  // term 0 NaN; codes are those of zeros
+    if (!live) return;
+    uint8_t* crow = a.h3q + row * 3 * a.I;
+#pragma unroll
+    for (int rg = 0; rg < 2; rg++) {
+        // elements 32b + 16rg + 4g .. +3 of the chunk: reader lane (2b + rg) % 4,
+        // bytes 16 * (b / 2) + 4g .. +3 of its 32-byte piece
+        uint8_t* p = crow + (chunk * 4 + ((2 * b + rg) & 3)) * 96 + (b >> 1) * 16 + 4 * g;
+#pragma unroll
+        for (int tm = 0; tm < kHTerms; tm++)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(p + 32 * tm), code[tm][rg], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (g == 0)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h3s + row * (a.I / 8) + (chunk * 4 + b) * 4), scales,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Spin (sleeping) until *count >= need, reading it agent-coherently.  Gives

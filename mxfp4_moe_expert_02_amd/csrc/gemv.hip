@@ -21,8 +21,9 @@
 //     scaled by 2^(s-127) (exact) into the fp32 accumulator.
 //   * The K-reduction across the 16 lanes is a DPP rotate butterfly
 //     (row_ror 8, 4, 2, 1), leaving the sum in every lane.
-// gate_up items also apply SiLU(gate) * up and store h in bf16; down items
-// store the per-assignment outputs y in fp32.
+// gate_up items also apply SiLU(gate) * up and store h as bf16 hi/lo pairs
+// (h2_pos); down items dot each weight pair with both halves and store the
+// per-assignment outputs y in fp32.
 #include "device_common.h"
 
 namespace moe {
@@ -41,8 +42,22 @@ __device__ inline float row16_sum(float v) {
     return v;
 }
 
+// h between the GEMMs of this path: each fp32 value v as the bf16 pair
+// (hi, lo) = (bf16(v), bf16(v - hi)) (split_bf16), which holds v to about
+// 2^-17 relative where one bf16 rounding costs up to 2^-9 and, stacked on
+// the bf16 rounding of out, can exceed the layer's error budget.  A row of
+// I values is 2I bf16: [chunk n/128][half (n/16)%2][block (n/32)%4][hi,
+// lo][16 values]; h2_pos(n) is the index of element n's hi, its lo 16 later.
+__device__ inline int h2_pos(int n) {
+    return (((n >> 7) * 2 + ((n >> 4) & 1)) * 4 + ((n >> 5) & 3)) * 32 + (n & 15);
+}
+
 // LDS position (in 16-byte units) of quarter q of block b of a token row
 __device__ inline int xs_unit(int b, int q) { return b * 4 + ((q + (b >> 1)) & 3); }
+// ... of an h row in hi/lo pairs (8 units per block: the four hi quarters,
+// then the four lo quarters, each group rotated as above); its lo quarter
+// sits 4 units after its hi quarter
+__device__ inline int hs_unit(int b, int q) { return b * 8 + ((q + (b >> 1)) & 3); }
 
 // Stage rows of bf16 activations into LDS: dst[t][...] for t < M, each row
 // K elements, taken from src + row_index(t) * ld.  16-byte granularity.
@@ -53,6 +68,21 @@ __device__ inline void stage_rows(uint4* __restrict__ xs, int M, int K, RowFn ro
         int t = i / units, u = i % units;
         const uint4* src = reinterpret_cast<const uint4*>(row_ptr(t));
         xs[t * units + xs_unit(u >> 2, u & 3)] = src[u];
+    }
+}
+
+// Stage h rows in the hi/lo layout (2K bf16 each, see h2_pos) into LDS at
+// the hs_unit positions: 16-byte unit u of a row holds quarter q = 2*hf +
+// (u & 1) of part (u >> 1) & 1 (hi, lo) of block 4*(u >> 5) + ((u >> 2) & 3),
+// hf = (u >> 4) & 1.
+template <typename RowFn>
+__device__ inline void stage_rows_h2(uint4* __restrict__ xs, int M, int K, RowFn row_ptr) {
+    const int units = K / 4;  // 16-byte units per row of 2K bf16
+    for (int i = threadIdx.x; i < M * units; i += blockDim.x) {
+        const int t = i / units, u = i % units;
+        const int b = 4 * (u >> 5) + ((u >> 2) & 3), q = 2 * ((u >> 4) & 1) + (u & 1);
+        const uint4* src = reinterpret_cast<const uint4*>(row_ptr(t));
+        xs[t * units + hs_unit(b, q) + 4 * ((u >> 1) & 1)] = src[u];
     }
 }
 
@@ -73,7 +103,9 @@ struct StepBuf {
     uint32_t s[kGemvUnroll][R];
 };
 
-template <int MT, int R, typename RowsFn>
+// HL: the activations are h rows in hi/lo pairs (stage_rows_h2); each
+// decoded weight pair is dotted with the hi pair, then the lo pair.
+template <int MT, int R, bool HL, typename RowsFn>
 struct RowGemv {
     RowsFn rows_of;      // rows_of(unit, rows[R], srows[R])
     int unit0, unit_step, n_units, n_iter, nblk, lane16;
@@ -122,9 +154,16 @@ struct RowGemv {
                 for (int t = 0; t < MT; t++) part[r][t] = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                uint4 xv[MT];
+                uint4 xv[MT], xl[MT];
 #pragma unroll
-                for (int t = 0; t < MT; t++) xv[t] = xs[t * units_per_tok + xs_unit(blk, q)];
+                for (int t = 0; t < MT; t++) {
+                    if constexpr (HL) {
+                        xv[t] = xs[t * units_per_tok + hs_unit(blk, q)];
+                        xl[t] = xs[t * units_per_tok + hs_unit(blk, q) + 4];
+                    } else {
+                        xv[t] = xs[t * units_per_tok + xs_unit(blk, q)];
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     const uint32_t word = (q == 0) ? b.w[j][r].x : (q == 1) ? b.w[j][r].y
@@ -141,6 +180,12 @@ struct RowGemv {
                         v = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(xv[t].y), v, false);
                         v = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(xv[t].z), v, false);
                         v = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(xv[t].w), v, false);
+                        if constexpr (HL) {
+                            v = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(xl[t].x), v, false);
+                            v = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(xl[t].y), v, false);
+                            v = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(xl[t].z), v, false);
+                            v = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(xl[t].w), v, false);
+                        }
                         part[r][t] = v;
                     }
                 }
@@ -158,8 +203,8 @@ struct RowGemv {
 // Run a RowGemv over its steps: first loads, then stage() (which must end
 // with a workgroup barrier), then the pipelined loop.  epi(unit, sums)
 // receives the reduced sums (valid in every lane of the 16) after each unit.
-template <int MT, int R, typename RowsFn, typename StageFn, typename EpiFn>
-__device__ void run_row_gemv(const RowGemv<MT, R, RowsFn>& g, const uint4* xs, int units_per_tok,
+template <int MT, int R, bool HL, typename RowsFn, typename StageFn, typename EpiFn>
+__device__ void run_row_gemv(const RowGemv<MT, R, HL, RowsFn>& g, const uint4* xs, int units_per_tok,
                              StageFn stage, EpiFn epi) {
     const int S = g.steps();
     StepBuf<R> A, B;
@@ -208,11 +253,11 @@ __device__ void gate_up_pass(const GemmArgs& a, int e, int tile, int off, int m,
         srows[0] = S + (int64_t)n * nblk;
         srows[1] = S + (int64_t)(a.I + n) * nblk;
     };
-    RowGemv<MT, 2, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
-                                        slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
-                                        (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
-                                            (kGemvLanesPerRow * kGemvUnroll),
-                                        nblk, lane16};
+    RowGemv<MT, 2, false, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
+                                               slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
+                                               (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
+                                                   (kGemvLanesPerRow * kGemvUnroll),
+                                               nblk, lane16};
     uint4* xs = dyn_lds;
     auto stage = [&]() {
         stage_rows(xs, m, K, [&](int t) {
@@ -225,8 +270,13 @@ __device__ void gate_up_pass(const GemmArgs& a, int e, int tile, int off, int m,
         const int n = n0 + u;
 #pragma unroll
         for (int t = 0; t < MT; t++)
-            if (lane16 == t && t < m)
-                a.h[(int64_t)(off + t) * a.I + n] = f32_to_bf16_rne(silu_mul(sums[0][t], sums[1][t]));
+            if (lane16 == t && t < m) {
+                uint16_t hi, lo;
+                split_bf16(silu_mul(sums[0][t], sums[1][t]), hi, lo);
+                uint16_t* row = a.h + (int64_t)(off + t) * 2 * a.I + h2_pos(n);
+                row[0] = hi;
+                row[16] = lo;
+            }
     };
     run_row_gemv(g, xs, units, stage, epi);
     (void)tok0;
@@ -249,14 +299,14 @@ __device__ void down_pass(const GemmArgs& a, int e, int tile, int off, int m) {
         srows[0] = S + (int64_t)n * nblk;
         srows[1] = S + (int64_t)(n + 1) * nblk;
     };
-    RowGemv<MT, 2, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
-                                        slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
-                                        (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
-                                            (kGemvLanesPerRow * kGemvUnroll),
-                                        nblk, lane16};
+    RowGemv<MT, 2, true, decltype(rows_of)> g{rows_of, slot, kGemvSlots,
+                                              slot < nu ? (nu - slot + kGemvSlots - 1) / kGemvSlots : 0,
+                                              (nblk + kGemvLanesPerRow * kGemvUnroll - 1) /
+                                                  (kGemvLanesPerRow * kGemvUnroll),
+                                              nblk, lane16};
     uint4* xs = dyn_lds;
     auto stage = [&]() {
-        stage_rows(xs, m, K, [&](int t) { return a.h + (int64_t)(off + t) * K; });
+        stage_rows_h2(xs, m, K, [&](int t) { return a.h + (int64_t)(off + t) * 2 * K; });
         __syncthreads();
     };
     auto epi = [&](int u, float (&sums)[2][MT]) {
@@ -271,7 +321,7 @@ __device__ void down_pass(const GemmArgs& a, int e, int tile, int off, int m) {
                                    bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
     };
-    run_row_gemv(g, xs, units, stage, epi);
+    run_row_gemv(g, xs, 2 * units, stage, epi);
 }
 
 // gate_up: blockIdx.x = slot * tg + tile over an upper bound of active
@@ -296,6 +346,12 @@ gemv_gate_up_kernel(GemmArgs a) {
     }
 }
 
+// Tokens per down pass: the staged h rows (hi/lo pairs, 4*I bytes each)
+// stay within 128 KB of LDS, so up to 4 tokens for I <= 8192 and 2 above.
+__host__ __device__ inline int gemv_down_tokens(int I) {
+    return (int64_t)kGemvMaxTok * I * 4 <= (128 << 10) ? kGemvMaxTok : 2;
+}
+
 // down: blockIdx.x = slot * td + tile; a tile is kColTile output columns.
 // After writing its rows of y, a block counts the tile done for each of its
 // tokens; the block whose count completes a token's k experts combines that
@@ -311,8 +367,9 @@ gemv_down_kernel(GemmArgs a) {
     if (slot >= uniform(a.meta[a.list_meta])) return;
     const int e = uniform(a.list[slot]);
     const int M = uniform(a.counts[e]), off = uniform(a.offsets[e]);
-    for (int t0 = 0; t0 < M; t0 += kGemvMaxTok) {
-        const int m = min(kGemvMaxTok, M - t0);
+    const int per = gemv_down_tokens(a.I);
+    for (int t0 = 0; t0 < M; t0 += per) {
+        const int m = min(per, M - t0);
         __syncthreads();
         switch (m) {
             case 1: down_pass<1>(a, e, tile, off + t0, m); break;
@@ -320,7 +377,11 @@ gemv_down_kernel(GemmArgs a) {
             case 3: down_pass<3>(a, e, tile, off + t0, m); break;
             default: down_pass<4>(a, e, tile, off + t0, m); break;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's y stores done
+        // every wave's y stores have completed before any of its tokens is
+        // counted: the combining workgroup may run on another XCD and read y
+        // as soon as the count completes (a workgroup-scope fence would not
+        // wait for them)
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
         if ((int)threadIdx.x < m) {
             const int token = a.sorted[off + t0 + threadIdx.x] / a.k;
@@ -345,7 +406,7 @@ hipError_t launch_gemv_gate_up(const GemmArgs& a, int max_active, hipStream_t st
 }
 
 hipError_t launch_gemv_down(const GemmArgs& a, int max_active, hipStream_t stream) {
-    const size_t lds = (size_t)kGemvMaxTok * a.I * 2;
+    const size_t lds = (size_t)gemv_down_tokens(a.I) * a.I * 4;  // h rows as hi/lo pairs
     gemv_down_kernel<<<max_active * a.col_tiles, kGemvThreads, lds, stream>>>(a);
     return hipGetLastError();
 }

@@ -45,18 +45,18 @@ namespace {
 // weights are then decoded once per 64 tokens), else 16.
 template <int NT, typename X>
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu)))
 shared_gate_up_kernel(GemmArgs a) {
     __shared__ f32x4_t red[kRedGateUp * NT];
     shared_gate_up_block<NT, X>(a, blockIdx.x, red);
 }
 
-template <int NT, typename X>
+template <int NT>
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu)))
 shared_down_kernel(GemmArgs a) {
     __shared__ f32x4_t red[kRedDown * NT];
-    shared_down_block<NT, X>(a, blockIdx.x, red);
+    shared_down_block<NT>(a, blockIdx.x, red);
 }
 
 // gate_up: blockIdx.x = item * quads + quad; quad q = gate rows 32q..32q+31
@@ -64,7 +64,7 @@ shared_down_kernel(GemmArgs a) {
 // up to kMfmaItemTok tokens (1..4 column tiles of 16); otherwise items of
 // at most 16 tokens, compiled without the wider cases (fewer registers).
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu)))
 mfma_gate_up_kernel(GemmArgs a) {
     __shared__ f32x4_t red[kRedGateUp];
     const int quads = a.I / 32;
@@ -90,7 +90,7 @@ mfma_gate_up_kernel(GemmArgs a) {
 // pair.  The wave holding a quad's summed accumulator writes its y rows;
 // the combine kernel reads them after this kernel.
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(3)))
 mfma_down_kernel(GemmArgs a) {
     __shared__ f32x4_t red[kRedDown];
     const int quads = a.H / 64, pairs = (quads + 1) / 2;
@@ -98,7 +98,7 @@ mfma_down_kernel(GemmArgs a) {
     if (a.sh_wdn) {  // the shared expert's blocks first (16-token tiles)
         const int nb = shared_blocks(pairs, (a.T + 15) / 16);
         if (b < nb) {
-            shared_down_block<1, XB>(a, b, red);
+            shared_down_block<1>(a, b, red);
             return;
         }
         b -= nb;
@@ -107,7 +107,7 @@ mfma_down_kernel(GemmArgs a) {
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    down_item<1, false, W4, XB>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
+    down_item<1, false, W4>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
                                 a.sdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 256,
                                 SortedRows{row0, m}, red);
 }
@@ -156,7 +156,7 @@ struct SelfRows<false> {
 // expert e, for the tokens that chose e, h rows by slot.
 template <bool LISTS>
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu)))
 self_gate_up_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16)))
     float smem[kSelfLdsFloats > 4 * kRedGateUp ? kSelfLdsFloats : 4 * kRedGateUp];
@@ -193,14 +193,14 @@ self_gate_up_kernel(GemmArgs a) {
 // sh_row0 + t).
 template <bool LISTS>
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(LISTS ? 3 : 2)))
 self_down_kernel(GemmArgs a) {
     __shared__ f32x4_t red[kRedDown];
     const int pairs = (a.H / 64 + 1) / 2;
     int b = blockIdx.x;
     if (a.sh_wdn) {  // the shared expert's quad pairs first
         if (b < pairs) {
-            down_item<1, false, W8, XB>(a, b, a.sh_wdn, a.sh_sdn, TokenRows{0, a.T, a.sh_row0}, red);
+            down_item<1, false, W8P>(a, b, a.sh_wdn, a.sh_sdn, TokenRows{0, a.T, a.sh_row0}, red);
             return;
         }
         b -= pairs;
@@ -208,13 +208,11 @@ self_down_kernel(GemmArgs a) {
     const int e = b / pairs, pair = b % pairs;
     const auto rows = SelfRows<LISTS>::get(a, e);
     if (rows.m == 0) return;
-    down_item<1, false, W4, XB>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
+    down_item<1, false, W4>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
                                 a.sdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 256, rows, red);
 }
 
-#ifndef MOE_FUSED_WAVES_PER_EU
-#define MOE_FUSED_WAVES_PER_EU 2
-#endif
+constexpr int kFusedWavesPerEu = 2;  // launch bound of the single-launch kernel
 
 // The expert layer after routing in one persistent launch: every workgroup
 // dequeues units from one counter, first the gate_up units (item, quad),
@@ -235,7 +233,7 @@ self_down_kernel(GemmArgs a) {
 // block anyone: a workgroup holds a gate_up unit only while running a
 // gate_up unit, which never waits.
 __global__ void __launch_bounds__(kMfmaThreads)
-__attribute__((amdgpu_waves_per_eu(MOE_FUSED_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kFusedWavesPerEu)))
 mfma_fused_kernel(GemmArgs a) {
     __shared__ f32x4_t red[2][kRedGateUp];
     __shared__ int s_unit[2];
@@ -266,7 +264,7 @@ mfma_fused_kernel(GemmArgs a) {
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
             const int64_t e = uniform(it.x);
-            down_item<1, true, W4, XB>(a, v % dn_units, a.wdn + e * (a.H / 64) * (a.I / 128) * 4096,
+            down_item<1, true, W4>(a, v % dn_units, a.wdn + e * (a.H / 64) * (a.I / 128) * 4096,
                                        a.sdn + e * (a.H / 64) * (a.I / 128) * 256,
                                        SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
         }
@@ -288,14 +286,16 @@ hipError_t launch_shared_gate_up(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// down reads h as hi/lo pairs (twice the B operand of gate_up), so its
+// wide tiles are 32 tokens: four 16-token tiles would spill
 hipError_t launch_shared_down(const GemmArgs& a, hipStream_t stream) {
     const bool wide = a.T >= kSharedWideTok;
-    const int tok = wide ? kSharedWideTok : 16;
+    const int tok = wide ? 32 : 16;
     const int grid = shared_blocks((a.H / 64 + 1) / 2, (a.T + tok - 1) / tok);
     if (wide)
-        shared_down_kernel<4, XB><<<grid, kMfmaThreads, 0, stream>>>(a);
+        shared_down_kernel<2><<<grid, kMfmaThreads, 0, stream>>>(a);
     else
-        shared_down_kernel<1, XB><<<grid, kMfmaThreads, 0, stream>>>(a);
+        shared_down_kernel<1><<<grid, kMfmaThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

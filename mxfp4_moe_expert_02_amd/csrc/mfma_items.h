@@ -11,15 +11,9 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_MFMA_CHUNKS_PER_STEP
-#define MOE_MFMA_CHUNKS_PER_STEP 2
-#endif
-#ifndef MOE_MFMA_WAVES_PER_EU
-#define MOE_MFMA_WAVES_PER_EU 2
-#endif
-
+constexpr int kMfmaWavesPerEu = 2;            // launch bound: at least 2 waves per SIMD
 constexpr int kWaves = kMfmaThreads / kWave;  // 4, split K
-constexpr int kChunksPerStep = MOE_MFMA_CHUNKS_PER_STEP;  // 128-column chunks per prefetch step
+constexpr int kChunksPerStep = 2;             // 128-column chunks per prefetch step
 constexpr int kGroups = 4;                    // 16-row groups per quad
 
 // ---- weight formats of the tile layout (one 64-row quad, one 128-k chunk)
@@ -45,6 +39,41 @@ struct W4 {
     static __device__ bf16x8_t a(const Chunk& b, int rg, int q) {
         return decode8(word_of(b.w[rg], q), e8m0_as_scale((b.s >> (8 * rg)) & 0xffu));
     }
+    // as the A operand of the scaled FP4 x FP8 matrix cores: the lane's 32
+    // codes as they are (format 4 = FP4 E2M1); byte rg of s is its block scale
+    static constexpr int kFmt = 4;
+    static __device__ i32x8_t sop(const Chunk& b, int rg) {
+        const uint4& w = b.w[rg];
+        return i32x8_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    }
+};
+// W8P: MXFP8 weights (the MXFP8 tile layout) as the A operand of the scaled
+// matrix cores: an 8-bit A operand gives lane (r, g) the 16-byte pieces g
+// and g + 4 of row r's 128 codes, with the scale of MX block g (the pairing
+// of the B operand); in the MXFP8 tile layout piece p of row r sits in half
+// p % 2 of lane r + 16 (p / 2), so the lane loads those two 16-byte pieces.
+struct W8P {
+    static constexpr int kChunkBytes = 8192;
+    static constexpr int kFmt = 0;  // FP8 E4M3
+    struct Chunk {
+        uint4 w[kGroups][2];
+        uint32_t s;
+    };
+    static __device__ void load(const uint8_t* tiles, const uint8_t* tscales, int ci, Chunk& b) {
+        const int lane = threadIdx.x % kWave, r = lane % 16, g = lane / 16;
+        const uint8_t* t = tiles + (int64_t)ci * kChunkBytes + (g & 1) * 1024 + (r + 16 * (g >> 1)) * 16;
+#pragma unroll
+        for (int rg = 0; rg < kGroups; rg++) {
+            b.w[rg][0] = load_stream16(t + rg * 2048);        // piece g
+            b.w[rg][1] = load_stream16(t + rg * 2048 + 512);  // piece g + 4: lane r + 16 (g / 2 + 2)
+        }
+        b.s = *reinterpret_cast<const uint32_t*>(tscales + (int64_t)ci * 256 + lane * 4);
+    }
+    static __device__ i32x8_t sop(const Chunk& b, int rg) {
+        const uint4& lo = b.w[rg][0];
+        const uint4& hi = b.w[rg][1];
+        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
 };
 struct W8 {
     static constexpr int kChunkBytes = 8192;
@@ -69,10 +98,13 @@ struct W8 {
 };
 
 // ---- the activation format of the B operand (one token row, 128-k
-// chunk): lane (c, g) takes block g of the chunk; b(x, q) is the bf16 B
-// operand of step q (elements 8q..8q+7 of the block).  XB: bf16 rows;
-// row(a, token) is a token's x row, hrow(a, r) row r of h.
+// chunk).  XB: bf16 rows of x (row(a, token)); lane (c, g) takes block g of
+// the chunk and b(x, q) is the bf16 B operand of step q (elements
+// 8q..8q+7 of the block).  XQ3: rows of h as three MXFP8 terms (store_h3,
+// hrow(a, r)) for the scaled matrix cores; term(x, tm) is lane (c, g)'s
+// 32 codes of term tm and byte tm of its s the block scale.
 struct XB {
+    static constexpr bool kScaled = false;
     struct Row {
         const uint16_t* p;
     };
@@ -80,7 +112,6 @@ struct XB {
         uint4 x[4];
     };
     static __device__ Row row(const GemmArgs& a, int t) { return Row{a.x + (int64_t)t * a.H}; }
-    static __device__ Row hrow(const GemmArgs& a, int r) { return Row{a.h + (int64_t)r * a.I}; }
     static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
         const uint4* src = reinterpret_cast<const uint4*>(r.p + (int64_t)(4 * chunk + g) * 32);
 #pragma unroll
@@ -88,17 +119,38 @@ struct XB {
     }
     static __device__ bf16x8_t b(const Chunk& c, int q) { return __builtin_bit_cast(bf16x8_t, c.x[q]); }
 };
-// chunks per prefetch step: MXFP4 single-tile items kChunksPerStep, wider
-// ones one (their x operands alone fill 16 VGPRs per tile and chunk);
-// MXFP8 weights one (a chunk is already twice the bytes)
-#ifndef MOE_MFMA_WIDE_CPS
-#define MOE_MFMA_WIDE_CPS 1
-#endif
-
-template <int NT, typename W>
+struct XQ3 {
+    static constexpr bool kScaled = true;
+    struct Row {
+        const uint8_t* q;  // codes of the row
+        const uint8_t* s;  // scales of the row
+    };
+    struct Chunk {
+        uint4 x[2 * kHTerms];
+        uint32_t s;
+    };
+    static __device__ Row hrow(const GemmArgs& a, int r) {
+        return Row{a.h3q + (int64_t)r * 3 * a.I, a.h3s + (int64_t)r * (a.I / 8)};
+    }
+    static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
+        const uint4* src = reinterpret_cast<const uint4*>(r.q + (chunk * 4 + g) * 96);
+#pragma unroll
+        for (int i = 0; i < 2 * kHTerms; i++) c.x[i] = src[i];
+        c.s = *reinterpret_cast<const uint32_t*>(r.s + (chunk * 4 + g) * 4);
+    }
+    static __device__ i32x8_t term(const Chunk& c, int tm) {
+        const uint4& lo = c.x[2 * tm];
+        const uint4& hi = c.x[2 * tm + 1];
+        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+};
+// chunks per prefetch step: MXFP4 weights against one column tile
+// kChunksPerStep; wider items one (their B operands alone fill 16 or 25
+// VGPRs per tile and chunk); MXFP8 weights one (a chunk is already twice
+// the bytes)
+template <int NT, typename W, typename X>
 struct Cps {
-    static constexpr int value =
-        W::kChunkBytes != 4096 ? 1 : NT == 1 ? kChunksPerStep : NT == 2 ? MOE_MFMA_WIDE_CPS : 1;
+    static constexpr int value = W::kChunkBytes != 4096 || NT != 1 ? 1 : kChunksPerStep;
 };
 
 template <typename W, int CPS>
@@ -130,7 +182,7 @@ struct XStep {
 template <int NT, typename W, typename X, typename RowsFn>
 __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, RowsFn rows_of,
                                  int c_begin, int c_end, f32x4_t (&acc)[kGroups][NT]) {
-    constexpr int CPS = Cps<NT, W>::value;
+    constexpr int CPS = Cps<NT, W, X>::value;
     const int lane = threadIdx.x % kWave, g = lane / 16;
     typename X::Row xrow[NT];
 #pragma unroll
@@ -153,15 +205,29 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
 #pragma unroll
         for (int i = 0; i < CPS; i++) {
             if (c0 + i >= c_end) break;  // the repeated chunk of a partial step
+            if constexpr (X::kScaled) {  // one scaled MFMA per group, tile and term
+                // terms outermost: consecutive MFMAs go to different accumulators
+                static_for<kHTerms>([&](auto tm) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
+                    for (int t = 0; t < NT; t++) {
+                        const i32x8_t B = X::term(xb.x[i][t], tm);
+                        static_for<kGroups>([&](auto rg) {
+                            acc[rg][t] = mfma_scaled<W::kFmt, rg, tm>(W::sop(b.c[i], rg), B, acc[rg][t],
+                                                                      b.c[i].s, xb.x[i][t].s);
+                        });
+                    }
+                });
+            } else {
 #pragma unroll
-                for (int rg = 0; rg < kGroups; rg++) {
-                    const bf16x8_t A = W::a(b.c[i], rg, q);
+                for (int q = 0; q < 4; q++) {
 #pragma unroll
-                    for (int t = 0; t < NT; t++)
-                        acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, X::b(xb.x[i][t], q),
-                                                                             acc[rg][t], 0, 0, 0);
+                    for (int rg = 0; rg < kGroups; rg++) {
+                        const bf16x8_t A = W::a(b.c[i], rg, q);
+#pragma unroll
+                        for (int t = 0; t < NT; t++)
+                            acc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, X::b(xb.x[i][t], q),
+                                                                                 acc[rg][t], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -233,13 +299,34 @@ __device__ inline void wave_chunk_range(int chunks, int& c_begin, int& c_end) {
 constexpr int kRedGateUp = (kWaves - 1) * kGroups * kWave;
 constexpr int kRedDown = 2 * kGroups * kWave;
 
+// The SiLU(gate) * up epilogue of a gate_up quad: acc[rg][t] of lane
+// (c, g) holds rows 4g..4g+3 of group rg for token row 16t + c; groups 0, 1
+// are gate rows 32*quad + 16*rg + 4g + i, groups 2, 3 the matching up rows,
+// so the lane forms h elements 32*quad + 16*rg + 4g .. +3 of its token's h
+// row (rows.row), h block `quad`, stored as three MXFP8 terms.
+template <int NT, typename Rows>
+__device__ inline void store_h_tile(const GemmArgs& a, int quad, const Rows& rows,
+                                    const f32x4_t (&acc)[kGroups][NT]) {
+    const int c = threadIdx.x % 16;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int j = 16 * t + c;
+        float v[2][4];
+#pragma unroll
+        for (int rg = 0; rg < 2; rg++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[rg][i] = silu_mul(acc[rg][t][i], acc[rg + 2][t][i]);
+        store_h3(a, rows.row(min(j, rows.m - 1)), quad, v, j < rows.m);
+    }
+}
+
 // gate_up body for items of NT column tiles, token rows from `rows`
 // (SortedRows, SlotRows, ListRows or TokenRows); gu/gus: the expert's
-// gate_up tiles (format W), x and h in format X.
+// gate_up tiles (format W), x in format X; h goes out as hi/lo pairs.
 template <int NT, typename W, typename X, typename Rows>
 __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* gu,
                                     const uint8_t* gus, const Rows& rows, f32x4_t* red) {
-    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+    const int c = threadIdx.x % 16;
     const int m = rows.m;
     const int chunks = a.H / 128;
     int cb, ce;
@@ -255,27 +342,14 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* 
                         cb, ce, acc);
     reduce_waves<NT>(acc, red);
     if (threadIdx.x >= kWave) return;
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int j = 16 * t + c;
-        if (j >= m) continue;
-        uint16_t* hrow = a.h + (int64_t)rows.row(j) * a.I + 32 * quad + 4 * g;
-#pragma unroll
-        for (int rg = 0; rg < 2; rg++) {
-            ushort4 o;
-            o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
-            o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
-            o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
-            o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
-            store_h4(hrow + 16 * rg, o);
-        }
-    }
+    store_h_tile<NT>(a, quad, rows, acc);
 }
 
 // down body for items of NT column tiles (see mfma_down_kernel), token rows
-// from `rows`; dn/dns: the expert's down tiles (format W), h in format X;
+// from `rows`; dn/dns: the expert's down tiles (format W: W4, or W8P for
+// MXFP8 weights), h as three MXFP8 terms on the scaled matrix cores (XQ3);
 // COMBINE: see store_down_tile
-template <int NT, bool COMBINE, typename W, typename X, typename Rows>
+template <int NT, bool COMBINE, typename W, typename Rows>
 __device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
                                  const uint8_t* dns, const Rows& rows, f32x4_t* red) {
     const int m = rows.m;
@@ -288,12 +362,12 @@ __device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
     f32x4_t acc[kGroups][NT];
     if (live) {
         const int hc = (chunks + 1) / 2;
-        mfma_quad<NT, W, X>(dn + (int64_t)quad * chunks * W::kChunkBytes,
-                            dns + (int64_t)quad * chunks * 256,
-                            [&](typename X::Row (&xrow)[NT]) {
+        mfma_quad<NT, W, XQ3>(dn + (int64_t)quad * chunks * W::kChunkBytes,
+                              dns + (int64_t)quad * chunks * 256,
+                              [&](XQ3::Row (&xrow)[NT]) {
 #pragma unroll
-                                for (int t = 0; t < NT; t++)
-                                    xrow[t] = X::hrow(a, rows.row(min(16 * t + c, m - 1)));
+                                  for (int t = 0; t < NT; t++)
+                                      xrow[t] = XQ3::hrow(a, rows.row(min(16 * t + c, m - 1)));
                             },
                             half ? hc : 0, half ? chunks : hc, acc);
         if (half) {
@@ -345,14 +419,14 @@ __device__ inline void shared_gate_up_block(const GemmArgs& a, int b, f32x4_t* r
                             red);
 }
 
-template <int NT, typename X>
+template <int NT>
 __device__ inline void shared_down_block(const GemmArgs& a, int b, f32x4_t* red) {
     const int tok = 16 * NT;
     int pair, tile;
     if (!shared_unit(b, (a.H / 64 + 1) / 2, (a.T + tok - 1) / tok, pair, tile)) return;
     const int t0 = tok * tile;
-    down_item<NT, false, W8, X>(a, pair, a.sh_wdn, a.sh_sdn,
-                                TokenRows{t0, min(tok, a.T - t0), a.sh_row0}, red);
+    down_item<NT, false, W8P>(a, pair, a.sh_wdn, a.sh_sdn, TokenRows{t0, min(tok, a.T - t0), a.sh_row0},
+                              red);
 }
 
 }  // namespace

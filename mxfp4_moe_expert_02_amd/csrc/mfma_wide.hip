@@ -20,15 +20,14 @@
 // unconditional loads (rows past the item repeat its last token: they only
 // feed output columns that are never stored).  No cross-wave reduction is
 // needed: each wave ends with its quad's complete sums.
+#include <type_traits>
+
 #include "mfma_items.h"
 
 namespace moe {
 namespace {
 
-#ifndef MOE_WIDE_WAVES_PER_EU
-#define MOE_WIDE_WAVES_PER_EU 2
-#endif
-
+constexpr int kWideWavesPerEu = 2;  // launch bound: at least 2 waves per SIMD
 constexpr int kWThreads = 256;
 constexpr int kWQuads = 4;                     // quads per workgroup (one per wave)
 constexpr int kWMaxTiles = kMfmaItemTok / 16;  // 4
@@ -138,9 +137,126 @@ __device__ inline void wide_mainloop(const uint8_t* tiles, const uint8_t* tscale
     }
 }
 
+// ---- the down GEMM: B is h as three MXFP8 terms (store_h3), on the scaled
+// FP4 x FP8 matrix cores.  Per chunk a staged token row is 400 bytes of LDS:
+// the chunk's 384 code bytes ([g][term][32], as stored) and its 16 scale
+// bytes ([g][term]); at that stride a quarter-wave's 16-byte reads of 16
+// rows cover all 64 banks once.  Each staged row (16 NT rows, or 64 for
+// NT = 3) is copied by kTpr threads, thread (n, l) = (tid / kTpr, tid %
+// kTpr) taking 16-byte units l, l + kTpr, ... of its 25: units 0..23 are
+// code bytes, unit 24 the scales; a thread's last unit past 24 loads the
+// scales again and is not stored.  Rows past the item's m tokens repeat
+// row m - 1 (they only feed output columns that are never stored).  The
+// loads are issued at the start of a step and written to the other buffer
+// after its MFMAs.
+constexpr int kQRow = 400;
+constexpr int kQUnits = kQRow / 16;  // 24 code units, then 1 scale unit
+
+struct WQSmem {
+    alignas(16) uint8_t q[2][kWMaxTiles * 16 * kQRow];
+};
+
+template <int NT>
+struct QStage {
+    static constexpr int kTpr = NT == 1 ? 16 : NT == 2 ? 8 : 4;  // threads per staged row
+    static constexpr int kPer = (kQUnits + kTpr - 1) / kTpr;      // units per thread
+    const uint8_t* q;   // chunk 0 of this thread's first code unit
+    const uint8_t* sc;  // chunk 0 of its row's scales
+    uint4 v[kPer];
+};
+
+template <int NT>
+__device__ inline void q_stage_init(const GemmArgs& a, int row0, int m, QStage<NT>& st) {
+    constexpr int kTpr = QStage<NT>::kTpr;
+    const int n = threadIdx.x / kTpr, l = threadIdx.x % kTpr;
+    const int64_t r = row0 + min(n, m - 1);
+    st.q = a.h3q + r * 3 * a.I + 16 * l;
+    st.sc = a.h3s + r * (a.I / 8);
+}
+
+template <int NT>
+__device__ inline void q_load(QStage<NT>& st, int chunk) {
+    constexpr int kTpr = QStage<NT>::kTpr, kPer = QStage<NT>::kPer;
+    const int l = threadIdx.x % kTpr;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        const uint8_t* p = st.q + chunk * 384 + 16 * kTpr * i;
+        if (i == kPer - 1 && l + kTpr * i >= kQUnits - 1) p = st.sc + chunk * 16;
+        st.v[i] = *reinterpret_cast<const uint4*>(p);
+    }
+}
+
+template <int NT>
+__device__ inline void q_store(WQSmem& sm, int buf, const QStage<NT>& st) {
+    constexpr int kTpr = QStage<NT>::kTpr, kPer = QStage<NT>::kPer;
+    const int n = threadIdx.x / kTpr, l = threadIdx.x % kTpr;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        const int u = l + kTpr * i;
+        if (u < kQUnits) *reinterpret_cast<uint4*>(&sm.q[buf][n * kQRow + 16 * u]) = st.v[i];
+    }
+}
+
+// The 12*NT scaled MFMAs of one chunk: weights b (this wave's quad, FP4
+// codes and scales as they are), h's terms from LDS buffer `buf`.
+template <int NT>
+__device__ inline void chunk_mfma_q3(const WQSmem& sm, int buf, const WChunk& b,
+                                     f32x4_t (&acc)[kGroups][NT]) {
+    const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const uint8_t* row = &sm.q[buf][(16 * t + c) * kQRow];
+        const uint32_t sb = *reinterpret_cast<const uint32_t*>(row + 384 + 4 * g);
+        static_for<kHTerms>([&](auto tm) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(row + 96 * g + 32 * tm);
+            const uint4 hi = *reinterpret_cast<const uint4*>(row + 96 * g + 32 * tm + 16);
+            const i32x8_t B = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            static_for<kGroups>([&](auto rg) {
+                const uint4& w = b.w[rg];
+                const i32x8_t A = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+                // scale bytes: rg of the lane's weight scales, tm of its h scales
+                acc[rg][t] = mfma_scaled<4, rg, tm>(A, B, acc[rg][t], b.s, sb);
+            });
+        });
+    }
+}
+
+// Main loop of the down GEMM over all `chunks` chunks: chunk s + 1's h is
+// staged and its weights loaded while chunk s is computed (weights in the
+// buffer chunk s - 1 left), as in wide_mainloop.
+template <int NT>
+__device__ inline void wide_mainloop_q3(const GemmArgs& a, const uint8_t* tiles, const uint8_t* tscales,
+                                        bool live, int row0, int m, int chunks, WQSmem& sm,
+                                        f32x4_t (&acc)[kGroups][NT]) {
+#pragma unroll
+    for (int rg = 0; rg < kGroups; rg++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    QStage<NT> st;
+    q_stage_init<NT>(a, row0, m, st);
+    q_load<NT>(st, 0);
+    WChunk w[2];
+    if (live) load_chunk(tiles, tscales, 0, w[0]);
+    q_store<NT>(sm, 0, st);
+    __syncthreads();
+    auto step = [&](int s, WChunk& cur, WChunk& ahead) {
+        q_load<NT>(st, s + 1 < chunks ? s + 1 : s);
+        if (live && s + 1 < chunks) load_chunk(tiles, tscales, s + 1, ahead);
+        if (live) chunk_mfma_q3<NT>(sm, s & 1, cur, acc);
+        q_store<NT>(sm, (s & 1) ^ 1, st);
+        __syncthreads();
+    };
+    for (int s0 = 0; s0 < chunks; s0 += 2) {
+        step(s0, w[0], w[1]);
+        if (s0 + 1 >= chunks) break;
+        step(s0 + 1, w[1], w[0]);
+    }
+}
+
 template <int NT>
 __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, c = lane % 16, g = lane / 16;
+    const int tid = threadIdx.x, w = tid / kWave;
     const int K = a.H, chunks = K / 128, quads = a.I / 32;
     const int quad = kWQuads * qb + w;  // quads % 4 == 0: always live
     const int64_t quad_id = (int64_t)e * quads + quad;
@@ -153,45 +269,37 @@ __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, 
     f32x4_t acc[kGroups][NT];
     wide_mainloop<NT>(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, true, rows,
                       chunks, sm, acc);
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int j = 16 * t + c;
-        if (j >= m) continue;
-        uint16_t* hrow = a.h + (int64_t)(row0 + j) * a.I + 32 * quad + 4 * g;
-#pragma unroll
-        for (int rg = 0; rg < 2; rg++) {
-            ushort4 o;
-            o.x = f32_to_bf16_rne(silu_mul(acc[rg][t][0], acc[rg + 2][t][0]));
-            o.y = f32_to_bf16_rne(silu_mul(acc[rg][t][1], acc[rg + 2][t][1]));
-            o.z = f32_to_bf16_rne(silu_mul(acc[rg][t][2], acc[rg + 2][t][2]));
-            o.w = f32_to_bf16_rne(silu_mul(acc[rg][t][3], acc[rg + 2][t][3]));
-            store_h4(hrow + 16 * rg, o);
-        }
-    }
+    store_h_tile<NT>(a, quad, SortedRows{row0, m}, acc);
 }
 
 template <int NT, bool COMBINE>
-__device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
-    const int tid = threadIdx.x, w = tid / kWave;
-    const int K = a.I, chunks = K / 128, quads = a.H / 64;
+__device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int m, WQSmem& sm) {
+    const int w = threadIdx.x / kWave;
+    const int chunks = a.I / 128, quads = a.H / 64;
     const int quad = kWQuads * qb + w;
     const bool live = quad < quads;
     const int64_t quad_id = (int64_t)e * quads + (live ? quad : 0);
-    const uint16_t* rows[NT];
-#pragma unroll
-    for (int n = 0; n < NT; n++) {
-        const int j = min(16 * n + tid / 16, m - 1);
-        rows[n] = a.h + (int64_t)(row0 + j) * K + 8 * (tid % 16);
-    }
     f32x4_t acc[kGroups][NT];
-    wide_mainloop<NT>(a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
-                      chunks, sm, acc);
+    wide_mainloop_q3<NT>(a, a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, row0,
+                         m, chunks, sm, acc);
     if (!live) return;
     store_down_tile<NT, COMBINE>(a, quad, SortedRows{row0, m}, acc);
 }
 
+// Call fn(std::integral_constant<int, NT>) for an item of m tokens: NT =
+// its 16-token column tiles (1..4).
+template <typename Fn>
+__device__ inline void by_tiles(int m, Fn fn) {
+    switch ((m + 15) / 16) {
+        case 1: fn(std::integral_constant<int, 1>{}); break;
+        case 2: fn(std::integral_constant<int, 2>{}); break;
+        case 3: fn(std::integral_constant<int, 3>{}); break;
+        default: fn(std::integral_constant<int, 4>{}); break;
+    }
+}
+
 // gate_up: blockIdx.x = item * (I / 128) + quad block (quads 4qb..4qb+3)
-__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_gate_up_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_gate_up_kernel(GemmArgs a) {
     __shared__ WSmem sm;
     static_assert(sizeof(WSmem) >= sizeof(f32x4_t) * kRedGateUp * 2, "LDS of the shared blocks");
     const int qblocks = a.I / 128;
@@ -208,29 +316,19 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_gate_up
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    switch ((m + 15) / 16) {
-        case 1: wide_gate_up<1>(a, qb, e, row0, m, sm); break;
-#if MOE_WIDE_ITEM_TOK > 32
-        case 2: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
-        case 3: wide_gate_up<3>(a, qb, e, row0, m, sm); break;
-        default: wide_gate_up<4>(a, qb, e, row0, m, sm); break;
-#else
-        default: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
-#endif
-    }
+    by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value>(a, qb, e, row0, m, sm); });
 }
 
-// down: blockIdx.x = item * ceil(H / 256) + quad block; a quad is also the
-// combine tile (the last finisher of a token's k experts combines it)
-__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_kernel(GemmArgs a) {
-    __shared__ WSmem sm;
-    static_assert(sizeof(WSmem) >= sizeof(f32x4_t) * kRedDown * 2, "LDS of the shared blocks");
+// down: blockIdx.x = item * ceil(H / 256) + quad block
+__global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_down_kernel(GemmArgs a) {
+    __shared__ WQSmem sm;
+    static_assert(sizeof(WQSmem) >= sizeof(f32x4_t) * kRedDown, "LDS of the shared blocks");
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
     int b = blockIdx.x;
-    if (a.sh_wdn) {  // the shared expert's blocks first
-        const int nb = shared_blocks((a.H / 64 + 1) / 2, (a.T + 31) / 32);
+    if (a.sh_wdn) {  // the shared expert's blocks first (16-token tiles, split-K)
+        const int nb = shared_blocks((a.H / 64 + 1) / 2, (a.T + 15) / 16);
         if (b < nb) {
-            shared_down_block<2, XB>(a, b, reinterpret_cast<f32x4_t*>(&sm));
+            shared_down_block<1>(a, b, reinterpret_cast<f32x4_t*>(&sm));
             return;
         }
         b -= nb;
@@ -239,24 +337,19 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_down_ke
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    switch ((m + 15) / 16) {
-        case 1: wide_down<1, false>(a, qb, e, row0, m, sm); break;
-#if MOE_WIDE_ITEM_TOK > 32
-        case 2: wide_down<2, false>(a, qb, e, row0, m, sm); break;
-        case 3: wide_down<3, false>(a, qb, e, row0, m, sm); break;
-        default: wide_down<4, false>(a, qb, e, row0, m, sm); break;
-#else
-        default: wide_down<2, false>(a, qb, e, row0, m, sm); break;
-#endif
-    }
+    by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, false>(a, qb, e, row0, m, sm); });
 }
-
 
 // The wide kernels in one persistent launch (see mfma_fused_kernel in
 // mfma.hip: the same queue, publication and bounded wait; a gate_up unit
-// is (item, quad block of four quads), and every wave stores h of its quad).
-__global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_kernel(GemmArgs a) {
-    __shared__ WSmem sm;
+// is (item, quad block of four quads), and every wave stores h of its quad;
+// a down unit is (item, quad block), and the last finisher of a token's k
+// experts on a quad combines it).
+__global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(GemmArgs a) {
+    __shared__ union {
+        WSmem x;
+        WQSmem q;
+    } sm;
     __shared__ int s_unit[2];
     const int n_items = uniform(a.meta[kMetaNumMfmaItems]);
     const int gu_units = a.I / 128, dn_units = (a.H / 64 + kWQuads - 1) / kWQuads;
@@ -275,16 +368,7 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_k
             const int item = u / gu_units, qb = u % gu_units;
             const int4 it = a.items[item];
             const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-            switch ((m + 15) / 16) {
-                case 1: wide_gate_up<1>(a, qb, e, row0, m, sm); break;
-#if MOE_WIDE_ITEM_TOK > 32
-                case 2: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
-                case 3: wide_gate_up<3>(a, qb, e, row0, m, sm); break;
-                default: wide_gate_up<4>(a, qb, e, row0, m, sm); break;
-#else
-                default: wide_gate_up<2>(a, qb, e, row0, m, sm); break;
-#endif
-            }
+            by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value>(a, qb, e, row0, m, sm.x); });
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's h stores completed
             __syncthreads();
             if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
@@ -294,16 +378,7 @@ __global__ void __launch_bounds__(kWThreads, MOE_WIDE_WAVES_PER_EU) wide_fused_k
             const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
-            switch ((m + 15) / 16) {
-                case 1: wide_down<1, true>(a, qb, e, row0, m, sm); break;
-#if MOE_WIDE_ITEM_TOK > 32
-                case 2: wide_down<2, true>(a, qb, e, row0, m, sm); break;
-                case 3: wide_down<3, true>(a, qb, e, row0, m, sm); break;
-                default: wide_down<4, true>(a, qb, e, row0, m, sm); break;
-#else
-                default: wide_down<2, true>(a, qb, e, row0, m, sm); break;
-#endif
-            }
+            by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, true>(a, qb, e, row0, m, sm.q); });
         }
         __syncthreads();  // LDS free for the next unit, whose index is now visible
     }
@@ -319,7 +394,7 @@ hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t str
 
 hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream) {
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
-    const int sh = a.sh_wdn ? shared_blocks((a.H / 64 + 1) / 2, (a.T + 31) / 32) : 0;
+    const int sh = a.sh_wdn ? shared_blocks((a.H / 64 + 1) / 2, (a.T + 15) / 16) : 0;
     wide_down_kernel<<<sh + max_items * qblocks, kWThreads, 0, stream>>>(a);
     return hipGetLastError();
 }

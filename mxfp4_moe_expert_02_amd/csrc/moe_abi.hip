@@ -74,7 +74,9 @@ size_t layout(Workspace* ws, char* base) {
     ws->router_partial = (float*)take((size_t)moe::kRouterMaxSplit * split_te * 4);
     ws->router_cnt = (int32_t*)take((size_t)2 * moe::kRouterWaves * 4);
     const size_t R = S + (size_t)ws->max_tokens;  // routed rows, then the shared expert's
-    ws->h = (uint16_t*)take(R * ws->I * 2);
+    ws->h = (uint16_t*)take(R * ws->I * 4);  // bf16 hi/lo pairs (GEMV path)
+    ws->h3q = (uint8_t*)take(R * ws->I * 3);  // three MXFP8 terms (matrix-core paths)
+    ws->h3s = (uint8_t*)take(R * (ws->I / 8));
     ws->y = (float*)take(R * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
     ws->x_scales = (uint8_t*)take((size_t)ws->max_tokens * (ws->H / 32));
@@ -238,6 +240,25 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     const int max_active = S < E ? S : E;
     hipError_t err;
 
+    const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
+    const bool mx8 = o.act_format == MOE_ACT_MXFP8;
+    // bf16 MFMA items of the routed launch: 16 tokens, or up to 64 when the
+    // experts average >= kMfmaWideMeanTok tokens (four quads per workgroup
+    // then share the item's staged activations, and an expert's weights are
+    // read once per 64 tokens)
+    const bool wide = (int64_t)T * k >= (int64_t)moe::kMfmaWideMeanTok * E;
+    const int item_tok = mx8 ? moe::kMx8Tok : wide ? moe::kMfmaItemTok : moe::kMfmaTok;
+    // The self-routed layer (no sorting pass: the GEMM workgroups find their
+    // experts' tokens themselves) covers the bf16 matrix-core path with
+    // single-tile items of at most kSelfMaxTok tokens; AUTO takes it
+    // wherever it applies.
+    const bool self_ok = !mx8 && path == MOE_PATH_MFMA && T <= moe::kSelfMaxTok &&
+                         (int64_t)T * E <= moe::kSelfMaxPairs &&
+                         (int64_t)T * k < (int64_t)moe::kSelfMaxMeanTok * E;
+    // (decided before anything is enqueued: a rejected call enqueues nothing)
+    if (o.launch == MOE_LAUNCH_SELF_ROUTED && !self_ok) return MOE_E_OPTION;
+    const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO);
+
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
     if (o.router_weight) {  // the router linear layer, ahead of the routing
         err = moe::launch_router_gemm((const uint16_t*)x, (const uint16_t*)o.router_weight, T, E, H,
@@ -245,20 +266,6 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         if (err != hipSuccess) return hip_fail(err, "router");
         router_logits = ws->logits;
     }
-    const int path = o.weight_layout == MOE_LAYOUT_TILES ? MOE_PATH_MFMA : MOE_PATH_GEMV;
-    const bool mx8 = o.act_format == MOE_ACT_MXFP8;
-    // bf16 MFMA items: 16 tokens, or up to 64 when experts average >= 8
-    // tokens (an expert's weights are then read once per 64 tokens)
-    const bool wide = (int64_t)T * k >= (int64_t)moe::kMfmaWideMeanTok * E;
-    const int item_tok = mx8 ? moe::kMx8Tok : wide ? moe::kMfmaItemTok : moe::kMfmaTok;
-    // The self-routed layer (no sorting pass: the GEMM workgroups find their
-    // experts' tokens themselves) covers the bf16 matrix-core path with
-    // single-tile items of at most kSelfMaxTok tokens; AUTO takes it
-    // wherever it applies.
-    const bool self_ok = !mx8 && path == MOE_PATH_MFMA && !wide && T <= moe::kSelfMaxTok &&
-                         (int64_t)T * E <= moe::kSelfMaxPairs;
-    if (o.launch == MOE_LAUNCH_SELF_ROUTED && !self_ok) return MOE_E_OPTION;
-    const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO);
     // the routing pass also runs for a self-routed layer when its results
     // are asked for (it writes the same ids and weights the layer uses)
     const bool want_route = o.ids || o.weights || o.counts || o.offsets || o.sorted;
@@ -296,6 +303,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.meta = ws->meta;
     a.list_meta = moe::kMetaNumGemv;
     a.h = ws->h;
+    a.h3q = ws->h3q;
+    a.h3s = ws->h3s;
     a.y = ws->y;
     a.H = H;
     a.I = I;

@@ -46,15 +46,11 @@ constexpr int kColTile = 2 * kDownUnits;
 // kMfmaDownRows output rows (also its combine tile width); the 4 waves of a
 // workgroup split K.
 constexpr int kMfmaTok = 16;      // tokens per MFMA column tile
-#ifndef MOE_WIDE_ITEM_TOK
-#define MOE_WIDE_ITEM_TOK 64
-#endif
-constexpr int kMfmaItemTok = MOE_WIDE_ITEM_TOK;  // tokens per wide item of the bf16 MFMA path
-// wide items when the layer averages at least this many tokens per expert
-#ifndef MOE_WIDE_MEAN_TOK
-#define MOE_WIDE_MEAN_TOK 8
-#endif
-constexpr int kMfmaWideMeanTok = MOE_WIDE_MEAN_TOK;
+constexpr int kMfmaItemTok = 64;  // tokens per wide item of the bf16 MFMA path
+// The routed launch uses wide items (four quads per workgroup, the item's
+// activations staged in LDS) when the layer averages at least this many
+// tokens per expert (T * top_k >= kMfmaWideMeanTok * E)
+constexpr int kMfmaWideMeanTok = 4;
 // MXFP8 (prefill) path: items of up to kMx8Tok tokens (eight 16-token MFMA
 // column tiles), weights in the same tile layout.
 constexpr int kMx8Tok = 128;
@@ -63,6 +59,8 @@ constexpr int kMx8Tok = 128;
 // weight pass holds in LDS.
 constexpr int kSelfMaxTok = 16;
 constexpr int kSelfMaxPairs = 4096;
+// ... and averaging fewer than kSelfMaxMeanTok tokens per expert
+constexpr int kSelfMaxMeanTok = 8;
 // Per-expert slot list of the self-routed layer: m, then the slots t*k + j
 // of its m tokens in ascending token order (one 128-byte line per expert).
 // Layers whose two GEMM grids hold at least kSelfListUnits workgroups
@@ -110,7 +108,13 @@ struct Workspace {
     int col_tiles = 0;             // H / kColTile
     // h and y: Tmax*kmax rows of the routed assignments (sorted order, or
     // slot order in a self-routed layer), then Tmax rows of the shared expert
-    uint16_t* h = nullptr;      // [Tmax*(kmax+1), I] bf16
+    // h: the routed rows of the GEMV path as bf16 hi/lo pairs [rows, 2I];
+    // h3q / h3s: h of the matrix-core paths (and of the shared expert on
+    // every bf16 path) as three MXFP8 terms, codes [rows, 3I] and scales
+    // [rows, I/8] (device_common.h, store_h3)
+    uint16_t* h = nullptr;
+    uint8_t* h3q = nullptr;
+    uint8_t* h3s = nullptr;
     float* y = nullptr;         // [Tmax*(kmax+1), H] fp32
     uint8_t* x_codes = nullptr;   // [Tmax, H] E4M3 codes of x (MXFP8 path)
     uint8_t* x_scales = nullptr;  // [Tmax, H/32] E8M0
@@ -131,7 +135,9 @@ struct GemmArgs {
     const int32_t* list;        // active experts for this path
     const int32_t* meta;
     int list_meta;              // which meta word holds the list length
-    uint16_t* h;
+    uint16_t* h;                // GEMV path's routed rows: [rows, 2I] bf16 hi/lo pairs (gemv.hip)
+    uint8_t* h3q;               // matrix-core paths and the shared expert: [rows, 3I] codes of
+    uint8_t* h3s;               // h's three MXFP8 terms, [rows, I/8] their scales (store_h3)
     float* y;
     int T, H, I, k;
     // combine state

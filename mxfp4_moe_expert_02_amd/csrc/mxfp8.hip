@@ -40,11 +40,7 @@
 namespace moe {
 namespace {
 
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-
-#ifndef MOE_PF_WAVES_PER_EU
-#define MOE_PF_WAVES_PER_EU 2
-#endif
+constexpr int kPfWavesPerEu = 2;  // launch bound of the prefill kernels
 
 constexpr int kPfThreads = 256;
 constexpr int kPfTiles = 4;               // 16-token column tiles per wave
@@ -458,7 +454,7 @@ __device__ inline void mx8_shared_down(const GemmArgs& a, int b, PfSmem& sm) {
 // row block holds quads 2rb, 2rb+1, each 32 gate rows (groups 0, 1) with
 // their 32 up rows (groups 2, 3), so SiLU(gate) * up is formed in
 // registers.  With a shared expert its blocks come first.
-__global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
+__global__ void __launch_bounds__(kPfThreads, kPfWavesPerEu)
 mx8_gate_up_kernel(GemmArgs a) {
     __shared__ PfSmem sm;
     const int rowblocks = a.I / 64;
@@ -492,7 +488,7 @@ mx8_gate_up_kernel(GemmArgs a) {
 // 2rb+1 of the output rows).  y goes out through plain 16-byte stores; the
 // combine runs as its own kernel after this one (combine.hip).  With a
 // shared expert its blocks come first.
-__global__ void __launch_bounds__(kPfThreads, MOE_PF_WAVES_PER_EU)
+__global__ void __launch_bounds__(kPfThreads, kPfWavesPerEu)
 mx8_down_kernel(GemmArgs a) {
     __shared__ PfSmem sm;
     const int rowblocks = a.H / 128;

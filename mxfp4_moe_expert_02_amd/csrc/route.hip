@@ -32,10 +32,7 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kFusedPairs = 12288;    // logits held in LDS by the single-workgroup kernel
-#ifndef MOE_FUSED_MAX_PAIRS
-#define MOE_FUSED_MAX_PAIRS 4096
-#endif
-constexpr int kFusedMaxPairs = MOE_FUSED_MAX_PAIRS;  // T*E routed by the single-workgroup kernel
+constexpr int kFusedMaxPairs = 4096;  // T*E routed by the single-workgroup kernel
 static_assert(kFusedMaxPairs <= kFusedPairs, "the single-workgroup route holds T*E logits in LDS");
 constexpr int kSlotBlock = kRouteSlotBlock;
 constexpr int kTopkThreads = 256;

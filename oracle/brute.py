@@ -171,21 +171,27 @@ def hidden_mxfp8_rows(x_bf16: np.ndarray, k: int, I: int,
 
 def down_from_h(h_codes: np.ndarray, h_scales: np.ndarray, k: int,
                 experts: Mapping[int, Sequence[np.ndarray]], ids: np.ndarray, w: np.ndarray,
-                pos: np.ndarray) -> np.ndarray:
+                pos: np.ndarray, tokens: Sequence[int] | None = None) -> np.ndarray:
     """The rest of the layer on a given MXFP8 h (rows in expert-sorted order,
     pos[t*k + j] = the row of slot t*k + j): out[t] = sum_j w[t, j] *
-    Wdown[ids[t, j]] @ dequant(h row pos[t*k + j]), in fp64, slots in order."""
-    T = ids.shape[0]
-    h = mxfp8_dequant(h_codes, h_scales)
-    down = {}
-    out = None
-    for t in range(T):
+    Wdown[ids[t, j]] @ dequant(h row pos[t*k + j]), in fp64, slots in order,
+    for the given tokens (default all; rows of the result in that order).
+    Each expert's down matrix is decoded once, its slots taken together."""
+    tokens = list(range(ids.shape[0])) if tokens is None else [int(t) for t in tokens]
+    by_expert = {}
+    for i, t in enumerate(tokens):
         for j in range(k):
-            e = int(ids[t, j])
-            if e not in down:
-                down[e] = mxfp4_dequant(experts[e][2], experts[e][3])
-            term = w[t, j] * (down[e] @ h[int(pos[t * k + j])])
-            if out is None:
-                out = np.zeros((T, term.shape[0]))
-            out[t] += term
+            by_expert.setdefault(int(ids[t, j]), []).append((i, t, j))
+    terms = {}
+    for e, slots in by_expert.items():
+        down = mxfp4_dequant(experts[e][2], experts[e][3])
+        for i, t, j in slots:
+            p = int(pos[t * k + j])
+            hrow = mxfp8_dequant(h_codes[p:p + 1], h_scales[p:p + 1])[0]
+            terms[(i, j)] = w[t, j] * (down @ hrow)
+        del down
+    out = np.zeros((len(tokens), next(iter(terms.values())).shape[0]))
+    for i in range(len(tokens)):
+        for j in range(k):
+            out[i] += terms[(i, j)]
     return out

@@ -5,25 +5,40 @@ matrix cores) against the CPU oracle run with the same MXFP8 rule.
   sides start from the same bf16 values and the encoding is exact
   arithmetic on them
 * routing bit-exact (the prefill path groups 64 tokens per work item)
-* layer output: max |out - ref| <= 2e-2 * rms(ref); h is encoded from fp32
-  on the GPU and from fp64 in the oracle, so a code of h may differ where
-  the value sits on a rounding boundary.  At the fixed shapes here that
-  stays within the bar.  On the small layers here (and in the seed sweep),
-  where one flipped code matters more, each difference is checked to lie
-  on a boundary and the output is compared with the oracle finished from
-  the GPU's own h codes; the full-size layers keep the fp64 oracle
+* layer output: h is encoded from fp32 on the GPU and from fp64 in the
+  oracle, so a code of h may differ where the value sits within fp32 error
+  of a rounding boundary: the decision is taken in the kernel's precision.
+  Every code of h of the compared tokens is checked to be such a case
+  (check_mxfp8_h) and max |out - ref| <= 2e-2 * rms(ref) against the oracle
+  finished from the GPU's own h codes; against the plain fp64 oracle too,
+  except the layers listed in MXFP8_PLAIN_OVER (twice the bar).
+  Full-size layers compare a set of tokens that puts one compared token in
+  every 128-token prefill item (or 16-token tile) of every touched expert.
 """
 import numpy as np
 import pytest
 
-from tests.gpu_common import (bf16_tensor_to_f64, check_mxfp8_h, get_layer, oracle_experts,
-                              parity_ratio, run, say)
+from tests.gpu_common import (bf16_tensor_to_f64, check_mxfp8_h, covering_tokens, get_layer,
+                              oracle_experts, parity_detail, parity_ratio, parity_ratio_past_rounding,
+                              run, say)
 from workloads import Config, get_config, make_logits, make_x_bf16
 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
 MX8 = 1  # MOE_ACT_MXFP8
+# Layers whose output, against the plain fp64 oracle, lands over the bar
+# while every code of h is a correct rounding of its value within the fp32
+# error bound (check_mxfp8_h) and the output is within the bar against the
+# oracle finished from those codes: an E4M3 code that flips on a rounding
+# boundary moves h by up to 1/8 of its value.  They are held to twice the
+# bar against the plain oracle.
+MXFP8_PLAIN_OVER = {"batched_verify_t72_e128_h7168_i2048_k8", "prefill_t4096_e128_h7168_i2048_k8"}
+# Layers where the rounding of out to bf16 alone exceeds the bar: an output
+# element far above the rms (batched-verify shape: 7.0 x rms, where half a
+# bf16 step is 2.38e-2 of rms and the GPU's value is the correctly rounded
+# reference).  There the error past that rounding must be within the bar.
+OUT_ROUNDING_OVER = {"batched_verify_t72_e128_h7168_i2048_k8"}
 
 
 @pytest.fixture(scope="module")
@@ -64,17 +79,22 @@ def _parity(M, oracle_lib, cfg, layer, tokens, logits=None, x_bits=None):
     assert np.array_equal(dbg["offsets"], route["offsets"])
     full = bf16_tensor_to_f64(layer.out)
     assert np.isfinite(full).all()  # every (token, column) was written
-    if cfg.T * cfg.k <= 512 and cfg.H * cfg.I <= 384 * 256:
-        # small layers: h's encoding decision taken in the kernel's precision
-        # (checked code by code), the oracle finishing from the GPU's own h
-        ex = oracle_experts(oracle_lib, cfg, route["ids"].ravel())
-        ref = check_mxfp8_h(oracle_lib, cfg, xb, ex, route, dbg)[tokens]
+    ex = oracle_experts(oracle_lib, cfg, route["ids"][tokens].ravel())
+    ref = oracle_lib.forward(xb, lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens, act_mxfp8=True)
+    plain = parity_ratio(full[tokens], ref)
+    # h's encoding decision checked code by code, then the oracle finished
+    # from the GPU's own h codes
+    sref = check_mxfp8_h(oracle_lib, cfg, xb, ex, route, dbg, tokens)
+    staged = parity_ratio(full[tokens], sref)
+    say(f"mxfp8 parity {cfg.name} {len(tokens)} tokens max|d|/rms = {plain:.3e} (plain), "
+        f"{staged:.3e} (from the GPU's h codes); {parity_detail(full[tokens], sref)}")
+    if cfg.name in OUT_ROUNDING_OVER:
+        past = parity_ratio_past_rounding(full[tokens], sref)
+        say(f"mxfp8 parity {cfg.name}: past the rounding of out {past:.3e}")
+        assert past <= TOL and staged <= 2 * TOL
     else:
-        ex = oracle_experts(oracle_lib, cfg, route["ids"][tokens].ravel())
-        ref = oracle_lib.forward(xb, lg, cfg.k, cfg.H, cfg.I, ex, tokens=tokens, act_mxfp8=True)
-    ratio = parity_ratio(full[tokens], ref)
-    say(f"mxfp8 parity {cfg.name} tokens={list(tokens)[:8]} max|d|/rms = {ratio:.3e}")
-    assert ratio <= TOL
+        assert staged <= TOL
+    assert plain <= (2 * TOL if cfg.name in MXFP8_PLAIN_OVER else TOL)
     return dbg
 
 
@@ -141,16 +161,23 @@ def test_mxfp8_forward_one_hot_expert_ragged_items(torch_dev, M, oracle_lib):
     _parity(M, oracle_lib, cfg, layer, list(range(0, cfg.T, 7)) + [cfg.T - 1], logits=logits)
 
 
-def test_mxfp8_forward_batched_shape_sampled(torch_dev, M, oracle_lib):
+def _covering(oracle_lib, cfg, unit_rows):
+    tokens, runs = covering_tokens(oracle_lib.route(make_logits(cfg), cfg.k), cfg.k, unit_rows)
+    say(f"{cfg.name}: {len(tokens)} tokens cover {runs} runs of {unit_rows} rows of the touched experts")
+    return tokens
+
+
+def test_mxfp8_forward_batched_shape_every_tile(torch_dev, M, oracle_lib):
     """72 tokens over 128 experts at the full hidden sizes (mostly 1-10
     token items) with MXFP8 activations."""
     cfg = get_config("c3")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71])
+    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg, 16))
 
 
-def test_mxfp8_forward_prefill_sampled(torch_dev, M, oracle_lib):
+def test_mxfp8_forward_prefill_every_item(torch_dev, M, oracle_lib):
+    """The prefill chunk: one compared token in each of its 128-token items."""
     cfg = get_config("c5")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 1, 2047, 4095])
+    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg, 128))
 
 
 def test_mxfp8_forward_deterministic(torch_dev, M):

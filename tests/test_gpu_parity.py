@@ -2,16 +2,19 @@
 
 * routing (ids, counts, offsets, sorted order) bit-exact; weights within 1e-6
 * MXFP4 encoding of the weights bit-exact
-* layer output: max |out - ref| <= 2e-2 * rms(ref) (bf16 activations and h,
-  fp32 accumulation, bf16 output) -- on every token for the small workloads,
-  on sampled tokens for the full-size ones
+* layer output: max |out - ref| <= 2e-2 * rms(ref) (bf16 activations, h
+  carried to about 2^-12 relative, fp32 accumulation, bf16 output) -- on
+  every token of the small workloads and of the 9-token verify step, and on
+  the batched and skewed verify steps on a set of tokens that puts at least
+  one compared token in every 16-token column tile of every touched expert
+  (covering_tokens)
 * determinism, unread empty experts, and the ABI's synchronous errors
 """
 import numpy as np
 import pytest
 
-from tests.gpu_common import (bf16_tensor_to_f64, get_layer, oracle_experts, parity_ratio, run,
-                              say)
+from tests.gpu_common import (bf16_tensor_to_f64, covering_tokens, get_layer, oracle_experts,
+                              parity_ratio, run, say)
 from workloads import Config, get_config, make_logits, make_weight_fp32, make_x_bf16
 
 pytestmark = pytest.mark.gpu
@@ -197,21 +200,27 @@ def test_forward_tiny_all_tokens(torch_dev, M, oracle_lib, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_forward_verify_sampled(torch_dev, M, oracle_lib, path):
+def test_forward_verify_all_tokens(torch_dev, M, oracle_lib, path):
     cfg = get_config("c2")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 4, 8], path=path)
+    _parity(M, oracle_lib, cfg, get_layer(cfg), list(range(cfg.T)), path=path)
+
+
+def _covering(oracle_lib, cfg):
+    tokens, runs = covering_tokens(oracle_lib.route(make_logits(cfg), cfg.k), cfg.k, 16)
+    say(f"{cfg.name}: {len(tokens)} tokens cover {runs} 16-token tiles of the touched experts")
+    return tokens
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_forward_batched_verify_sampled(torch_dev, M, oracle_lib, path):
+def test_forward_batched_verify_every_tile(torch_dev, M, oracle_lib, path):
     cfg = get_config("c3")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 35, 71], path=path)
+    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg), path=path)
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_forward_zipf_verify_sampled(torch_dev, M, oracle_lib, path):
+def test_forward_zipf_verify_every_tile(torch_dev, M, oracle_lib, path):
     cfg = get_config("c4")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), [0, 143, 287], path=path)
+    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg), path=path)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -245,17 +254,26 @@ def test_forward_small_edges(torch_dev, M, oracle_lib, T, k, path):
 
 
 def test_forward_paths_agree(torch_dev, M):
-    """The VALU and matrix-core paths compute the same layer: their bf16
-    outputs differ only by accumulation order (within the parity bar)."""
-    import torch
+    """The VALU and matrix-core paths compute the same layer: before the
+    final rounding to bf16 their fp32 results differ only by accumulation
+    order and h's representation (relative 2^-17 and 2^-12 per element of
+    h), so every output element agrees to within one bf16 step of its
+    magnitude (an element near a rounding boundary may round either way)
+    plus 1e-3 of the output's rms (cancellation: an element near zero has
+    the absolute error of its summands), far inside the 2e-2 bar."""
     cfg = get_config("c2")
     layer = get_layer(cfg)
     run(M, layer, path=1)
-    a = layer.out.float().clone()
+    a = bf16_tensor_to_f64(layer.out)
     run(M, layer, path=2)
-    b = layer.out.float()
-    rms = torch.sqrt(torch.mean(a * a))
-    assert float((a - b).abs().max() / rms) <= TOL
+    b = bf16_tensor_to_f64(layer.out)
+    mag = np.maximum(np.abs(a), np.abs(b))
+    step = np.ldexp(1.0, np.frexp(mag)[1] - 8)  # bf16 spacing at that magnitude
+    floor = 1e-3 * np.sqrt(np.mean(a * a))
+    over = np.abs(a - b) > step + floor
+    say(f"paths agree: {int((a != b).sum())} of {a.size} elements differ, "
+        f"max |a-b| / (step + floor) = {float(np.max(np.abs(a - b) / (step + floor))):.2f}")
+    assert not over.any(), np.argwhere(over)[:5]
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -2,15 +2,18 @@
 
 Eight seeds, each with its own small shape (1 to 130 tokens, 8 to 32
 experts, top-1 to top-8; ragged token tiles, wide items where the experts
-average 8 or more tokens), each run through the C ABI on the VALU GEMV path,
+average 4 or more tokens), each run through the C ABI on the VALU GEMV path,
 the automatic matrix-core launch (self-routed where it applies), the split
 launch, the single launch and the MXFP8 path.  On every case the routing
 (ids, counts, offsets, sorted order) equals the oracle's bit for bit, the weights agree
 within 1e-6, and every token's output is within the bar of the fp64 oracle.
 On the MXFP8 path the x codes are bit-exact; the codes of h are a decision
 taken on fp32 values, so every code that differs from the oracle's must sit
-on a rounding or scale boundary, and the output is compared with the oracle
-finished from the GPU's own h (the decision taken in the kernel's precision).
+within fp32 error of a rounding or scale boundary (check_mxfp8_h), the
+output is compared with the oracle finished from the GPU's own h, and with
+the plain fp64 oracle -- where one flipped code of h moves a small layer's
+output over the bar against the plain oracle, the case is listed by name in
+MXFP8_PLAIN_OVER (and asserted to stay the exception it is).
 """
 import numpy as np
 import pytest
@@ -27,12 +30,17 @@ SHAPES = {  # seed: (T, E, k)
     201: (3, 8, 2),
     202: (16, 12, 3),
     203: (37, 8, 2),
-    204: (64, 16, 4),    # wide items (T*k >= 8E)
+    204: (64, 16, 4),    # wide items (T*k >= 4E) on the routed launches
     205: (100, 12, 6),   # wide, experts with more than 64 tokens
     206: (9, 16, 8),
     207: (130, 32, 4),   # wide, ragged last tile
     208: (1, 8, 1),
 }
+
+# (seed, path) cases whose MXFP8 output is over the bar against the plain
+# fp64 oracle although every code of h is a correct rounding of its fp32
+# value (a code on a boundary flips, which a layer this small feels)
+MXFP8_PLAIN_OVER = {(205, "mx8"), (207, "mx8")}
 
 PATHS = {  # name: (gemm path, activation format, launch)
     "gemv": (1, 0, 0),
@@ -89,26 +97,23 @@ def test_seed_sweep_vs_oracle(M, oracle_lib, seed, path):
         xc, xs = oracle_lib.quantize_mxfp8(bf16_to_f64(x))
         np.testing.assert_array_equal(dbg["x_codes"], xc)
         np.testing.assert_array_equal(dbg["x_scales"], xs)
-        ref = check_mxfp8_h(oracle_lib, cfg, x, ex, r, dbg)
-    else:
-        ref = oracle_lib.forward(x, lg, cfg.k, cfg.H, cfg.I, ex)
-    ratio = parity_ratio(full, ref)
+        staged = parity_ratio(full, check_mxfp8_h(oracle_lib, cfg, x, ex, r, dbg))
+        plain = parity_ratio(full, oracle_lib.forward(x, lg, cfg.k, cfg.H, cfg.I, ex, act_mxfp8=True))
+        say(f"seed sweep {cfg.name} {path}: max|d|/rms = {plain:.3e} (plain), {staged:.3e} "
+            f"(from the GPU's h)")
+        assert staged <= TOL
+        if (seed, path) in MXFP8_PLAIN_OVER:
+            assert plain > TOL, "listed as over the bar against the plain oracle, now under"
+        else:
+            assert plain <= TOL
+        return
+    ratio = parity_ratio(full, oracle_lib.forward(x, lg, cfg.k, cfg.H, cfg.I, ex))
     say(f"seed sweep {cfg.name} {path}: max|d|/rms = {ratio:.3e}")
     assert ratio <= TOL
 
 
-# Seed 202 with the shared expert lands at 2.001e-2 of rms on every path (the
-# same bits): the layer's two bf16 roundings -- h between the GEMMs and out --
-# stack on an element at 4.4x the rms; rounding the fp64 layer at those two
-# points gives the same 2.0014e-2.  Kept as an expected failure: it runs, and
-# would report if it ever passed.
-SHARED_SEEDS = [pytest.param(s, marks=pytest.mark.xfail(
-    strict=True, reason="bf16 h and bf16 out roundings stack to 2.0014e-2 rms (bar 2e-2)"))
-    if s == 202 else s for s in SHAPES]
-
-
 @pytest.mark.parametrize("path", ["gemv", "auto", "split", "fused"])
-@pytest.mark.parametrize("seed", SHARED_SEEDS)
+@pytest.mark.parametrize("seed", list(SHAPES))
 def test_seed_sweep_with_shared_expert(M, oracle_lib, seed, path):
     """The same sweep with an MXFP8 shared expert beside the routed ones
     (bf16 activations, so h involves no encoding decision)."""

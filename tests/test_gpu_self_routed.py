@@ -143,3 +143,32 @@ def test_self_routed_rejects_ineligible(M, shape):
     with pytest.raises(M.MoeError) as ei:
         run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_SELF_ROUTED)
     assert ei.value.status == M.MOE_E_OPTION
+
+
+def test_rejected_call_enqueues_nothing(M):
+    """A self-routed call on an ineligible layer is rejected before anything
+    reaches the stream: the stage event it was given keeps the time it was
+    recorded at before the call (recording it again would move it past a
+    later reference event), and the router linear layer it asked for does
+    not run."""
+    import time
+
+    import torch
+    cfg = _cfg(17, 8, 256, 128, 2, 60)
+    layer = get_layer(cfg)
+    M.moe_mxfp4_init(cfg.T, cfg.E, cfg.H, cfg.I, cfg.k)
+    ev = torch.cuda.Event(enable_timing=True)
+    ev.record()
+    torch.cuda.synchronize()
+    time.sleep(0.01)
+    ref = torch.cuda.Event(enable_timing=True)
+    ref.record()
+    torch.cuda.synchronize()
+    router = torch.zeros((cfg.E, cfg.H), dtype=torch.bfloat16, device="cuda")
+    wgu, wdn, scales = layer.weights(M.MOE_LAYOUT_TILES)
+    rc = M.moe_mxfp4_forward_ex(layer.x, None, cfg.k, wgu, wdn, scales, layer.out,
+                                weight_layout=M.MOE_LAYOUT_TILES, launch=M.MOE_LAUNCH_SELF_ROUTED,
+                                events=[ev], router_weight=router, check=False)
+    torch.cuda.synchronize()
+    assert rc == M.MOE_E_OPTION
+    assert ref.elapsed_time(ev) < 0  # ev still holds its earlier time
