@@ -20,8 +20,11 @@
  *
  * The pages give no router or FFN formula; this is the standard softmax
  * top-k MoE with a SiLU-gated FFN, the plainest reading of "experts" they
- * describe.  Accumulation is fp32; the intermediate h is bf16 (bf16
- * activations) or MXFP8 (prefill); out is bf16 rounded to nearest even.
+ * describe.  Accumulation is fp32.  With bf16 activations the intermediate
+ * h is carried to about 2^-12 relative (three MXFP8 terms on the matrix-core
+ * paths, bf16 hi/lo pairs on the VALU path), so that the layer's error is
+ * that of fp32 arithmetic between bf16 x and bf16 out; with MXFP8
+ * activations (prefill) h is MXFP8.  out is bf16 rounded to nearest even.
  *
  * Data layout (all row-major, contiguous, caller-owned device memory):
  *   x              [T, H]        bf16 bit patterns

@@ -57,7 +57,11 @@ __device__ inline uint32_t word_of(const uint4& v, int q) {
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u with the hardware reciprocal (v_rcp_f32, about 1 ulp) in
+// place of an IEEE division; 1 + exp(-g) overflowing to infinity gives 0
+__device__ inline float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -133,7 +137,9 @@ constexpr int kHTerms = 3;
 // the remainder.  A block holding a NaN or an infinity gets term 0 scale
 // 0xFF (NaN) and zero codes.  Agent-coherent stores: in the single-launch
 // layer the down unit that reads them may run on another XCD in the same
-// launch (its L2 never held these lines in this launch).
+// launch (its L2 never held these lines in this launch); plain stores
+// otherwise (PUBLISH = false: the kernel boundary makes them visible).
+template <bool PUBLISH>
 __device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const float (&v)[2][4],
                                 bool live) {
     typedef short s16x2_t __attribute__((ext_vector_type(2)));
@@ -161,7 +167,9 @@ __device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const f
         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
         if (tm == 0) special = amax >= 0x7f800000u;
-        const int se = special || amax == 0 ? -127 : min(floor_log2_bits(amax) - 7, 127);
+        const int se = special || amax == 0
+                           ? -127
+                           : min(__builtin_amdgcn_frexp_expf(__uint_as_float(amax)) - 8, 127);
         scales |= (uint32_t)(se + 127) << (8 * tm);
 #pragma unroll
         for (int rg = 0; rg < 2; rg++) {
@@ -192,13 +200,21 @@ __device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const f
         // bytes 16 * (b / 2) + 4g .. +3 of its 32-byte piece
         uint8_t* p = crow + (chunk * 4 + ((2 * b + rg) & 3)) * 96 + (b >> 1) * 16 + 4 * g;
 #pragma unroll
-        for (int tm = 0; tm < kHTerms; tm++)
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(p + 32 * tm), code[tm][rg], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int tm = 0; tm < kHTerms; tm++) {
+            uint32_t* d = reinterpret_cast<uint32_t*>(p + 32 * tm);
+            if constexpr (PUBLISH)
+                __hip_atomic_store(d, code[tm][rg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *d = code[tm][rg];
+        }
     }
-    if (g == 0)
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h3s + row * (a.I / 8) + (chunk * 4 + b) * 4), scales,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (g == 0) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(a.h3s + row * (a.I / 8) + (chunk * 4 + b) * 4);
+        if constexpr (PUBLISH)
+            __hip_atomic_store(d, scales, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *d = scales;
+    }
 }
 
 // Spin (sleeping) until *count >= need, reading it agent-coherently.  Gives

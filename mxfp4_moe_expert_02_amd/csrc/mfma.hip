@@ -251,7 +251,7 @@ mfma_fused_kernel(GemmArgs a) {
             const int item = u / gu_units;
             const int4 it = a.items[item];
             const int64_t e = uniform(it.x);
-            gate_up_item<1, W4, XB>(a, u % gu_units, a.wgu + e * gu_units * (a.H / 128) * 4096,
+            gate_up_item<1, W4, XB, true>(a, u % gu_units, a.wgu + e * gu_units * (a.H / 128) * 4096,
                                     a.sgu + e * gu_units * (a.H / 128) * 256,
                                     SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
             if (threadIdx.x < kWave) {  // wave 0 stored the h rows

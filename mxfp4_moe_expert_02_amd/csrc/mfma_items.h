@@ -303,8 +303,9 @@ constexpr int kRedDown = 2 * kGroups * kWave;
 // (c, g) holds rows 4g..4g+3 of group rg for token row 16t + c; groups 0, 1
 // are gate rows 32*quad + 16*rg + 4g + i, groups 2, 3 the matching up rows,
 // so the lane forms h elements 32*quad + 16*rg + 4g .. +3 of its token's h
-// row (rows.row), h block `quad`, stored as three MXFP8 terms.
-template <int NT, typename Rows>
+// row (rows.row), h block `quad`, stored as three MXFP8 terms (PUBLISH:
+// for readers in the same launch, see store_h3).
+template <int NT, bool PUBLISH, typename Rows>
 __device__ inline void store_h_tile(const GemmArgs& a, int quad, const Rows& rows,
                                     const f32x4_t (&acc)[kGroups][NT]) {
     const int c = threadIdx.x % 16;
@@ -316,14 +317,15 @@ __device__ inline void store_h_tile(const GemmArgs& a, int quad, const Rows& row
         for (int rg = 0; rg < 2; rg++)
 #pragma unroll
             for (int i = 0; i < 4; i++) v[rg][i] = silu_mul(acc[rg][t][i], acc[rg + 2][t][i]);
-        store_h3(a, rows.row(min(j, rows.m - 1)), quad, v, j < rows.m);
+        store_h3<PUBLISH>(a, rows.row(min(j, rows.m - 1)), quad, v, j < rows.m);
     }
 }
 
 // gate_up body for items of NT column tiles, token rows from `rows`
 // (SortedRows, SlotRows, ListRows or TokenRows); gu/gus: the expert's
-// gate_up tiles (format W), x in format X; h goes out as hi/lo pairs.
-template <int NT, typename W, typename X, typename Rows>
+// gate_up tiles (format W), x in format X; h goes out as three MXFP8 terms
+// (PUBLISH: for a down unit of the same launch).
+template <int NT, typename W, typename X, bool PUBLISH = false, typename Rows>
 __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* gu,
                                     const uint8_t* gus, const Rows& rows, f32x4_t* red) {
     const int c = threadIdx.x % 16;
@@ -342,7 +344,7 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* 
                         cb, ce, acc);
     reduce_waves<NT>(acc, red);
     if (threadIdx.x >= kWave) return;
-    store_h_tile<NT>(a, quad, rows, acc);
+    store_h_tile<NT, PUBLISH>(a, quad, rows, acc);
 }
 
 // down body for items of NT column tiles (see mfma_down_kernel), token rows

@@ -165,11 +165,13 @@ struct QStage {
     uint4 v[kPer];
 };
 
-template <int NT>
-__device__ inline void q_stage_init(const GemmArgs& a, int row0, int m, QStage<NT>& st) {
+// staged row n is h row rows.row(min(n, m - 1)) (Rows: SortedRows, or the
+// slot list of a self-routed expert)
+template <int NT, typename Rows>
+__device__ inline void q_stage_init(const GemmArgs& a, const Rows& rows, QStage<NT>& st) {
     constexpr int kTpr = QStage<NT>::kTpr;
     const int n = threadIdx.x / kTpr, l = threadIdx.x % kTpr;
-    const int64_t r = row0 + min(n, m - 1);
+    const int64_t r = rows.row(min(n, rows.m - 1));
     st.q = a.h3q + r * 3 * a.I + 16 * l;
     st.sc = a.h3s + r * (a.I / 8);
 }
@@ -225,16 +227,16 @@ __device__ inline void chunk_mfma_q3(const WQSmem& sm, int buf, const WChunk& b,
 // Main loop of the down GEMM over all `chunks` chunks: chunk s + 1's h is
 // staged and its weights loaded while chunk s is computed (weights in the
 // buffer chunk s - 1 left), as in wide_mainloop.
-template <int NT>
+template <int NT, typename Rows>
 __device__ inline void wide_mainloop_q3(const GemmArgs& a, const uint8_t* tiles, const uint8_t* tscales,
-                                        bool live, int row0, int m, int chunks, WQSmem& sm,
+                                        bool live, const Rows& rows, int chunks, WQSmem& sm,
                                         f32x4_t (&acc)[kGroups][NT]) {
 #pragma unroll
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     QStage<NT> st;
-    q_stage_init<NT>(a, row0, m, st);
+    q_stage_init<NT>(a, rows, st);
     q_load<NT>(st, 0);
     WChunk w[2];
     if (live) load_chunk(tiles, tscales, 0, w[0]);
@@ -254,7 +256,7 @@ __device__ inline void wide_mainloop_q3(const GemmArgs& a, const uint8_t* tiles,
     }
 }
 
-template <int NT>
+template <int NT, bool PUBLISH>
 __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, int m, WSmem& sm) {
     const int tid = threadIdx.x, w = tid / kWave;
     const int K = a.H, chunks = K / 128, quads = a.I / 32;
@@ -269,21 +271,23 @@ __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, 
     f32x4_t acc[kGroups][NT];
     wide_mainloop<NT>(a.wgu + quad_id * chunks * 4096, a.sgu + quad_id * chunks * 256, true, rows,
                       chunks, sm, acc);
-    store_h_tile<NT>(a, quad, SortedRows{row0, m}, acc);
+    store_h_tile<NT, PUBLISH>(a, quad, SortedRows{row0, m}, acc);
 }
 
-template <int NT, bool COMBINE>
-__device__ inline void wide_down(const GemmArgs& a, int qb, int e, int row0, int m, WQSmem& sm) {
+// Down quads 4qb .. 4qb+3 of expert e (one per wave) for the token rows
+// `rows` (SortedRows of a routed item, or ListRows of a self-routed expert)
+template <int NT, bool COMBINE, typename Rows>
+__device__ inline void wide_down(const GemmArgs& a, int qb, int e, const Rows& rows, WQSmem& sm) {
     const int w = threadIdx.x / kWave;
     const int chunks = a.I / 128, quads = a.H / 64;
     const int quad = kWQuads * qb + w;
     const bool live = quad < quads;
     const int64_t quad_id = (int64_t)e * quads + (live ? quad : 0);
     f32x4_t acc[kGroups][NT];
-    wide_mainloop_q3<NT>(a, a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, row0,
-                         m, chunks, sm, acc);
+    wide_mainloop_q3<NT>(a, a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
+                         chunks, sm, acc);
     if (!live) return;
-    store_down_tile<NT, COMBINE>(a, quad, SortedRows{row0, m}, acc);
+    store_down_tile<NT, COMBINE>(a, quad, rows, acc);
 }
 
 // Call fn(std::integral_constant<int, NT>) for an item of m tokens: NT =
@@ -316,7 +320,7 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_gate_up_kerne
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value>(a, qb, e, row0, m, sm); });
+    by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value, false>(a, qb, e, row0, m, sm); });
 }
 
 // down: blockIdx.x = item * ceil(H / 256) + quad block
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_down_kernel(G
     if (item >= uniform(a.meta[kMetaNumMfmaItems])) return;
     const int4 it = a.items[item];
     const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-    by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, false>(a, qb, e, row0, m, sm); });
+    by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, false>(a, qb, e, SortedRows{row0, m}, sm); });
 }
 
 // The wide kernels in one persistent launch (see mfma_fused_kernel in
@@ -368,7 +372,7 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
             const int item = u / gu_units, qb = u % gu_units;
             const int4 it = a.items[item];
             const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-            by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value>(a, qb, e, row0, m, sm.x); });
+            by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value, true>(a, qb, e, row0, m, sm.x); });
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's h stores completed
             __syncthreads();
             if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
@@ -378,7 +382,9 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
             const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
             if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
             __syncthreads();
-            by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, true>(a, qb, e, row0, m, sm.q); });
+            by_tiles(m, [&](auto nt) {
+                wide_down<decltype(nt)::value, true>(a, qb, e, SortedRows{row0, m}, sm.q);
+            });
         }
         __syncthreads();  // LDS free for the next unit, whose index is now visible
     }

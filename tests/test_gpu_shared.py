@@ -110,12 +110,13 @@ def _e2m1_to_e4m3(oracle_lib):
 
 @pytest.mark.parametrize("launch", ["auto", "split"])
 def test_mxfp8_copy_of_an_mxfp4_expert_gives_the_same_bits(M, oracle_lib, launch):
-    """Layer A: 2 experts, every token routed to expert 0 (k = 1, weight 1).
-    Layer B: both routed experts zero, the shared expert the MXFP8 copy of
-    expert 0.  Same bf16 A and B operands in the same MFMA order: the same
-    output bits."""
+    """Layer A: 4 experts, every token routed to expert 0 (k = 1, weight 1).
+    Layer B: the routed experts zero, the shared expert the MXFP8 copy of
+    expert 0.  Same weight values and the same h terms in the same MFMA
+    order (the routed items are single 16-token tiles, as the shared
+    expert's blocks): the same output bits."""
     import torch
-    T, E, H, I = 9, 2, 256, 128
+    T, E, H, I = 9, 4, 256, 128
     rng = np.random.default_rng(43)
     dev = "cuda"
     mats = {}
@@ -156,7 +157,7 @@ def test_mxfp8_copy_of_an_mxfp4_expert_gives_the_same_bits(M, oracle_lib, launch
     x = torch.from_numpy(make_x_bf16(Config("s", "s", T, E, H, I, 1, "normal", "bf16", 44))
                          .view(np.int16)).view(torch.bfloat16).to(dev)
     lg = torch.zeros((T, E), dtype=torch.float32, device=dev)
-    lg[:, 1] = -1.0  # expert 0 for every token
+    lg[:, 1:] = -1.0  # expert 0 for every token
     lmode = M.MOE_LAUNCH_SPLIT if launch == "split" else M.MOE_LAUNCH_AUTO
     M.moe_mxfp4_init(T, E, H, I, 1)
     outs = []
