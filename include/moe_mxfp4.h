@@ -78,6 +78,7 @@ extern "C" {
 #define MOE_E_NOT_INIT (-6)  /* moe_mxfp4_init was not called for the current device */
 #define MOE_E_HIP (-7)       /* a HIP runtime call or kernel launch failed */
 #define MOE_E_OPTION (-8)    /* an option value is not recognised */
+#define MOE_E_LIMIT (-9)     /* a size exceeds the fixed limits of moe_mxfp4_forward_noalloc */
 
 /* activation formats fed to the expert GEMMs */
 #define MOE_ACT_BF16 0       /* x and h in bf16 (verify token counts) */
@@ -277,6 +278,33 @@ int moe_mxfp8_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* code
 int moe_mxfp8_prepack(const uint8_t* codes, const uint8_t* scales, int64_t num_matrices,
                       int64_t rows, int64_t cols, int32_t gate_up_pairs, uint8_t* tiles,
                       uint8_t* tile_scales, void* stream);
+
+/* The layer for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * needs no moe_mxfp4_init and calls no allocating routine: its working set
+ * (per-expert slot lists, routing weights, h, the per-assignment outputs)
+ * lives in one fixed device array of the library, about 5.6 MB, which each
+ * device holds from its first call until the process ends.  It runs the
+ * self-routed layer (the launches of moe_mxfp4_forward_ex with
+ * MOE_LAUNCH_SELF_ROUTED, bf16 activations, weights in the MFMA tile layout
+ * of moe_mxfp4_prepack, no shared expert), with the same output bits, for
+ * layers of at most 16 tokens, 256 experts, top_k 8, hidden 8192 and inter
+ * 4096 (multiples of 128) with num_tokens * num_experts <= 4096 and
+ * num_tokens * top_k < 8 * num_experts; larger ones return MOE_E_LIMIT
+ * (moe_mxfp4_status_string names the limits), bad pointers, sizes or
+ * top_k the codes of moe_mxfp4_forward, all before anything is enqueued.
+ * Arguments as moe_mxfp4_forward, plus the layer's num_experts, hidden and
+ * inter sizes (which the workspace gives moe_mxfp4_forward); x,
+ * router_logits and out hold num_tokens rows.  Nothing in the array needs
+ * clearing between calls (every piece is written before it is read), but
+ * all calls on one device share it: calls whose work overlaps on one device
+ * (two streams, or two host threads) race.  The first call on a device
+ * takes the array's device address (hipGetSymbolAddress) and may not be
+ * captured into a graph; later calls may. */
+int moe_mxfp4_forward_noalloc(const void* x, const float* router_logits, int64_t num_tokens,
+                              int32_t top_k, int64_t num_experts, int64_t hidden, int64_t inter,
+                              const uint8_t* W_gate_up, const uint8_t* W_down,
+                              const moe_mxfp4_scales* scales, void* out, void* stream);
 
 /* Static text of a status code; for MOE_E_HIP, the text of the last HIP
  * error seen by the calling thread. */

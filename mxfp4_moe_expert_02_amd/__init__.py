@@ -5,12 +5,14 @@ The layer itself is hand-written HIP in ``csrc/`` behind the C ABI of
 ``_lib`` is the ctypes binding (same names as the C ABI); ``layer`` builds a
 device-resident synthetic layer for tests and benchmarks.
 """
-from ._lib import (MOE_ACT_BF16, MOE_ACT_MXFP8, MOE_E_ALIGN, MOE_E_HIP, MOE_E_NOT_INIT,
-                   MOE_E_NULL, MOE_E_OPTION, MOE_E_SHAPE, MOE_E_TOKENS, MOE_E_TOPK, MOE_OK,
+from ._lib import (MOE_ACT_BF16, MOE_ACT_MXFP8, MOE_E_ALIGN, MOE_E_HIP, MOE_E_LIMIT,
+                   MOE_E_NOT_INIT, MOE_E_NULL, MOE_E_OPTION, MOE_E_SHAPE, MOE_E_TOKENS, MOE_E_TOPK,
+                   MOE_OK,
                    MOE_LAUNCH_AUTO, MOE_LAUNCH_FUSED, MOE_LAUNCH_SELF_ROUTED, MOE_LAUNCH_SPLIT,
                    MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES, MOE_PATH_AUTO, MOE_PATH_GEMV,
                    MOE_PATH_MFMA, MoeError, lib, moe_mxfp4_prepack,
-                   moe_mxfp4_finalize, moe_mxfp4_forward, moe_mxfp4_forward_ex, moe_mxfp4_init,
+                   moe_mxfp4_finalize, moe_mxfp4_forward, moe_mxfp4_forward_ex,
+                   moe_mxfp4_forward_noalloc, moe_mxfp4_init,
                    moe_mxfp4_quantize, moe_mxfp4_status_string, moe_mxfp8_prepack,
                    moe_mxfp8_quantize, moe_probe_copy,
                    moe_probe_sink_words, moe_probe_stream_read)

@@ -25,6 +25,7 @@ MOE_E_TOKENS = -5
 MOE_E_NOT_INIT = -6
 MOE_E_HIP = -7
 MOE_E_OPTION = -8
+MOE_E_LIMIT = -9
 
 MOE_ACT_BF16 = 0
 MOE_ACT_MXFP8 = 1
@@ -41,7 +42,8 @@ MOE_LAUNCH_SELF_ROUTED = 3
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
             "moe_mxfp4_prepack", "moe_mxfp8_quantize", "moe_mxfp8_prepack",
-            "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy")
+            "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy",
+            "moe_mxfp4_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_forward.argtypes = fwd
         L.moe_mxfp4_forward_ex.restype = ctypes.c_int
         L.moe_mxfp4_forward_ex.argtypes = fwd + [ctypes.POINTER(moe_mxfp4_options)]
+        L.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
+        L.moe_mxfp4_forward_noalloc.argtypes = [vp, vp, i64, i32, i64, i64, i64, vp, vp,
+                                                ctypes.POINTER(moe_mxfp4_scales), vp, vp]
         L.moe_mxfp4_quantize.restype = ctypes.c_int
         L.moe_mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.moe_mxfp4_status_string.restype = ctypes.c_char_p
@@ -240,6 +245,25 @@ def moe_mxfp4_forward(x, router_logits, top_k: int, W_gate_up, W_down, scales, o
     rc = lib().moe_mxfp4_forward(_ptr(x), _ptr(router_logits), T, top_k, _ptr(W_gate_up),
                                  _ptr(W_down), ctypes.byref(sc), _ptr(out), _stream(stream))
     return _check(rc, "moe_mxfp4_forward") if check else rc
+
+
+def moe_mxfp4_forward_noalloc(x, router_logits, top_k: int, W_gate_up, W_down, scales, out,
+                              num_experts: int, hidden: int, inter: int, stream=None,
+                              check: bool = True) -> int:
+    """The allocation-free layer (weights in the MFMA tile layout, at most 16
+    tokens; see include/moe_mxfp4.h): x [T, H] bfloat16, router_logits
+    [T, E] float32, out [T, H] bfloat16; W_gate_up / W_down / scales as
+    written by moe_mxfp4_prepack."""
+    import torch
+    T = x.shape[0]
+    _expect(x, torch.bfloat16, (T, hidden), "x")
+    _expect(router_logits, torch.float32, (T, num_experts), "router_logits")
+    _expect(out, torch.bfloat16, (T, hidden), "out")
+    sc = moe_mxfp4_scales(_ptr(scales[0]), _ptr(scales[1]))
+    rc = lib().moe_mxfp4_forward_noalloc(_ptr(x), _ptr(router_logits), T, top_k, num_experts, hidden,
+                                         inter, _ptr(W_gate_up), _ptr(W_down), ctypes.byref(sc),
+                                         _ptr(out), _stream(stream))
+    return _check(rc, "moe_mxfp4_forward_noalloc") if check else rc
 
 
 def moe_mxfp4_prepack(packed, scales, tiles, tile_scales, gate_up_pairs: bool,

@@ -107,6 +107,52 @@ Workspace* current_ws() {
     return g_ws[dev];
 }
 
+// ---- the allocation-free verify layer (moe_mxfp4_forward_noalloc): the
+// self-routed layer of at most kNaMaxTokens tokens, its working set in one
+// file-scope device array instead of a workspace.  Byte offsets of its
+// pieces, each sized for the largest accepted layer (rows = tokens x top_k,
+// row strides those of the call):
+constexpr int64_t kNaMaxTokens = 16, kNaMaxExperts = 256, kNaMaxTopK = 8;
+constexpr int64_t kNaMaxHidden = 8192, kNaMaxInter = 4096;
+constexpr size_t kNaRows = (size_t)(kNaMaxTokens * kNaMaxTopK);
+constexpr size_t kNaLists = 0;  // [E][kSlotListInts] int32: per-expert slot lists
+constexpr size_t kNaIds = kNaLists + (size_t)kNaMaxExperts * moe::kSlotListInts * 4;  // [T*k] int32
+constexpr size_t kNaWts = kNaIds + kNaRows * 4;                                       // [T*k] fp32
+constexpr size_t kNaH3q = kNaWts + kNaRows * 4;                          // [T*k][3I] h's term codes
+constexpr size_t kNaH3s = kNaH3q + kNaRows * 3 * (size_t)kNaMaxInter;      // [T*k][I/8] their scales
+constexpr size_t kNaY = kNaH3s + kNaRows * (size_t)kNaMaxInter / 8;        // [T*k][H] fp32
+constexpr size_t kNaBytes = kNaY + kNaRows * (size_t)kNaMaxHidden * 4;     // 5.6 MB
+static_assert(kNaH3q % 256 == 0 && kNaH3s % 256 == 0 && kNaY % 256 == 0, "aligned pieces");
+
+// per device: the device address of `scratch`, taken once
+void* g_na_scratch[kMaxDevices] = {};
+std::mutex g_na_mu;
+
+}  // namespace
+
+// The allocation-free entry point's working set (see kNaBytes).  Host code
+// uses its device address from hipGetSymbolAddress, never this name.
+static __device__ __align__(256) uint8_t scratch[kNaBytes];
+
+namespace {
+
+// The current device's address of `scratch` (taken on its first call there)
+hipError_t na_scratch(uint8_t** p) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_na_mu);
+    if (!g_na_scratch[dev]) {
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        g_na_scratch[dev] = ptr;
+    }
+    *p = (uint8_t*)g_na_scratch[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 namespace moe {
@@ -446,6 +492,61 @@ int moe_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* pack
     return MOE_OK;
 }
 
+int moe_mxfp4_forward_noalloc(const void* x, const float* router_logits, int64_t num_tokens,
+                              int32_t top_k, int64_t num_experts, int64_t hidden, int64_t inter,
+                              const uint8_t* W_gate_up, const uint8_t* W_down,
+                              const moe_mxfp4_scales* scales, void* out, void* stream) {
+    if (num_tokens < 0) return MOE_E_SHAPE;
+    if (num_tokens == 0) return MOE_OK;
+    if (num_experts < 1 || hidden < 128 || hidden % 128 || inter < 128 || inter % 128)
+        return MOE_E_SHAPE;
+    if (top_k < 1 || top_k > num_experts) return MOE_E_TOPK;
+    // the fixed scratch limits, and the self-routed layer's own bounds
+    if (num_tokens > kNaMaxTokens || num_experts > kNaMaxExperts || top_k > kNaMaxTopK ||
+        hidden > kNaMaxHidden || inter > kNaMaxInter || num_tokens * num_experts > moe::kSelfMaxPairs ||
+        num_tokens * top_k >= (int64_t)moe::kSelfMaxMeanTok * num_experts)
+        return MOE_E_LIMIT;
+    if (!x || !router_logits || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
+    if (!scales->gate_up || !scales->down) return MOE_E_NULL;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(W_gate_up) || !aligned16(W_down) ||
+        !aligned16(scales->gate_up) || !aligned16(scales->down) || !aligned16(out))
+        return MOE_E_ALIGN;
+    uint8_t* base = nullptr;
+    hipError_t err = na_scratch(&base);
+    if (err != hipSuccess) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+    hipStream_t st = (hipStream_t)stream;
+    const int T = (int)num_tokens, E = (int)num_experts, H = (int)hidden, I = (int)inter;
+    moe::GemmArgs a{};
+    a.x = (const uint16_t*)x;
+    a.logits = router_logits;
+    a.T = T;
+    a.E = E;
+    a.k = top_k;
+    a.H = H;
+    a.I = I;
+    a.wgu = W_gate_up;
+    a.sgu = scales->gate_up;
+    a.wdn = W_down;
+    a.sdn = scales->down;
+    a.slot_lists = (int32_t*)(base + kNaLists);
+    a.route_ids = (int32_t*)(base + kNaIds);
+    a.route_wts = (float*)(base + kNaWts);
+    a.wts = a.route_wts;
+    a.pos = nullptr;  // h and y rows are the slots
+    a.h3q = base + kNaH3q;
+    a.h3s = base + kNaH3s;
+    a.y = (float*)(base + kNaY);
+    a.out = (uint16_t*)out;
+    // every piece is written before it is read (lists, routing weights, the
+    // h and y rows of every slot): nothing needs clearing between calls
+    const bool lists = (int64_t)E * (I / 32 + H / 128) >= moe::kSelfListUnits;
+    if (lists && (err = moe::launch_slot_lists(a, st)) != hipSuccess) return hip_fail(err, "slot lists");
+    if ((err = moe::launch_self_gate_up(a, lists, st)) != hipSuccess) return hip_fail(err, "gate_up");
+    if ((err = moe::launch_self_down(a, lists, st)) != hipSuccess) return hip_fail(err, "down");
+    if ((err = moe::launch_combine(a, st)) != hipSuccess) return hip_fail(err, "combine");
+    return MOE_OK;
+}
+
 const char* moe_mxfp4_status_string(int status) {
     switch (status) {
         case MOE_OK: return "ok";
@@ -457,6 +558,9 @@ const char* moe_mxfp4_status_string(int status) {
         case MOE_E_NOT_INIT: return "moe_mxfp4_init was not called for the current device";
         case MOE_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
         case MOE_E_OPTION: return "an option value is not recognised";
+        case MOE_E_LIMIT:
+            return "the layer exceeds the fixed limits of moe_mxfp4_forward_noalloc (at most 16 tokens, "
+                   "256 experts, top-8, hidden 8192, inter 4096; T*E <= 4096, T*top_k < 8*E)";
         default: return "unknown status";
     }
 }

@@ -35,7 +35,7 @@ def test_header_declares_the_abi():
         "moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward", "moe_mxfp4_forward_ex",
         "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_mxfp4_prepack",
         "moe_mxfp8_quantize", "moe_mxfp8_prepack", "moe_probe_stream_read",
-        "moe_probe_sink_words", "moe_probe_copy"])
+        "moe_probe_sink_words", "moe_probe_copy", "moe_mxfp4_forward_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         s = L.moe_mxfp4_status_string(code)
         assert s and s != "unknown status"
     assert L.moe_mxfp4_status_string(-99) == "unknown status"
@@ -130,6 +130,33 @@ def test_forward_validation_without_gpu(L):
     assert _fwd(L, opt=whole) == L.MOE_E_NOT_INIT         # a valid request
     whole.shared_down_scales = 0xB004
     assert _fwd(L, opt=whole) == L.MOE_E_ALIGN
+
+
+def _noalloc(L, x=0x1000, lg=0x2000, T=9, k=8, E=64, H=6144, I=2048, wgu=0x3000, wdn=0x4000,
+             sgu=0x5000, sdn=0x6000, out=0x7000):
+    sc = L.moe_mxfp4_scales(sgu, sdn)
+    return L.lib().moe_mxfp4_forward_noalloc(x, lg, T, k, E, H, I, wgu, wdn, ctypes.byref(sc), out,
+                                             None)
+
+
+def test_noalloc_validation_without_gpu(L):
+    """The allocation-free entry point rejects, before any HIP call, every
+    layer past its fixed limits (MOE_E_LIMIT) and bad pointers or sizes; a
+    valid-looking call then fails at its first HIP call (no device here)."""
+    assert _noalloc(L, T=0) == L.MOE_OK
+    assert _noalloc(L, T=-1) == L.MOE_E_SHAPE
+    assert _noalloc(L, H=6100) == L.MOE_E_SHAPE
+    assert _noalloc(L, k=0) == L.MOE_E_TOPK
+    assert _noalloc(L, k=65) == L.MOE_E_TOPK
+    for kw in (dict(T=17), dict(E=300), dict(k=9), dict(H=8192 + 128), dict(I=4096 + 128),
+               dict(T=16, E=257), dict(T=16, k=4, E=8)):  # T*top_k >= 8*E: not a self-routed layer
+        assert _noalloc(L, **kw) == L.MOE_E_LIMIT, kw
+    assert "16 tokens" in L.moe_mxfp4_status_string(L.MOE_E_LIMIT)
+    assert _noalloc(L, x=0) == L.MOE_E_NULL
+    assert _noalloc(L, sdn=0) == L.MOE_E_NULL
+    assert _noalloc(L, out=0x7008) == L.MOE_E_ALIGN
+    if not gpu_available():
+        assert _noalloc(L) == L.MOE_E_HIP
 
 
 def test_quantize_validation(L):
