@@ -54,10 +54,11 @@ def parse():
     p.add_argument("--path", type=int, default=0,
                    help="1: VALU GEMV over row-major weights; 2 (default): bf16 MFMA over "
                         "the tile layout (weights prepacked once before timing)")
-    p.add_argument("--launch", choices=["auto", "split", "self"], default="auto",
+    p.add_argument("--launch", choices=["auto", "split", "self", "fused"], default="auto",
                    help="bf16 MFMA path: auto (the library's choice: self-routed for at most "
                         "16 tokens), split (routing kernel, then the GEMMs), self (no routing "
-                        "kernel: each GEMM workgroup ranks its own expert)")
+                        "kernel: each GEMM workgroup ranks its own expert), fused (one "
+                        "persistent launch: the whole layer for at most 16 tokens)")
     p.add_argument("--router", action="store_true",
                    help="compute the router logits in the layer from a bf16 router weight [E, H] "
                         "(x . W_router^T on the matrix cores) instead of taking them as input")
@@ -208,11 +209,14 @@ def main():
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
 
     launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
-              "self": M.MOE_LAUNCH_SELF_ROUTED}[args.launch]
+              "self": M.MOE_LAUNCH_SELF_ROUTED, "fused": M.MOE_LAUNCH_FUSED}[args.launch]
     wide = cfg.T * cfg.k >= 4 * cfg.E  # the library's wide items (experts average >= 4 tokens)
     self_ok = (path == M.MOE_PATH_MFMA and not mx8 and cfg.T * cfg.k < 8 * cfg.E and cfg.T <= 16
                and cfg.T * cfg.E <= 4096)
     self_routed = self_ok and launch in (M.MOE_LAUNCH_AUTO, M.MOE_LAUNCH_SELF_ROUTED)
+    # one launch for the whole layer (the single-launch kernel's time is the
+    # "gate_up" stage, and it moves every touched byte)
+    fused = path == M.MOE_PATH_MFMA and not mx8 and launch == M.MOE_LAUNCH_FUSED
 
     router = None
     if args.router:
@@ -315,6 +319,8 @@ def main():
     # kernels when the experts average >= 4 tokens each; the self-routed one
     # for at most 16 tokens unless the split launch is asked for)
     kname = ("mx8_gate_up_kernel" if mx8 else
+             ("self_fused_kernel" if self_ok else "wide_fused_kernel" if wide else "mfma_fused_kernel")
+             if fused else
              "self_gate_up_kernel" if self_routed else
              ("wide_gate_up_kernel" if wide else "mfma_gate_up_kernel") if path == M.MOE_PATH_MFMA
              else "gemv_gate_up_kernel")
@@ -328,7 +334,8 @@ def main():
     us = ms_per_step * 1e3
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     gu_ms = stage_ms["gate_up"]
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    kbytes = total_bytes if fused else gu_bytes  # the single launch moves every byte
+    gu_gbs = kbytes / (gu_ms * 1e-3) / 1e9
     S = cfg.T * cfg.k
     S_all = S + (cfg.T if shared is not None else 0)  # rows through the FFN
     gu_flops = 2.0 * S_all * 2 * cfg.I * cfg.H
@@ -345,12 +352,13 @@ def main():
                 "algorithmic_bytes_per_launch": int(gu_bytes)}
     else:
         roof = {"bound": "hbm",
-                "kernel": kname + " (fused gate+up MXFP4 GEMM + SiLU*up)",
+                "kernel": kname + (" (the whole layer in one launch)" if fused else
+                                   " (fused gate+up MXFP4 GEMM + SiLU*up)"),
                 "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(cfg.name, kname),
                 "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
-                "algorithmic_bytes_per_launch": int(gu_bytes)}
+                "algorithmic_bytes_per_launch": int(kbytes)}
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -372,7 +380,8 @@ def main():
                        max_tokens_per_expert=int(counts_np.max()),
                        touched_weight_bytes=int(total_bytes),
                        gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
-                       launch="self_routed" if self_routed else "split",
+                       launch=("single_launch" if fused else "self_routed" if self_routed else
+                               "split"),
                        router="computed in the layer from W_router [E,H] bf16" if router is not None
                        else "logits given",
                        weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",

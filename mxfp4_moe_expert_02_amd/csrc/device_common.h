@@ -209,7 +209,7 @@ __device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const f
         }
     }
     if (g == 0) {
-        uint32_t* d = reinterpret_cast<uint32_t*>(a.h3s + row * (a.I / 8) + (chunk * 4 + b) * 4);
+        uint32_t* d = reinterpret_cast<uint32_t*>(a.h3s + row * h3s_stride(a.I) + (chunk * 4 + b) * 4);
         if constexpr (PUBLISH)
             __hip_atomic_store(d, scales, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -233,11 +233,12 @@ __device__ inline void wait_count(const int32_t* count, int need, int32_t* err) 
 }
 
 // sum_j w[t,j] * y[pos[t,j], n] over the k slots of token t, in slot order
-// j = 0..k-1, fp32, plus the shared expert's y[sh_row0 + t, n] if there is one.  y is read with agent-coherent loads because other
-// workgroups of the running kernel wrote it.  The slot indices and weights,
-// then the y values, are fetched 8 slots at a time with unconditional loads
-// (indices clamped to k-1), so each batch costs two memory latencies rather
-// than two per slot.
+// j = 0..k-1, fp32, plus the shared expert's y[sh_row0 + t, n] if there is
+// one.  Everything is read with agent-coherent loads: other workgroups of
+// the running kernel may have written it, on another XCD.  The slot indices
+// and weights, then the y values, are fetched 8 slots at a time with
+// unconditional loads (indices clamped to k-1), so each batch costs two
+// memory latencies rather than two per slot.
 __device__ inline float combine_column(const GemmArgs& a, int t, int n) {
     const int64_t base = (int64_t)t * a.k;
     float v = 0.f;
@@ -247,8 +248,9 @@ __device__ inline float combine_column(const GemmArgs& a, int t, int n) {
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int j = min(j0 + u, a.k - 1);
-            p[u] = a.pos[base + j];
-            w[u] = a.wts[base + j];
+            p[u] = a.pos ? __hip_atomic_load(a.pos + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : (int)(base + j);  // no pos: rows are the slots
+            w[u] = __hip_atomic_load(a.wts + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int u = 0; u < 8; u++)
@@ -307,19 +309,14 @@ struct ListRows {
 // One wave's share of a down-projection tile: acc[rg][t] holds rows 4g..4g+3
 // of row group rg of output quad `quad` (columns 64q + 16rg + 4g + i of out)
 // for token row 16t + c of the item (lane (c, g), the 16x16 MFMA D layout).
-// Each token's values go to its y row (rows.row).
-//
-// COMBINE = false (split launch): plain 16-byte stores; the combine runs as
-// its own kernel after this one (combine.hip), which the kernel boundary
-// makes see every y row.  COMBINE = true (single-launch layer): the y rows
-// go out through agent-coherent stores, then the wave counts its (token,
-// quad) tiles done and the wave that completes a token's k experts on the
-// quad combines those 64 columns (the last finisher), in slot order.
-template <int NT, bool COMBINE, typename Rows>
+// Each token's values go to its y row (rows.row): plain 16-byte stores when
+// a later kernel combines (the kernel boundary makes them visible), or,
+// with PUBLISH (a single-launch layer, whose own workgroups combine after
+// grid_combine's barrier), agent-coherent stores.
+template <int NT, bool PUBLISH, typename Rows>
 __device__ inline void store_down_tile(const GemmArgs& a, int quad, const Rows& rows,
                                        const f32x4_t (&acc)[4][NT]) {
     const int m = rows.m;
-    const int quads = a.H / 64;
     const int lane = threadIdx.x % kWave, c = lane % 16, g = lane / 16;
     const int n0 = 64 * quad;
 #pragma unroll
@@ -329,12 +326,11 @@ __device__ inline void store_down_tile(const GemmArgs& a, int quad, const Rows& 
         float* dst = a.y + (int64_t)rows.row(j) * a.H + n0 + 4 * g;
 #pragma unroll
         for (int rg = 0; rg < 4; rg++) {
-            if (!COMBINE) {
+            if (!PUBLISH) {
                 *reinterpret_cast<float4*>(dst + 16 * rg) =
                     make_float4(acc[rg][t][0], acc[rg][t][1], acc[rg][t][2], acc[rg][t][3]);
                 continue;
             }
-            // agent-coherent stores: the combining wave may run on another XCD
             const uint64_t lo = (uint64_t)__float_as_uint(acc[rg][t][0]) |
                                 ((uint64_t)__float_as_uint(acc[rg][t][1]) << 32);
             const uint64_t hi = (uint64_t)__float_as_uint(acc[rg][t][2]) |
@@ -345,26 +341,43 @@ __device__ inline void store_down_tile(const GemmArgs& a, int quad, const Rows& 
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if constexpr (COMBINE) {  // routed items only (rows.row0)
-        // every y store of this wave has completed before it counts the tiles
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        for (int j0 = 0; j0 < m; j0 += kWave) {
-            const int j = j0 + lane;
-            int token = -1;
-            bool last = false;
-            if (j < m) {
-                token = a.sorted[rows.row0 + j] / a.k;
-                last = atomicAdd(&a.tile_done[token * quads + quad], 1) == a.k - 1;
-            }
-            uint64_t todo = __ballot(last);
-            while (todo) {
-                const int src = __builtin_ctzll(todo);
-                todo &= todo - 1;
-                const int t = __builtin_amdgcn_readlane(token, src);
-                // out[t, n0 + lane] = sum_j w[t,j] * y[pos[t,j], n0 + lane], slot order
-                a.out[(int64_t)t * a.H + n0 + lane] = f32_to_bf16_rne(combine_column(a, t, n0 + lane));
-            }
+}
+
+// The combine of a single-launch layer, run by every workgroup once its
+// unit queue is exhausted.  Each wave first waits for its own stores (y
+// rows, h, routing) to complete; then the workgroup adds the units it ran,
+// `units`, to `done`.  The workgroup whose addition brings `done` to
+// `total`, the units of the whole queue, has seen every y row of the layer
+// completed and raises the kGoLines flags at `go` (kGoStride words apart);
+// every other workgroup waits (bounded; `err` raised on giving up) for its
+// flag, b % kGoLines (one line per 8 or so pollers, rather than the whole
+// grid on `done`).  Units are held only by running workgroups, which finish
+// them without waiting on anything dequeued later, so the wait ends whether
+// or not the whole grid is resident at once.  Then out[t, n] for all T x H
+// outputs, one per thread, grid-stride, in the combine kernel's order
+// (combine_column).  A combine per (token, column tile) by its last
+// finisher instead costs every down unit a store drain, a counter round
+// trip and a share of the combines while its workgroup's other waves wait
+// at the next unit's barrier: measured on the 9-token, 64-expert layer,
+// about 13 us of epilogue per unit and twice the layer time.
+__device__ inline void grid_combine(const GemmArgs& a, int units, int total, int32_t* done, int32_t* go,
+                                    int32_t* err) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores completed
+    __syncthreads();
+    if (threadIdx.x == 0 && total > 0) {
+        const bool last = units > 0 && atomicAdd(done, units) + units == total;
+        if (last) {
+            for (int i = 0; i < kGoLines; i++)
+                __hip_atomic_store(go + i * kGoStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            wait_count(go + (blockIdx.x % kGoLines) * kGoStride, 1, err);
         }
+    }
+    __syncthreads();
+    const int64_t n_out = (int64_t)a.T * a.H, stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += stride) {
+        const int t = (int)(i / a.H), n = (int)(i % a.H);
+        a.out[i] = f32_to_bf16_rne(combine_column(a, t, n));
     }
 }
 

@@ -216,8 +216,9 @@ constexpr int kFusedWavesPerEu = 2;  // launch bound of the single-launch kernel
 
 // The expert layer after routing in one persistent launch: every workgroup
 // dequeues units from one counter, first the gate_up units (item, quad),
-// then the down units (item, quad pair), until the queue is exhausted.  A
-// down unit first waits until all I/32 gate_up units of its item are done.
+// then the down units (item, quad pair), until the queue is exhausted, and
+// then the grid combines (grid_combine).  A down unit first waits until
+// all I/32 gate_up units of its item are done.
 // No wait can deadlock: the units a down unit waits for were dequeued
 // before it, by workgroups that are running and never wait themselves.
 // The wait is bounded (wait_count) and raises queue[kQueueError] if it ever
@@ -242,9 +243,11 @@ mfma_fused_kernel(GemmArgs a) {
     const int n_gu = n_items * gu_units, n_all = n_gu + n_items * dn_units;
     if (threadIdx.x == 0) s_unit[0] = atomicAdd(&a.queue[kQueueNext], 1);
     __syncthreads();
+    int n_run = 0;  // units this workgroup ran
     for (int cur = 0;; cur ^= 1) {
         const int u = uniform(s_unit[cur]);
-        if (u >= n_all) return;
+        if (u >= n_all) break;
+        n_run++;
         // read by every wave after this unit's barrier
         if (threadIdx.x == 0) s_unit[cur ^ 1] = atomicAdd(&a.queue[kQueueNext], 1);
         if (u < n_gu) {
@@ -256,12 +259,12 @@ mfma_fused_kernel(GemmArgs a) {
                                     SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
             if (threadIdx.x < kWave) {  // wave 0 stored the h rows
                 __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): they are complete
-                if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
+                if (threadIdx.x == 0) atomicAdd(&a.gu_done[(int64_t)item * kLineInts], 1);
             }
         } else {
             const int v = u - n_gu, item = v / dn_units;
             const int4 it = a.items[item];
-            if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
+            if (threadIdx.x == 0) wait_count(&a.gu_done[(int64_t)item * kLineInts], gu_units, &a.queue[kQueueError]);
             __syncthreads();
             const int64_t e = uniform(it.x);
             down_item<1, true, W4>(a, v % dn_units, a.wdn + e * (a.H / 64) * (a.I / 128) * 4096,
@@ -269,9 +272,140 @@ mfma_fused_kernel(GemmArgs a) {
                                        SortedRows{uniform(it.y), uniform(it.z)}, red[cur]);
         }
     }
+    grid_combine(a, n_run, n_all, &a.queue[kQueueDone], &a.queue[kQueueGo], &a.queue[kQueueError]);
 }
 
 constexpr int kSharedWideTok = 64;
+
+// ---- the self-routed layer in one launch.  The pages run a model as one
+// persistent engine kernel so that no launch, synchronisation or
+// global-memory round trip between operators is left exposed once a step
+// takes microseconds (tilert.ai blog, first leap; bjdmk.com.cn news page,
+// road to 1000 tokens/s); here the whole expert layer of at most 16 tokens
+// -- routing weights, per-expert slot lists, gate_up, down and the combine
+// -- is one launch of resident workgroups dequeuing units from one counter,
+// in this order:
+//   0                the routing weights (rank-count top-k of every token)
+//   1 .. L           slot lists of experts 4(u-1) .. 4(u-1)+3, one per wave
+//   shared gate_up   (with a shared expert) its I/32 quads over all tokens
+//   routed gate_up   (e, quad) for e < E, quad < I/32
+//   shared down      (with a shared expert) its quad pairs over all tokens
+//   routed down      (e, pair) for e < E, pair < ceil(H/128)
+// and then the combine of every output over the whole grid (grid_combine).
+// A gate_up unit of e waits until e's list is written; a down unit until
+// every gate_up unit of its expert has published h.  Every wait is on units
+// dequeued earlier by running workgroups that never wait on later ones, so
+// none can deadlock; each is bounded (wait_count) and raises the error flag
+// if it ever gives up.  Units of experts no token chose exit after reading
+// m = 0.  The arithmetic and its order are those of the split launch (same
+// item bodies; the combine's fmaf chain is the combine kernel's), so the
+// output has its bits.  The last workgroup to finish the combine clears the
+// counters for the next launch (every other workgroup has passed its last
+// wait by then).
+__device__ inline void wait_flag(const int32_t* count, int need, int32_t* err) {
+    if (threadIdx.x == 0) wait_count(count, need, err);
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(kFusedWavesPerEu)))
+self_fused_kernel(GemmArgs a, int32_t* flags) {
+    __shared__ __attribute__((aligned(16))) float s_lg[kSelfLdsFloats];  // the weights unit
+    __shared__ f32x4_t red[2][kRedGateUp];
+    __shared__ int s_unit[2];
+    const int E = a.E, quads = a.I / 32, pairs = (a.H / 64 + 1) / 2;
+    const bool sh = a.sh_wgu != nullptr;
+    // one line per counter (kLineInts words apart): list ready of expert e,
+    // gate_up units done of expert e (index E: the shared expert)
+    int32_t* list_ready = flags;
+    int32_t* gu_done = flags + (int64_t)(E + 1) * kLineInts;
+    int32_t* misc = flags + self_misc_word(E);  // SelfFlags
+    int32_t* go = flags + self_go_word(E);
+    const int n_lists = (E + 3) / 4;
+    const int u_sgu = 1 + n_lists, u_gu = u_sgu + (sh ? quads : 0);
+    const int u_sdn = u_gu + E * quads, u_dn = u_sdn + (sh ? pairs : 0);
+    const int n_all = u_dn + E * pairs;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    if (threadIdx.x == 0) s_unit[0] = atomicAdd(&misc[kSelfNext], 1);
+    __syncthreads();
+    int n_run = 0;  // units this workgroup ran
+    for (int cur = 0;; cur ^= 1) {
+        const int u = uniform(s_unit[cur]);
+        if (u >= n_all) break;
+        n_run++;
+        if (threadIdx.x == 0) s_unit[cur ^ 1] = atomicAdd(&misc[kSelfNext], 1);
+        if (u == 0) {  // the routing weights and ids of every slot (read by the combine)
+            for (int i = threadIdx.x; i < a.T * E; i += blockDim.x) s_lg[i] = a.logits[i];
+            __syncthreads();
+            float* sel_l = s_lg + a.T * E;
+            int* sel_id = reinterpret_cast<int*>(sel_l + a.T * a.k);
+            topk_tokens<true>(s_lg, a.T, 0, E, a.k, sel_id, sel_l, a.route_ids, a.route_wts);
+        } else if (u < u_sgu) {  // slot lists, one expert per wave
+            const int e = 4 * (u - 1) + w;
+            if (e < E) {
+                int slot;
+                const int m = expert_slots(a.logits, a.T, E, a.k, e, &slot);
+                int32_t* list = a.slot_lists + e * kSlotListInts;
+                if (lane < m) __hip_atomic_store(&list[1 + lane], slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0) __hip_atomic_store(&list[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the list is stored
+                if (lane == 0) __hip_atomic_store(&list_ready[(int64_t)e * kLineInts], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+        } else if (u < u_gu) {  // the shared expert's gate_up quads (every token)
+            gate_up_item<1, W8, XB, true>(a, u - u_sgu, a.sh_wgu, a.sh_sgu, TokenRows{0, a.T, a.sh_row0},
+                                          red[cur]);
+            if (threadIdx.x < kWave) {  // wave 0 stored the h rows
+                __builtin_amdgcn_s_waitcnt(0x0f70);
+                if (threadIdx.x == 0) atomicAdd(&gu_done[(int64_t)E * kLineInts], 1);
+            }
+        } else if (u < u_sdn) {  // routed gate_up (e, quad)
+            const int e = (u - u_gu) / quads, quad = (u - u_gu) % quads;
+            wait_flag(&list_ready[(int64_t)e * kLineInts], 1, &misc[kSelfError]);
+            const int32_t* list = a.slot_lists + e * kSlotListInts;
+            const int m = uniform(__hip_atomic_load(list, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (m > 0) {
+                gate_up_item<1, W4, XB, true>(a, quad, a.wgu + (int64_t)e * quads * (a.H / 128) * 4096,
+                                              a.sgu + (int64_t)e * quads * (a.H / 128) * 256,
+                                              ListRows{m, list + 1}, red[cur]);
+                if (threadIdx.x < kWave) {
+                    __builtin_amdgcn_s_waitcnt(0x0f70);
+                    if (threadIdx.x == 0) atomicAdd(&gu_done[(int64_t)e * kLineInts], 1);
+                }
+            }
+        } else if (u < u_dn) {  // the shared expert's down quad pairs
+            wait_flag(&gu_done[(int64_t)E * kLineInts], quads, &misc[kSelfError]);
+            down_item<1, true, W8P>(a, u - u_sdn, a.sh_wdn, a.sh_sdn, TokenRows{0, a.T, a.sh_row0},
+                                    red[cur]);
+        } else {  // routed down (e, pair)
+            const int e = (u - u_dn) / pairs, pair = (u - u_dn) % pairs;
+            wait_flag(&list_ready[(int64_t)e * kLineInts], 1, &misc[kSelfError]);
+            const int32_t* list = a.slot_lists + e * kSlotListInts;
+            const int m = uniform(__hip_atomic_load(list, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (m > 0) {
+                wait_flag(&gu_done[(int64_t)e * kLineInts], quads, &misc[kSelfError]);
+                down_item<1, true, W4>(a, pair, a.wdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 4096,
+                                       a.sdn + (int64_t)e * (a.H / 64) * (a.I / 128) * 256,
+                                       ListRows{m, list + 1}, red[cur]);
+            }
+        }
+    }
+    grid_combine(a, n_run, n_all, &misc[kSelfDone], go, &misc[kSelfError]);
+    // exit: the last workgroup out clears the counters for the next launch
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = atomicAdd(&misc[kSelfExits], 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = threadIdx.x; i < 2 * (E + 1); i += blockDim.x) flags[(int64_t)i * kLineInts] = 0;
+    for (int i = threadIdx.x; i < kGoLines; i += blockDim.x) go[i * kGoStride] = 0;
+    if (threadIdx.x == 0) {
+        misc[kSelfErrorOut] = misc[kSelfError];
+        misc[kSelfError] = 0;
+        misc[kSelfNext] = 0;
+        misc[kSelfDone] = 0;
+        misc[kSelfExits] = 0;
+    }
+}
 
 }  // namespace
 
@@ -328,6 +462,16 @@ hipError_t launch_self_down(const GemmArgs& a, bool lists, hipStream_t stream) {
         self_down_kernel<true><<<grid, kMfmaThreads, 0, stream>>>(a);
     else
         self_down_kernel<false><<<grid, kMfmaThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_self_fused(const GemmArgs& a, int32_t* flags, hipStream_t stream) {
+    const int quads = a.I / 32, pairs = (a.H / 64 + 1) / 2;
+    const int64_t units = 1 + (a.E + 3) / 4 + (int64_t)(a.E + (a.sh_wgu ? 1 : 0)) * (quads + pairs);
+    int grid = 0;
+    hipError_t err = resident_grid(reinterpret_cast<const void*>(self_fused_kernel), kMfmaThreads, &grid);
+    if (err != hipSuccess) return err;
+    self_fused_kernel<<<(int)(units < grid ? units : grid), kMfmaThreads, 0, stream>>>(a, flags);
     return hipGetLastError();
 }
 

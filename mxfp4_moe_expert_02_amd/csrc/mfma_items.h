@@ -130,7 +130,7 @@ struct XQ3 {
         uint32_t s;
     };
     static __device__ Row hrow(const GemmArgs& a, int r) {
-        return Row{a.h3q + (int64_t)r * 3 * a.I, a.h3s + (int64_t)r * (a.I / 8)};
+        return Row{a.h3q + (int64_t)r * 3 * a.I, a.h3s + (int64_t)r * h3s_stride(a.I)};
     }
     static __device__ void load(const Row& r, int chunk, int g, Chunk& c) {
         const uint4* src = reinterpret_cast<const uint4*>(r.q + (chunk * 4 + g) * 96);
@@ -350,8 +350,8 @@ __device__ inline void gate_up_item(const GemmArgs& a, int quad, const uint8_t* 
 // down body for items of NT column tiles (see mfma_down_kernel), token rows
 // from `rows`; dn/dns: the expert's down tiles (format W: W4, or W8P for
 // MXFP8 weights), h as three MXFP8 terms on the scaled matrix cores (XQ3);
-// COMBINE: see store_down_tile
-template <int NT, bool COMBINE, typename W, typename Rows>
+// PUBLISH: see store_down_tile
+template <int NT, bool PUBLISH, typename W, typename Rows>
 __device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
                                  const uint8_t* dns, const Rows& rows, f32x4_t* red) {
     const int m = rows.m;
@@ -386,7 +386,7 @@ __device__ inline void down_item(const GemmArgs& a, int pair, const uint8_t* dn,
     for (int rg = 0; rg < kGroups; rg++)
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rg][t] += red[(((w >> 1) * kGroups + rg) * NT + t) * kWave + lane];
-    store_down_tile<NT, COMBINE>(a, quad, rows, acc);
+    store_down_tile<NT, PUBLISH>(a, quad, rows, acc);
 }
 
 // ---- the shared expert: MXFP8 weights, every token.  The pages keep all

@@ -173,7 +173,7 @@ __device__ inline void q_stage_init(const GemmArgs& a, const Rows& rows, QStage<
     const int n = threadIdx.x / kTpr, l = threadIdx.x % kTpr;
     const int64_t r = rows.row(min(n, rows.m - 1));
     st.q = a.h3q + r * 3 * a.I + 16 * l;
-    st.sc = a.h3s + r * (a.I / 8);
+    st.sc = a.h3s + r * h3s_stride(a.I);
 }
 
 template <int NT>
@@ -276,7 +276,7 @@ __device__ inline void wide_gate_up(const GemmArgs& a, int qb, int e, int row0, 
 
 // Down quads 4qb .. 4qb+3 of expert e (one per wave) for the token rows
 // `rows` (SortedRows of a routed item, or ListRows of a self-routed expert)
-template <int NT, bool COMBINE, typename Rows>
+template <int NT, bool PUBLISH, typename Rows>
 __device__ inline void wide_down(const GemmArgs& a, int qb, int e, const Rows& rows, WQSmem& sm) {
     const int w = threadIdx.x / kWave;
     const int chunks = a.I / 128, quads = a.H / 64;
@@ -287,7 +287,7 @@ __device__ inline void wide_down(const GemmArgs& a, int qb, int e, const Rows& r
     wide_mainloop_q3<NT>(a, a.wdn + quad_id * chunks * 4096, a.sdn + quad_id * chunks * 256, live, rows,
                          chunks, sm, acc);
     if (!live) return;
-    store_down_tile<NT, COMBINE>(a, quad, rows, acc);
+    store_down_tile<NT, PUBLISH>(a, quad, rows, acc);
 }
 
 // Call fn(std::integral_constant<int, NT>) for an item of m tokens: NT =
@@ -347,8 +347,7 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_down_kernel(G
 // The wide kernels in one persistent launch (see mfma_fused_kernel in
 // mfma.hip: the same queue, publication and bounded wait; a gate_up unit
 // is (item, quad block of four quads), and every wave stores h of its quad;
-// a down unit is (item, quad block), and the last finisher of a token's k
-// experts on a quad combines it).
+// a down unit is (item, quad block); the grid combines at the end).
 __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(GemmArgs a) {
     __shared__ union {
         WSmem x;
@@ -364,9 +363,11 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
     // which never waits
     if (threadIdx.x == 0) s_unit[0] = atomicAdd(&a.queue[kQueueNext], 1);
     __syncthreads();
+    int n_run = 0;  // units this workgroup ran
     for (int cur = 0;; cur ^= 1) {
         const int u = uniform(s_unit[cur]);
-        if (u >= n_all) return;
+        if (u >= n_all) break;
+        n_run++;
         if (threadIdx.x == 0) s_unit[cur ^ 1] = atomicAdd(&a.queue[kQueueNext], 1);
         if (u < n_gu) {
             const int item = u / gu_units, qb = u % gu_units;
@@ -375,12 +376,12 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
             by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value, true>(a, qb, e, row0, m, sm.x); });
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's h stores completed
             __syncthreads();
-            if (threadIdx.x == 0) atomicAdd(&a.gu_done[item], 1);
+            if (threadIdx.x == 0) atomicAdd(&a.gu_done[(int64_t)item * kLineInts], 1);
         } else {
             const int v = u - n_gu, item = v / dn_units, qb = v % dn_units;
             const int4 it = a.items[item];
             const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
-            if (threadIdx.x == 0) wait_count(&a.gu_done[item], gu_units, &a.queue[kQueueError]);
+            if (threadIdx.x == 0) wait_count(&a.gu_done[(int64_t)item * kLineInts], gu_units, &a.queue[kQueueError]);
             __syncthreads();
             by_tiles(m, [&](auto nt) {
                 wide_down<decltype(nt)::value, true>(a, qb, e, SortedRows{row0, m}, sm.q);
@@ -388,6 +389,7 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
         }
         __syncthreads();  // LDS free for the next unit, whose index is now visible
     }
+    grid_combine(a, n_run, n_all, &a.queue[kQueueDone], &a.queue[kQueueGo], &a.queue[kQueueError]);
 }
 
 }  // namespace

@@ -66,8 +66,9 @@ size_t layout(Workspace* ws, char* base) {
     ws->bhist = (int32_t*)take((S + moe::kRouteSlotBlock - 1) / moe::kRouteSlotBlock * ws->E * 4);
     ws->max_items = (int)(ws->E + S / moe::kMfmaTok + 1);
     ws->queue = (int32_t*)take(moe::kQueueWords * 4);
-    ws->gu_done = (int32_t*)take((size_t)ws->max_items * 4);
+    ws->gu_done = (int32_t*)take((size_t)ws->max_items * moe::kLineInts * 4);
     ws->slot_lists = (int32_t*)take((size_t)ws->E * moe::kSlotListInts * 4);
+    ws->flags = (int32_t*)take((size_t)moe::self_flag_words(ws->E) * 4);
     const size_t TE = (size_t)ws->max_tokens * ws->E;
     const size_t split_te = TE < (size_t)moe::kRouterWaves * 512 ? TE : (size_t)moe::kRouterWaves * 512;
     ws->logits = (float*)take(TE * 4);
@@ -76,7 +77,7 @@ size_t layout(Workspace* ws, char* base) {
     const size_t R = S + (size_t)ws->max_tokens;  // routed rows, then the shared expert's
     ws->h = (uint16_t*)take(R * ws->I * 4);  // bf16 hi/lo pairs (GEMV path)
     ws->h3q = (uint8_t*)take(R * ws->I * 3);  // three MXFP8 terms (matrix-core paths)
-    ws->h3s = (uint8_t*)take(R * (ws->I / 8));
+    ws->h3s = (uint8_t*)take(R * moe::h3s_stride(ws->I));
     ws->y = (float*)take(R * ws->H * 4);
     ws->x_codes = (uint8_t*)take((size_t)ws->max_tokens * ws->H);
     ws->x_scales = (uint8_t*)take((size_t)ws->max_tokens * (ws->H / 32));
@@ -119,8 +120,8 @@ constexpr size_t kNaLists = 0;  // [E][kSlotListInts] int32: per-expert slot lis
 constexpr size_t kNaIds = kNaLists + (size_t)kNaMaxExperts * moe::kSlotListInts * 4;  // [T*k] int32
 constexpr size_t kNaWts = kNaIds + kNaRows * 4;                                       // [T*k] fp32
 constexpr size_t kNaH3q = kNaWts + kNaRows * 4;                          // [T*k][3I] h's term codes
-constexpr size_t kNaH3s = kNaH3q + kNaRows * 3 * (size_t)kNaMaxInter;      // [T*k][I/8] their scales
-constexpr size_t kNaY = kNaH3s + kNaRows * (size_t)kNaMaxInter / 8;        // [T*k][H] fp32
+constexpr size_t kNaH3s = kNaH3q + kNaRows * 3 * (size_t)kNaMaxInter;      // [T*k][h3s_stride(I)] their scales
+constexpr size_t kNaY = kNaH3s + kNaRows * (size_t)moe::h3s_stride(kNaMaxInter);  // [T*k][H] fp32
 constexpr size_t kNaBytes = kNaY + kNaRows * (size_t)kNaMaxHidden * 4;     // 5.6 MB
 static_assert(kNaH3q % 256 == 0 && kNaH3s % 256 == 0 && kNaY % 256 == 0, "aligned pieces");
 
@@ -303,7 +304,10 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
                          (int64_t)T * k < (int64_t)moe::kSelfMaxMeanTok * E;
     // (decided before anything is enqueued: a rejected call enqueues nothing)
     if (o.launch == MOE_LAUNCH_SELF_ROUTED && !self_ok) return MOE_E_OPTION;
-    const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO);
+    // FUSED on such a layer: the whole layer in one launch
+    const bool self_fused = self_ok && o.launch == MOE_LAUNCH_FUSED;
+    const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO ||
+                                  self_fused);
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
     if (o.router_weight) {  // the router linear layer, ahead of the routing
@@ -323,8 +327,9 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         err = moe::launch_route(router_logits, T, E, k, *ws, 1 << 30, path, item_tok, st);
         if (err != hipSuccess) return hip_fail(err, "route");
     }
-    // a large self-routed layer ranks each expert once, in a pre-pass
-    const bool lists = self && (int64_t)E * (I / 32 + H / 128) >= moe::kSelfListUnits;
+    // a large self-routed layer ranks each expert once, in a pre-pass (the
+    // single launch writes the lists in its own first units)
+    const bool lists = self && !self_fused && (int64_t)E * (I / 32 + H / 128) >= moe::kSelfListUnits;
     moe::GemmArgs a;
     a.logits = router_logits;
     a.T = T;
@@ -373,13 +378,14 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     a.sh_wdn = o.shared_down;
     a.sh_sdn = o.shared_down_scales;
     a.sh_row0 = S;
+    int32_t* self_misc = ws->flags + moe::self_misc_word(E);
     // The shared expert needs no routing: its gate_up runs ahead of the
     // routed gate_up, its down ahead of the routed down (which, on the VALU
     // path and in the single-launch layer, also combines), both in the
     // stages of the routed ones.  The matrix-core GEMM kernels of the split
     // launch run its workgroups themselves, ahead of the routed ones; the
     // VALU path and the single-launch layer launch them on their own.
-    const bool shared_inside = path == MOE_PATH_MFMA && (mx8 || o.launch != MOE_LAUNCH_FUSED);
+    const bool shared_inside = path == MOE_PATH_MFMA && (mx8 || o.launch != MOE_LAUNCH_FUSED || self_fused);
     auto shared_gate_up = [&]() -> hipError_t {
         return shared && !shared_inside ? moe::launch_shared_gate_up(a, st) : hipSuccess;
     };
@@ -387,7 +393,12 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         return shared && !shared_inside ? moe::launch_shared_down(a, st) : hipSuccess;
     };
     if ((err = shared_gate_up()) != hipSuccess) return hip_fail(err, "shared gate_up");
-    if (self) {
+    if (self_fused) {
+        a.pos = nullptr;  // h and y rows are the slots
+        err = moe::launch_self_fused(a, ws->flags, st);
+        if (err != hipSuccess) return hip_fail(err, "self-routed single launch");
+        if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    } else if (self) {
         a.pos = nullptr;  // h and y rows are the slots
         err = moe::launch_self_gate_up(a, lists, st);
         if (err != hipSuccess) return hip_fail(err, "gate_up");
@@ -452,7 +463,7 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         {mx8 ? o.x_scales : nullptr, ws->x_scales, (size_t)T * (H / 32)},
         {mx8 ? o.h_codes : nullptr, ws->h_codes, (size_t)S * I},
         {mx8 ? o.h_scales : nullptr, ws->h_scales, (size_t)S * (I / 32)},
-        {o.wait_error, ws->queue + moe::kQueueError, 4},
+        {o.wait_error, self_fused ? self_misc + moe::kSelfErrorOut : ws->queue + moe::kQueueError, 4},
         {o.logits_out, router_logits, (size_t)T * E * 4},
     };
     for (auto& c : copies) {

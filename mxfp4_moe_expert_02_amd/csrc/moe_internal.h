@@ -22,11 +22,43 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kRouteSlotBlock = 256;  // slots per block of the multi-block routing sort
 
-// words of Workspace::queue (the single-launch expert layer)
+// Counters that workgroups of a running kernel poll sit one per 128-byte
+// line, kLineInts words apart: hundreds of pollers on one line keep one
+// memory channel busy, and every workgroup's weight stream, which crosses
+// all channels, then runs at that channel's pace (measured on the 9-token,
+// 64-expert single launch: down units 9 -> 35 us once the first
+// workgroups polled a shared counter).  The single launches' combine
+// barrier: the unit that completes the queue raises kGoLines flags
+// kGoStride words apart, and workgroup b polls flag b % kGoLines.
+constexpr int kLineInts = 32;
+constexpr int kGoLines = 64, kGoStride = 64;
+
+// The self-routed single launch's counters (the int32 words at `flags`):
+// list ready of expert e (index E unused) at e * kLineInts, gate_up units
+// done of expert e (index E: the shared expert) at (E + 1 + e) * kLineInts,
+// then one line of SelfFlags words, then the go flags.
+enum SelfFlags : int {
+    kSelfNext = 0,      // next unit to dequeue
+    kSelfDone = 1,      // units run (the combine waits for all of them)
+    kSelfExits = 2,     // workgroups done with the combine
+    kSelfError = 3,     // a wait gave up (this launch)
+    kSelfErrorOut = 4,  // ... as left by the last launch, for the caller
+};
+__host__ __device__ constexpr int64_t self_misc_word(int E) { return (int64_t)2 * (E + 1) * kLineInts; }
+__host__ __device__ constexpr int64_t self_go_word(int E) { return self_misc_word(E) + kGoStride; }
+__host__ __device__ constexpr int64_t self_flag_words(int E) {
+    return self_go_word(E) + (int64_t)kGoLines * kGoStride;
+}
+
+// words of Workspace::queue (the single-launch expert layer of routed
+// items): a line of these, then the go flags from kQueueGo
 enum Queue : int {
-    kQueueNext = 0,   // next unit to dequeue
-    kQueueError = 1,  // nonzero: a unit gave up waiting for its gate_up units
-    kQueueWords = 4,
+    kQueueNext = 0,    // next unit to dequeue
+    kQueueError = 1,   // nonzero: a wait gave up
+    kQueueDone = 2,    // units run (the combine waits for all of them)
+    kQueueHead = 4,
+    kQueueGo = kGoStride,
+    kQueueWords = kQueueGo + kGoLines * kGoStride,
 };
 
 // meta[] words in the workspace
@@ -69,6 +101,17 @@ constexpr int kSelfMaxMeanTok = 8;
 // workgroup (no pre-pass launch).
 constexpr int kSlotListInts = 32;
 constexpr int kSelfListUnits = 2048;
+
+// Bytes per row of h3s (h's four E8M0 scale bytes per 32-column block, the
+// three terms' and a pad: I/8 bytes), rounded up to whole 128-byte cache
+// lines.  In a single-launch layer one line of narrower rows would hold
+// rows of items of different experts, finished at different times; a down
+// unit's plain load of its own row would bring another row's unwritten
+// bytes into its CU's and XCD's caches, where a later unit of that other
+// expert could hit them.  With whole lines per row every line belongs to
+// one item and is first read once that item's gate_up units are done.  (The
+// code rows, 3I bytes with I a multiple of 128, are whole lines already.)
+__host__ __device__ constexpr int h3s_stride(int I) { return (I / 8 + 127) / 128 * 128; }
 // router GEMM: K is split (at most kRouterMaxSplit ways, over tiles of 16
 // tokens x 16 experts) only for layers of fewer than kRouterWaves / 2 tiles
 // of 16 tokens x 64 experts, so then T*E < kRouterWaves * 512 and there are
@@ -98,9 +141,10 @@ struct Workspace {
     int32_t* meta = nullptr;       // [kMetaWords]
     int32_t* tile_done = nullptr;  // [Tmax * H/kMfmaDownRows] finished down tiles per (token, column tile)
     int32_t* bhist = nullptr;      // [ceil(Tmax*kmax/kRouteSlotBlock) * E] per-block expert histograms
-    int32_t* queue = nullptr;      // [kQueueWords] single-launch layer: next unit, error flag
-    int32_t* gu_done = nullptr;    // [E + Tmax*kmax/kMfmaTok + 1] finished gate_up units per MFMA item
+    int32_t* queue = nullptr;      // [kQueueWords] single-launch layer: Queue words, go flags
+    int32_t* gu_done = nullptr;    // [max_items * kLineInts] finished gate_up units per MFMA item, one line each
     int32_t* slot_lists = nullptr; // [E * kSlotListInts] self-routed layer: per-expert slot lists
+    int32_t* flags = nullptr;      // [self_flag_words(E)] the self-routed single launch (SelfFlags)
     float* logits = nullptr;       // [Tmax * E] logits computed from a router weight
     float* router_partial = nullptr;  // [kRouterMaxSplit * min(Tmax*E, kRouterWaves*512)] split-K partials
     int32_t* router_cnt = nullptr;    // [2 * kRouterWaves] finished splits per tile (split-K only)
@@ -137,7 +181,7 @@ struct GemmArgs {
     int list_meta;              // which meta word holds the list length
     uint16_t* h;                // GEMV path's routed rows: [rows, 2I] bf16 hi/lo pairs (gemv.hip)
     uint8_t* h3q;               // matrix-core paths and the shared expert: [rows, 3I] codes of
-    uint8_t* h3s;               // h's three MXFP8 terms, [rows, I/8] their scales (store_h3)
+    uint8_t* h3s;               // h's three MXFP8 terms, [rows, h3s_stride(I)] their scales (store_h3)
     float* y;
     int T, H, I, k;
     // combine state
@@ -153,8 +197,8 @@ struct GemmArgs {
     uint16_t* out;              // [T, H] bf16
     int col_tiles;
     // single-launch layer (route, then one kernel for gate_up + down + combine)
-    int32_t* queue;             // [kQueueWords], zeroed by the route
-    int32_t* gu_done;           // [max items] finished gate_up units per item, zeroed by the route
+    int32_t* queue;             // [kQueueWords], counters and go flags zeroed by the route
+    int32_t* gu_done;           // [max items * kLineInts] finished gate_up units of item i at i * kLineInts, zeroed by the route
     // self-routed layer (no routing pass): each GEMM workgroup ranks its own
     // expert for every token from the router logits
     const float* logits;        // [T, E] fp32
@@ -216,6 +260,11 @@ hipError_t launch_combine(const GemmArgs& a, hipStream_t stream);
 // waits (bounded) until every gate_up unit of its item has published h.
 // Needs the queue words and gu_done zeroed (the route does it).
 hipError_t launch_mfma_fused(const GemmArgs& a, int max_items, hipStream_t stream);
+// The whole self-routed layer (routing weights, slot lists, gate_up, down
+// and the combine) in one persistent launch; a.slot_lists and the flags
+// (zero at the first launch; the launch leaves them zero) from the
+// workspace.
+hipError_t launch_self_fused(const GemmArgs& a, int32_t* flags, hipStream_t stream);
 hipError_t launch_wide_fused(const GemmArgs& a, int max_items, hipStream_t stream);
 // MXFP8 (prefill) path: encode x per token along H, then the scaled
 // FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue;

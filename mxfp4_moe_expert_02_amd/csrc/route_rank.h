@@ -26,7 +26,9 @@ __device__ inline bool beats(float av, int ai, float bv, int bi) {
 // (lg[i*E + e] for token t0+i).  sel_id/sel_l [nt*k] are LDS scratch.
 // Writes ids and weights of those tokens: w[t, j] = exp(l_j - l_0) / sum_q
 // exp(l_q - l_0) over the chosen logits l_0 >= l_1 >= ..., summed in slot
-// order.  Uses every thread of the block.
+// order.  Uses every thread of the block.  PUBLISH: agent-coherent stores,
+// for readers on other XCDs in the same launch.
+template <bool PUBLISH = false>
 __device__ inline void topk_tokens(const float* lg, int nt, int t0, int E, int k, int* sel_id,
                                    float* sel_l, int32_t* ids, float* wts) {
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -53,8 +55,14 @@ __device__ inline void topk_tokens(const float* lg, int nt, int t0, int E, int k
         float s = 0.f;
         for (int q = 0; q < k; q++) s += __expf(sel_l[i * k + q] - top);
         const int64_t o = (int64_t)(t0 + i) * k + j;
-        ids[o] = sel_id[p];
-        wts[o] = __expf(sel_l[p] - top) / s;
+        const float wv = __expf(sel_l[p] - top) / s;
+        if constexpr (PUBLISH) {
+            __hip_atomic_store(&ids[o], sel_id[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&wts[o], wv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            ids[o] = sel_id[p];
+            wts[o] = wv;
+        }
     }
 }
 

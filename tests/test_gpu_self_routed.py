@@ -172,3 +172,60 @@ def test_rejected_call_enqueues_nothing(M):
     torch.cuda.synchronize()
     assert rc == M.MOE_E_OPTION
     assert ref.elapsed_time(ev) < 0  # ev still holds its earlier time
+
+
+@pytest.mark.parametrize("key", KEYS)
+def test_self_routed_single_launch_bit_exact(M, key):
+    """The whole self-routed layer in one launch (MOE_LAUNCH_FUSED on an
+    eligible layer: routing weights, slot lists, gate_up, down and the
+    combine as units of one persistent kernel) gives the bits of the
+    self-routed launches, and none of its bounded waits gives up."""
+    import torch
+    cfg, layer = _layer(key)
+    run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_SELF_ROUTED)
+    ref = layer.out.clone()
+    dbg = run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_FUSED)
+    assert int(dbg["wait_error"][0]) == 0
+    assert torch.equal(ref.view(torch.int16), layer.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("key", ["ties", "t16e256k8", "t16e200k5"])
+def test_single_launch_repeats_track_inputs(M, key):
+    """Back-to-back single launches with x changed in place between them each
+    give the self-routed bits of their own x.  The layers have I < 1024, where
+    unpadded rows of h's scales would share cache lines across experts; such
+    sharing once let a down unit read another expert's scale row before its
+    gate_up units had written it (one token's 128 output columns wrong, now
+    and then)."""
+    import dataclasses
+
+    import torch
+    cfg, shared_layer = _layer(key)
+    # a private copy of the cached layer: its own x (changed in place) and out
+    layer = dataclasses.replace(shared_layer, x=shared_layer.x.clone(), out=shared_layer.out.clone())
+    gen = torch.Generator().manual_seed(7)
+    for rep in range(4):
+        x = torch.randn(layer.x.shape, generator=gen).to(torch.bfloat16)
+        layer.x.copy_(x.to(layer.x.device))
+        run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_SELF_ROUTED, init=rep == 0)
+        ref = layer.out.clone()
+        dbg = run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_FUSED, init=False)
+        assert int(dbg["wait_error"][0]) == 0
+        assert torch.equal(ref.view(torch.int16), layer.out.view(torch.int16)), rep
+
+
+def test_single_launch_after_other_paths(M):
+    """The single launch resets its own counters: after a VALU call and a
+    routed call on the same workspace (which leave their own counts behind)
+    it still gives the self-routed bits, twice in a row."""
+    import torch
+    cfg = get_config("c2")
+    layer = get_layer(cfg)
+    run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_SELF_ROUTED)
+    ref = layer.out.clone()
+    run(M, layer, path=1, init=False)
+    run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_SPLIT, init=False)
+    for _ in range(2):
+        dbg = run(M, layer, path=MFMA, launch=M.MOE_LAUNCH_FUSED, init=False)
+        assert int(dbg["wait_error"][0]) == 0
+        assert torch.equal(ref.view(torch.int16), layer.out.view(torch.int16))
