@@ -8,9 +8,16 @@ weights ~ N(0,0.02) encoded to MXFP4 on the GPU).
 
 One step = one full layer (route -> gate_up + SiLU*up -> down -> combine) on
 inputs already resident in HBM; layers of at most 16 tokens run self-routed
-(the GEMM workgroups rank their own experts: no routing kernel).  Prints ONE
-JSON line:
+(the GEMM workgroups rank their own experts: no routing kernel).  The steps
+rotate through --weight-sets separately allocated copies of the expert
+weights (default 3), so a step never finds the previous step's weights in
+L2 or the 256 MiB Infinity Cache, as in a decode that reads each layer's
+own weights once.  Prints ONE JSON line:
   value  = touched-expert weight bytes (packed E2M1 + E8M0) / mean layer time, GB/s
+  step_us = median / p10 / p90 of single steps (events between steps)
+  cold   = steps after a 1 GiB cache-allocating read that evicts L2 and the
+           Infinity Cache (then a stream sync, so no write-back lands in the
+           step), per stage, median over 30
   roofline = the dominant kernel (gate_up: 2/3 of the bytes) against the
              8 TB/s HBM peak, timed live with HIP events the library records
              between its kernels
@@ -72,7 +79,30 @@ def parse():
                    help="also time the layer replayed from a captured HIP graph")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run one probe copy of this many bytes (counter calibration)")
+    p.add_argument("--weight-sets", type=int, default=3,
+                   help="separately allocated copies of the expert weights; step i uses copy "
+                        "i mod N (1: every step rereads the same weights)")
     return p.parse_args()
+
+
+def build_info() -> dict:
+    """What produced the numbers: git commit (if the tree has .git), the
+    kernel sources' sha256, ROCm and HIP runtime versions."""
+    import subprocess
+    sha = None
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    rocm = None
+    for f in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(f):
+            rocm = open(f).read().strip()
+            break
+    import torch
+    return {"git_sha": sha, "kernel_sources_sha256": sources_sha256(), "rocm_version": rocm,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__}
 
 
 def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:
@@ -206,6 +236,10 @@ def main():
     path = args.path or M.MOE_PATH_MFMA
     layout = M.MOE_LAYOUT_TILES if path == M.MOE_PATH_MFMA else M.MOE_LAYOUT_ROWS
     wgu, wdn, scales = layer.weights(layout)
+    # the weight sets the steps rotate through: the layer's own, then copies
+    nsets = max(1, args.weight_sets)
+    wsets = [(wgu, wdn, scales)] + [(wgu.clone(), wdn.clone(), tuple(t.clone() for t in scales))
+                                    for _ in range(nsets - 1)]
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
 
     launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
@@ -229,9 +263,10 @@ def main():
         from mxfp4_moe_expert_02_amd.layer import build_shared
         shared = build_shared(cfg)
 
-    def step(events=None):
-        M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, wgu,
-                               wdn, scales, layer.out, gemm_path=path, weight_layout=layout,
+    def step(i=0, events=None):
+        w_gu, w_dn, w_sc = wsets[i % nsets]
+        M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, cfg.k, w_gu,
+                               w_dn, w_sc, layer.out, gemm_path=path, weight_layout=layout,
                                events=events, act_format=act, launch=launch, router_weight=router,
                                shared=None if shared is None else shared.tiles)
 
@@ -247,9 +282,9 @@ def main():
         dn_bytes += cfg.H * cfg.I + cfg.H * cfg.I // 32
     total_bytes = gu_bytes + dn_bytes
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
+    print(f"[bench] warmup {args.warmup}, {nsets} weight set(s)", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     # timed region: K back-to-back layers, bracketed by synchronisation
@@ -257,11 +292,23 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     stop.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
+          flush=True)
+
+    # the distribution of single steps: the same K steps with an event between
+    # consecutive steps
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    sev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        sev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
 
     graph_ms = None
     if args.graph:
@@ -272,7 +319,7 @@ def main():
             step()  # warm the capture stream
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s_cap):
-                step()
+                step()  # one weight set: the graph holds its pointers
         torch.cuda.synchronize()
         for _ in range(3):
             g.replay()
@@ -291,28 +338,53 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
           for _ in range(args.steps)]
     for i in range(args.steps):
-        step(events=ev[i])
+        step(i, events=ev[i])
     torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(STAGES)}
     dn_ms = stage_ms["down_combine"]
 
-    # cold steps: a 512 MiB write between steps evicts the 256 MiB Infinity Cache and L2
+    # cold steps: a 1 GiB cache-allocating read evicts L2 and the 256 MiB
+    # Infinity Cache without leaving dirty lines, and the stream is synced
+    # before the step, whose stages are timed by the library's events; for
+    # comparison, the earlier method: a 512 MiB write enqueued just before
+    # the step
     cold = None
     if not args.no_cold:
+        evict = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(M.moe_probe_sink_words(), dtype=torch.int32, device="cuda")
+        reps = min(args.steps, 30)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+               for _ in range(reps)]
+        for r in range(reps):
+            M.moe_probe_read_cached(evict, sink)
+            torch.cuda.synchronize()
+            step(r, events=cev[r])
+            torch.cuda.synchronize()
+        del evict, sink
+        cold_ms = np.array([cev[r][0].elapsed_time(cev[r][-1]) for r in range(reps)])
+        cold_stage = {s: float(np.median([cev[r][j].elapsed_time(cev[r][j + 1]) for r in range(reps)]))
+                      for j, s in enumerate(STAGES)}
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        times = []
-        for i in range(min(args.steps, 50)):
-            flush.fill_(i & 0xff)
+        wf = []
+        for r in range(reps):
+            flush.fill_(r & 0xff)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            step()
+            step(r)
             e1.record(stream)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
+            wf.append(e0.elapsed_time(e1))
         del flush
-        cold = float(np.median(times))
+        cold = {"method": "1 GiB read with cache-allocating loads, stream sync, then one step "
+                          "(stage events included)", "reps": reps,
+                "us_per_layer": round(float(np.median(cold_ms)) * 1e3, 2),
+                "p10_us": round(float(np.percentile(cold_ms, 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(cold_ms, 90)) * 1e3, 2),
+                "GBps": round(total_bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2),
+                "stage_us": {k: round(v * 1e3, 2) for k, v in cold_stage.items()},
+                "write_flush_us_per_layer": round(float(np.median(wf)) * 1e3, 2)}
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
     # the gate_up kernel the library runs for this layer (the wide bf16
@@ -392,6 +464,11 @@ def main():
                    "gate_up": round(gu_flops / (gu_ms * 1e-3) / 1e12, 2),
                    "down_combine": round(dn_flops / (dn_ms * 1e-3) / 1e12, 2)},
         "library": lib_path,
+        "build": build_info(),
+        "weight_sets": nsets,
+        "step_us": {"median": round(float(np.median(step_ms)) * 1e3, 2),
+                    "p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                    "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2)},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
@@ -400,8 +477,8 @@ def main():
     if graph_ms is not None:
         result["graph_us_per_layer"] = round(graph_ms * 1e3, 2)
     if cold is not None:
-        result["cold_us_per_layer"] = round(cold * 1e3, 2)
-        result["cold_GBps"] = round(total_bytes / (cold * 1e-3) / 1e9, 2)
+        result["cold"] = cold
+        result["cold_us_per_layer"] = cold["us_per_layer"]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, total_bytes / 1e9, shared=shared is not None)

@@ -22,12 +22,18 @@
 extern "C" {
 #endif
 
-/* Read `bytes` from src with 128-bit loads across the whole GPU; one uint32
- * per thread (a fold of what it read) goes to sink, which must hold
- * moe_probe_sink_words() words. */
+/* Read `bytes` from src with 128-bit nontemporal loads across the whole
+ * GPU, each workgroup streaming contiguous 256 KB ranges (the expert
+ * kernels' access pattern); one uint32 per thread (a fold of what it read)
+ * goes to sink, which must hold moe_probe_sink_words() words. */
 int moe_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
-/* Words the sink of moe_probe_stream_read must hold. */
+/* The same read with ordinary loads, which allocate in L2 and the Infinity
+ * Cache: reading more than those hold evicts them without leaving dirty
+ * lines to write back (a cold step's setup). */
+int moe_probe_read_cached(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/* Words the sink of moe_probe_stream_read / moe_probe_read_cached must hold. */
 int64_t moe_probe_sink_words(void);
 
 /* Copy `bytes` from src to dst with 128-bit loads and stores. */

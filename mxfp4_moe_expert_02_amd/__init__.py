@@ -15,6 +15,6 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_MXFP8, MOE_E_ALIGN, MOE_E_HIP, MOE_E_LI
                    moe_mxfp4_forward_noalloc, moe_mxfp4_init,
                    moe_mxfp4_quantize, moe_mxfp4_status_string, moe_mxfp8_prepack,
                    moe_mxfp8_quantize, moe_probe_copy,
-                   moe_probe_sink_words, moe_probe_stream_read)
+                   moe_probe_read_cached, moe_probe_sink_words, moe_probe_stream_read)
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_"))] + ["MoeError", "lib"]

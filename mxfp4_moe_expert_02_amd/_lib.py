@@ -42,7 +42,7 @@ MOE_LAUNCH_SELF_ROUTED = 3
 EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
             "moe_mxfp4_prepack", "moe_mxfp8_quantize", "moe_mxfp8_prepack",
-            "moe_probe_stream_read", "moe_probe_sink_words", "moe_probe_copy",
+            "moe_probe_stream_read", "moe_probe_read_cached", "moe_probe_sink_words", "moe_probe_copy",
             "moe_mxfp4_forward_noalloc")
 
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.moe_probe_stream_read.restype = ctypes.c_int
         L.moe_probe_stream_read.argtypes = [vp, i64, vp, vp]
+        L.moe_probe_read_cached.restype = ctypes.c_int
+        L.moe_probe_read_cached.argtypes = [vp, i64, vp, vp]
         L.moe_probe_sink_words.restype = i64
         L.moe_probe_sink_words.argtypes = []
         L.moe_probe_copy.restype = ctypes.c_int
@@ -330,6 +332,13 @@ def moe_probe_stream_read(src, sink, stream=None, check: bool = True) -> int:
     rc = lib().moe_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                      _stream(stream))
     return _check(rc, "moe_probe_stream_read") if check else rc
+
+
+def moe_probe_read_cached(src, sink, stream=None, check: bool = True) -> int:
+    """Read every byte of the device tensor ``src`` with cache-allocating loads."""
+    rc = lib().moe_probe_read_cached(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                     _stream(stream))
+    return _check(rc, "moe_probe_read_cached") if check else rc
 
 
 def moe_probe_copy(src, dst, stream=None, check: bool = True) -> int:

@@ -110,13 +110,15 @@ __device__ inline void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
 // budget.  So h is carried as three MXFP8 terms, h ~ t0 + t1 + t2: t0 is
 // an MXFP8 encoding of h (E4M3 elements, one E8M0 scale per block of 32),
 // t1 that of the remainder h - t0, t2 that of h - t0 - t1; each term leaves
-// at most 2^-4 of what it encodes, so the three hold h to about 2^-12
-// relative (8 times closer than bf16).  The down
+// about 2^-4 of what it encodes (measured against its block's largest
+// magnitude), so the three hold h to about 2^-12 of that magnitude (8 times
+// closer than a bf16 rounding of it).  The down
 // GEMM then runs on the scaled FP4 x FP8 matrix cores: per 128-k chunk and
 // 16-row group, one v_mfma_scale_f32_16x16x128_f8f6f4 per term, the
 // weights' FP4 codes and E8M0 scales taken as they are (no decode).
 //
-// Layout of row r of h (I values): codes h3q + r * 3I, scales h3s + r * I/8.
+// Layout of row r of h (I values): codes h3q + r * 3I, scales h3s + r *
+// h3s_stride(I) (I/8 bytes, the row padded to whole cache lines).
 // The B operand of one scaled MFMA gives lane (c, g) the 32 codes of
 // k = 16g .. 16g+15 and 64+16g .. 64+16g+15 of the chunk, with the scale
 // of MX block g (see mxfp8.hip), so a chunk's codes are stored per lane:
@@ -137,8 +139,10 @@ constexpr int kHTerms = 3;
 // the remainder.  A block holding a NaN or an infinity gets term 0 scale
 // 0xFF (NaN) and zero codes.  Agent-coherent stores: in the single-launch
 // layer the down unit that reads them may run on another XCD in the same
-// launch (its L2 never held these lines in this launch); plain stores
-// otherwise (PUBLISH = false: the kernel boundary makes them visible).
+// launch, whose caches cannot hold these lines before it reads them (rows
+// are whole cache lines, and only the row's own expert reads them, after
+// its gate_up units are done); plain stores otherwise (PUBLISH = false:
+// the kernel boundary makes them visible).
 template <bool PUBLISH>
 __device__ inline void store_h3(const GemmArgs& a, int64_t row, int blk, const float (&v)[2][4],
                                 bool live) {

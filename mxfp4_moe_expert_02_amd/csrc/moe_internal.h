@@ -155,7 +155,7 @@ struct Workspace {
     // h: the routed rows of the GEMV path as bf16 hi/lo pairs [rows, 2I];
     // h3q / h3s: h of the matrix-core paths (and of the shared expert on
     // every bf16 path) as three MXFP8 terms, codes [rows, 3I] and scales
-    // [rows, I/8] (device_common.h, store_h3)
+    // [rows, h3s_stride(I)] (device_common.h, store_h3)
     uint16_t* h = nullptr;
     uint8_t* h3q = nullptr;
     uint8_t* h3s = nullptr;

@@ -35,7 +35,8 @@ def test_header_declares_the_abi():
         "moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward", "moe_mxfp4_forward_ex",
         "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_mxfp4_prepack",
         "moe_mxfp8_quantize", "moe_mxfp8_prepack", "moe_probe_stream_read",
-        "moe_probe_sink_words", "moe_probe_copy", "moe_mxfp4_forward_noalloc"])
+        "moe_probe_read_cached", "moe_probe_sink_words", "moe_probe_copy",
+        "moe_mxfp4_forward_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(L):
