@@ -79,6 +79,7 @@ extern "C" {
 #define MOE_E_HIP (-7)       /* a HIP runtime call or kernel launch failed */
 #define MOE_E_OPTION (-8)    /* an option value is not recognised */
 #define MOE_E_LIMIT (-9)     /* a size exceeds the fixed limits of moe_mxfp4_forward_noalloc */
+#define MOE_E_DTYPE (-10)    /* a tensor descriptor's element type is not the one required */
 
 /* activation formats fed to the expert GEMMs */
 #define MOE_ACT_BF16 0       /* x and h in bf16 (verify token counts) */
@@ -121,6 +122,22 @@ typedef struct moe_mxfp4_scales {
     const uint8_t* gate_up; /* [E, 2I, H/32] */
     const uint8_t* down;    /* [E, H, I/32]  */
 } moe_mxfp4_scales;
+
+/* Element types of moe_tensor */
+#define MOE_DT_BF16 1        /* bfloat16 bit patterns (2 bytes) */
+#define MOE_DT_F32 2         /* float32 */
+#define MOE_DT_U8 3          /* uint8 (packed codes, E8M0 scales) */
+#define MOE_DT_I32 4         /* int32 */
+
+/* A caller tensor as moe_mxfp4_forward_t sees it: device pointer, element
+ * type (MOE_DT_*), rank 1..4 and extents; row-major and contiguous.  The
+ * library reads the descriptor during the call only. */
+typedef struct moe_tensor {
+    void* data;
+    int64_t shape[4];
+    int32_t ndim;
+    int32_t dtype;
+} moe_tensor;
 
 /* Options of moe_mxfp4_forward_ex.  Zero-initialised = moe_mxfp4_forward.
  * The optional outputs are device buffers the call fills (NULL to skip):
@@ -225,6 +242,32 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
                          int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
                          const moe_mxfp4_scales* scales, void* out, void* stream,
                          const moe_mxfp4_options* opt);
+
+/* moe_mxfp4_forward_ex with every tensor described (element type, rank,
+ * extents), for C callers that want the checks a framework binding makes.
+ * Before anything else it requires, with T = x->shape[0] and H, E, I read
+ * from the descriptors themselves:
+ *   x              rank 2, BF16, [T, H]
+ *   router_logits  rank 2, F32,  [T, E]   (NULL, or data NULL, when
+ *                                          opt->router_weight is set)
+ *   W_gate_up      rank 3, U8,   [E, 2I, H/2]
+ *   W_down         rank 3, U8,   [E, H, I/2]
+ *   scales[0]      rank 3, U8,   [E, 2I, H/32]
+ *   scales[1]      rank 3, U8,   [E, H, I/32]
+ *   out            rank 2, BF16, [T, H]
+ * (the tile layout of opt->weight_layout = MOE_LAYOUT_TILES is stored in
+ * tensors of the same shapes and byte counts), H even and I even, and, if
+ * the current device has a workspace, E, H and I equal to those given to
+ * moe_mxfp4_init.  A descriptor or data pointer that is NULL returns
+ * MOE_E_NULL, a wrong element type MOE_E_DTYPE, a wrong rank or extent
+ * MOE_E_SHAPE -- nothing is enqueued and out is untouched.  Then
+ * it is moe_mxfp4_forward_ex on those pointers with num_tokens = T, whose
+ * own checks (against the sizes given to moe_mxfp4_init, alignment,
+ * options) follow.  scales points at two descriptors. */
+int moe_mxfp4_forward_t(const moe_tensor* x, const moe_tensor* router_logits, int32_t top_k,
+                        const moe_tensor* W_gate_up, const moe_tensor* W_down,
+                        const moe_tensor* scales, const moe_tensor* out, void* stream,
+                        const moe_mxfp4_options* opt);
 
 /* Encode a float32 matrix w [rows, cols] to MXFP4 along cols (the block
  * rule of the weights: scale 2^(floor(log2 amax) - 2) with the exponent

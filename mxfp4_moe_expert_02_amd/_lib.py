@@ -26,6 +26,12 @@ MOE_E_NOT_INIT = -6
 MOE_E_HIP = -7
 MOE_E_OPTION = -8
 MOE_E_LIMIT = -9
+MOE_E_DTYPE = -10
+
+MOE_DT_BF16 = 1
+MOE_DT_F32 = 2
+MOE_DT_U8 = 3
+MOE_DT_I32 = 4
 
 MOE_ACT_BF16 = 0
 MOE_ACT_MXFP8 = 1
@@ -43,7 +49,7 @@ EXPORTED = ("moe_mxfp4_init", "moe_mxfp4_finalize", "moe_mxfp4_forward",
             "moe_mxfp4_forward_ex", "moe_mxfp4_quantize", "moe_mxfp4_status_string",
             "moe_mxfp4_prepack", "moe_mxfp8_quantize", "moe_mxfp8_prepack",
             "moe_probe_stream_read", "moe_probe_read_cached", "moe_probe_sink_words", "moe_probe_copy",
-            "moe_mxfp4_forward_noalloc")
+            "moe_mxfp4_forward_noalloc", "moe_mxfp4_forward_t")
 
 
 class MoeError(RuntimeError):
@@ -54,6 +60,11 @@ class MoeError(RuntimeError):
 
 class moe_mxfp4_scales(ctypes.Structure):
     _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
+
+
+class moe_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("shape", ctypes.c_int64 * 4), ("ndim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class moe_mxfp4_options(ctypes.Structure):
@@ -90,6 +101,11 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_forward.argtypes = fwd
         L.moe_mxfp4_forward_ex.restype = ctypes.c_int
         L.moe_mxfp4_forward_ex.argtypes = fwd + [ctypes.POINTER(moe_mxfp4_options)]
+        L.moe_mxfp4_forward_t.restype = ctypes.c_int
+        L.moe_mxfp4_forward_t.argtypes = [ctypes.POINTER(moe_tensor), ctypes.POINTER(moe_tensor), i32,
+                                          ctypes.POINTER(moe_tensor), ctypes.POINTER(moe_tensor),
+                                          ctypes.POINTER(moe_tensor), ctypes.POINTER(moe_tensor), vp,
+                                          ctypes.POINTER(moe_mxfp4_options)]
         L.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
         L.moe_mxfp4_forward_noalloc.argtypes = [vp, vp, i64, i32, i64, i64, i64, vp, vp,
                                                 ctypes.POINTER(moe_mxfp4_scales), vp, vp]
@@ -231,6 +247,39 @@ def moe_mxfp4_forward_ex(x, router_logits, top_k: int, W_gate_up, W_down, scales
                                     _ptr(W_down), ctypes.byref(sc) if sc is not None else None,
                                     _ptr(out), _stream(stream), ctypes.byref(opt))
     return _check(rc, "moe_mxfp4_forward_ex") if check else rc
+
+
+def tensor_desc(t) -> moe_tensor:
+    """The moe_tensor descriptor of a torch tensor (its own dtype, rank and
+    shape: the library checks them, nothing is checked here)."""
+    import torch
+    codes = {torch.bfloat16: MOE_DT_BF16, torch.float32: MOE_DT_F32, torch.uint8: MOE_DT_U8,
+             torch.int32: MOE_DT_I32}
+    d = moe_tensor()
+    d.data = t.data_ptr()
+    d.ndim = t.dim()
+    for i, n in enumerate(t.shape[:4]):
+        d.shape[i] = n
+    d.dtype = codes.get(t.dtype, 0)
+    return d
+
+
+def moe_mxfp4_forward_t(x, router_logits, top_k: int, W_gate_up, W_down, scales, out, stream=None,
+                        weight_layout: int = MOE_LAYOUT_ROWS, gemm_path: int = MOE_PATH_AUTO,
+                        launch: int = MOE_LAUNCH_AUTO, router_weight=None,
+                        check: bool = True) -> int:
+    """moe_mxfp4_forward_t: every tensor passed as a descriptor, the library
+    checking element types, ranks and shapes (no checks in Python)."""
+    sc = (moe_tensor * 2)(tensor_desc(scales[0]), tensor_desc(scales[1]))
+    opt = moe_mxfp4_options()
+    opt.weight_layout, opt.gemm_path, opt.launch = weight_layout, gemm_path, launch
+    opt.router_weight = _ptr(router_weight)
+    lg = None if router_logits is None else ctypes.byref(tensor_desc(router_logits))
+    rc = lib().moe_mxfp4_forward_t(ctypes.byref(tensor_desc(x)), lg, top_k,
+                                   ctypes.byref(tensor_desc(W_gate_up)), ctypes.byref(tensor_desc(W_down)),
+                                   sc, ctypes.byref(tensor_desc(out)), _stream(stream),
+                                   ctypes.byref(opt))
+    return _check(rc, "moe_mxfp4_forward_t") if check else rc
 
 
 def moe_mxfp4_forward(x, router_logits, top_k: int, W_gate_up, W_down, scales, out,

@@ -61,6 +61,51 @@ def build(verbose: bool = False, out: str | None = None, defines: dict | None = 
     return lib
 
 
+# host-side sanitizers (each flag after -Xarch_host, so device code is not
+# instrumented): AddressSanitizer and UndefinedBehaviorSanitizer, a UB report
+# fatal
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def build_host_sanitized(build_dir: str | None = None) -> str:
+    """The library with moe_abi.hip -- argument validation, workspace layout
+    and ownership, launch sequencing -- compiled with host AddressSanitizer
+    and UBSan, linked with the other objects of the regular build (build()
+    first).  Loaded with the compiler's ASan runtime preloaded
+    (asan_runtime()).  Returns the path of the .so (under _build/san/)."""
+    bdir = build_dir or BUILD
+    sdir = os.path.join(bdir, "san")
+    os.makedirs(sdir, exist_ok=True)
+    abi = os.path.join(CSRC, "moe_abi.hip")
+    obj = _compile(abi, sdir, SAN_FLAGS)
+    others = [os.path.join(bdir, os.path.basename(s) + ".o") for s in sources() if s != abi]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing}")
+    lib = os.path.join(sdir, "libmoe_mxfp4_san.so")
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", obj, *others, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of hipcc's clang (to LD_PRELOAD)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    path = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        path = hits[0] if hits else ""
+    if not path:
+        raise RuntimeError("clang's ASan runtime not found")
+    return path
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

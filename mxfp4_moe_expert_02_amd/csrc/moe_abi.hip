@@ -224,6 +224,61 @@ void moe_mxfp4_finalize(void) {
     g_num_ws = 0;
 }
 
+namespace {
+
+// A descriptor of rank `ndim`, element type `dtype` and extents `shape`
+// (MOE_E_NULL / MOE_E_DTYPE / MOE_E_SHAPE otherwise).
+int check_tensor(const moe_tensor* t, int32_t dtype, int32_t ndim, const int64_t* shape) {
+    if (!t || !t->data) return MOE_E_NULL;
+    if (t->dtype != dtype) return MOE_E_DTYPE;
+    if (t->ndim != ndim) return MOE_E_SHAPE;
+    for (int i = 0; i < ndim; i++)
+        if (t->shape[i] != shape[i]) return MOE_E_SHAPE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+int moe_mxfp4_forward_t(const moe_tensor* x, const moe_tensor* router_logits, int32_t top_k,
+                        const moe_tensor* W_gate_up, const moe_tensor* W_down,
+                        const moe_tensor* scales, const moe_tensor* out, void* stream,
+                        const moe_mxfp4_options* opt) {
+    if (!x || !W_gate_up || !W_down || !scales || !out) return MOE_E_NULL;
+    if (!x->data || !W_gate_up->data) return MOE_E_NULL;
+    if (x->dtype != MOE_DT_BF16 || W_gate_up->dtype != MOE_DT_U8) return MOE_E_DTYPE;
+    // the sizes, from the descriptors: T, H from x; E, 2I from W_gate_up
+    if (x->ndim != 2 || W_gate_up->ndim != 3) return MOE_E_SHAPE;
+    const int64_t T = x->shape[0], H = x->shape[1];
+    const int64_t E = W_gate_up->shape[0], I2 = W_gate_up->shape[1];
+    if (T < 0 || H <= 0 || E <= 0 || I2 <= 0 || H % 2 || I2 % 4) return MOE_E_SHAPE;
+    const int64_t I = I2 / 2;
+    const int64_t sx[2] = {T, H}, sl[2] = {T, E};
+    const int64_t sgu[3] = {E, I2, H / 2}, sdn[3] = {E, H, I / 2};
+    const int64_t ssg[3] = {E, I2, H / 32}, ssd[3] = {E, H, I / 32};
+    int rc;
+    if ((rc = check_tensor(x, MOE_DT_BF16, 2, sx)) != MOE_OK) return rc;
+    const bool computed = opt && opt->router_weight;  // logits computed in the layer
+    if (!(computed && (!router_logits || !router_logits->data)) &&
+        (rc = check_tensor(router_logits, MOE_DT_F32, 2, sl)) != MOE_OK)
+        return rc;
+    if ((rc = check_tensor(W_gate_up, MOE_DT_U8, 3, sgu)) != MOE_OK) return rc;
+    if ((rc = check_tensor(W_down, MOE_DT_U8, 3, sdn)) != MOE_OK) return rc;
+    if ((rc = check_tensor(&scales[0], MOE_DT_U8, 3, ssg)) != MOE_OK) return rc;
+    if ((rc = check_tensor(&scales[1], MOE_DT_U8, 3, ssd)) != MOE_OK) return rc;
+    if ((rc = check_tensor(out, MOE_DT_BF16, 2, sx)) != MOE_OK) return rc;
+    // the layer's own sizes must be the workspace's (forward_ex reports a
+    // missing workspace, after its option checks)
+    if (T > 0) {
+        const Workspace* ws = current_ws();
+        if (ws && (E != ws->E || H != ws->H || I != ws->I)) return MOE_E_SHAPE;
+    }
+    const moe_mxfp4_scales sc = {(const uint8_t*)scales[0].data, (const uint8_t*)scales[1].data};
+    return moe_mxfp4_forward_ex(x->data, computed && (!router_logits || !router_logits->data)
+                                             ? nullptr : (const float*)router_logits->data,
+                                T, top_k, (const uint8_t*)W_gate_up->data,
+                                (const uint8_t*)W_down->data, &sc, out->data, stream, opt);
+}
+
 int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_tokens,
                          int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
                          const moe_mxfp4_scales* scales, void* out, void* stream,
@@ -569,6 +624,7 @@ const char* moe_mxfp4_status_string(int status) {
         case MOE_E_NOT_INIT: return "moe_mxfp4_init was not called for the current device";
         case MOE_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
         case MOE_E_OPTION: return "an option value is not recognised";
+        case MOE_E_DTYPE: return "a tensor's element type is not the one required";
         case MOE_E_LIMIT:
             return "the layer exceeds the fixed limits of moe_mxfp4_forward_noalloc (at most 16 tokens, "
                    "256 experts, top-8, hidden 8192, inter 4096; T*E <= 4096, T*top_k < 8*E)";

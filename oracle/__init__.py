@@ -33,7 +33,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB may name another build of oracle.c (the sanitizer build of the
+# CPU tests)
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = True) -> str:
@@ -45,6 +47,17 @@ def build(force: bool = True) -> str:
                        check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(out: str) -> str:
+    """oracle.c with AddressSanitizer and UBSan (a UB report fatal), at
+    `out`; loaded with gcc's libasan preloaded."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    subprocess.run(["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                    "-ffp-contract=off", "-fno-fast-math", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", _SRC, "-o", out,
+                    "-lm"], check=True)
+    return out
 
 
 _lib = None

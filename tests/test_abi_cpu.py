@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
         "moe_mxfp4_quantize", "moe_mxfp4_status_string", "moe_mxfp4_prepack",
         "moe_mxfp8_quantize", "moe_mxfp8_prepack", "moe_probe_stream_read",
         "moe_probe_read_cached", "moe_probe_sink_words", "moe_probe_copy",
-        "moe_mxfp4_forward_noalloc"])
+        "moe_mxfp4_forward_noalloc", "moe_mxfp4_forward_t"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         s = L.moe_mxfp4_status_string(code)
         assert s and s != "unknown status"
     assert L.moe_mxfp4_status_string(-99) == "unknown status"
@@ -131,6 +131,62 @@ def test_forward_validation_without_gpu(L):
     assert _fwd(L, opt=whole) == L.MOE_E_NOT_INIT         # a valid request
     whole.shared_down_scales = 0xB004
     assert _fwd(L, opt=whole) == L.MOE_E_ALIGN
+
+
+def _desc(L, data, dtype, *shape):
+    d = L.moe_tensor()
+    d.data, d.dtype, d.ndim = data, dtype, len(shape)
+    for i, n in enumerate(shape):
+        d.shape[i] = n
+    return d
+
+
+def _fwd_t(L, T=9, E=8, H=256, I=128, k=2, opt=None, **over):
+    """moe_mxfp4_forward_t on descriptors of a consistent layer (fake,
+    never dereferenced device addresses), with some replaced by `over`."""
+    BF16, F32, U8 = L.MOE_DT_BF16, L.MOE_DT_F32, L.MOE_DT_U8
+    d = dict(x=_desc(L, 0x1000, BF16, T, H), lg=_desc(L, 0x2000, F32, T, E),
+             wgu=_desc(L, 0x3000, U8, E, 2 * I, H // 2), wdn=_desc(L, 0x4000, U8, E, H, I // 2),
+             sgu=_desc(L, 0x5000, U8, E, 2 * I, H // 32), sdn=_desc(L, 0x6000, U8, E, H, I // 32),
+             out=_desc(L, 0x7000, BF16, T, H))
+    d.update(over)
+    ref = lambda t: None if t is None else ctypes.byref(t)
+    sc = (L.moe_tensor * 2)(d["sgu"], d["sdn"])
+    return L.lib().moe_mxfp4_forward_t(ref(d["x"]), ref(d["lg"]), k, ref(d["wgu"]), ref(d["wdn"]), sc,
+                                       ref(d["out"]), None, None if opt is None else ctypes.byref(opt))
+
+
+def test_forward_t_validation_without_gpu(L):
+    """The descriptor entry point checks every tensor's element type, rank and
+    extents against the others before anything else (no GPU needed: it
+    returns before the first HIP call)."""
+    BF16, F32, U8, I32 = L.MOE_DT_BF16, L.MOE_DT_F32, L.MOE_DT_U8, L.MOE_DT_I32
+    assert _fwd_t(L) == L.MOE_E_NOT_INIT                        # consistent: on to the workspace
+    assert _fwd_t(L, T=0, x=_desc(L, 0x1000, BF16, 0, 256),
+                  lg=_desc(L, 0x2000, F32, 0, 8), out=_desc(L, 0x7000, BF16, 0, 256)) == L.MOE_OK
+    assert _fwd_t(L, x=None) == L.MOE_E_NULL
+    assert _fwd_t(L, x=_desc(L, 0, BF16, 9, 256)) == L.MOE_E_NULL
+    assert _fwd_t(L, x=_desc(L, 0x1000, F32, 9, 256)) == L.MOE_E_DTYPE
+    assert _fwd_t(L, x=_desc(L, 0x1000, BF16, 9, 256, 1)) == L.MOE_E_SHAPE
+    assert _fwd_t(L, lg=_desc(L, 0x2000, BF16, 9, 8)) == L.MOE_E_DTYPE
+    assert _fwd_t(L, lg=_desc(L, 0x2000, F32, 9, 7)) == L.MOE_E_SHAPE     # E differs from W_gate_up's
+    assert _fwd_t(L, lg=_desc(L, 0x2000, F32, 8, 8)) == L.MOE_E_SHAPE     # T differs from x's
+    assert _fwd_t(L, lg=None) == L.MOE_E_NULL                              # no router weight given
+    assert _fwd_t(L, wgu=_desc(L, 0x3000, I32, 8, 256, 128)) == L.MOE_E_DTYPE
+    assert _fwd_t(L, wgu=_desc(L, 0x3000, U8, 8, 256, 64)) == L.MOE_E_SHAPE   # H/2 != 128
+    assert _fwd_t(L, wdn=_desc(L, 0x4000, U8, 8, 256, 32)) == L.MOE_E_SHAPE  # I/2 != 64
+    assert _fwd_t(L, wdn=_desc(L, 0x4000, U8, 8 * 256 * 64)) == L.MOE_E_SHAPE  # flat bytes
+    assert _fwd_t(L, sgu=_desc(L, 0x5000, U8, 8, 256, 4)) == L.MOE_E_SHAPE
+    assert _fwd_t(L, sdn=_desc(L, 0x6000, F32, 8, 256, 4)) == L.MOE_E_DTYPE
+    assert _fwd_t(L, out=_desc(L, 0x7000, BF16, 9, 128)) == L.MOE_E_SHAPE
+    assert _fwd_t(L, out=_desc(L, 0x7000, U8, 9, 256)) == L.MOE_E_DTYPE
+    # with a router weight the logits may be absent
+    opt = L.moe_mxfp4_options(0, 0)
+    opt.router_weight = 0x8000
+    assert _fwd_t(L, lg=None, opt=opt) == L.MOE_E_NOT_INIT
+    # then the options are forward_ex's: checked after the descriptors
+    assert _fwd_t(L, opt=L.moe_mxfp4_options(7, 0)) == L.MOE_E_OPTION
+    assert _fwd_t(L, x=_desc(L, 0x1008, BF16, 9, 256)) == L.MOE_E_ALIGN
 
 
 def _noalloc(L, x=0x1000, lg=0x2000, T=9, k=8, E=64, H=6144, I=2048, wgu=0x3000, wdn=0x4000,
