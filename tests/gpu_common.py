@@ -114,19 +114,32 @@ def oracle_experts(oracle, cfg: Config, experts) -> dict:
         return dict(ex.map(one, todo))
 
 
-def covering_tokens(route: dict, k: int, unit_rows: int) -> tuple[list, int]:
+def covering_tokens(route: dict, k: int, unit_rows: int = 16, item_tok: int | None = None) -> tuple[list, int]:
     """Tokens whose outputs, compared with the oracle, exercise every unit
-    of work of the layer: the expert-sorted rows of each touched expert cut
-    into runs of `unit_rows` (the 16-token column tiles of the matrix-core
-    items, or whole 128-token prefill items), each run holding at least
-    one chosen token.  Greedy set cover (the token covering the most
-    uncovered runs first, ties to the lower token).  Returns (tokens in
-    ascending order, number of runs)."""
+    of work of the layer, each unit holding at least one chosen token.  The
+    units are the expert-sorted rows of each touched expert cut into runs
+    of `unit_rows` (the 16-token column tiles of the matrix-core items), or,
+    with `item_tok`, the items of the route's work list: an expert's c rows
+    in ceil(c / item_tok) items of equal numbers of 16-token tiles (+-1),
+    the larger ones first.  Greedy set cover (the token covering the most
+    uncovered units first, ties to the lower token).  Returns (tokens in
+    ascending order, number of units)."""
     sorted_slots, offsets = route["sorted"], route["offsets"]
     runs = []
     for e in range(len(offsets) - 1):
-        for r0 in range(int(offsets[e]), int(offsets[e + 1]), unit_rows):
-            r1 = min(r0 + unit_rows, int(offsets[e + 1]))
+        o0, o1 = int(offsets[e]), int(offsets[e + 1])
+        if item_tok is None:
+            bounds = [(r0, min(r0 + unit_rows, o1)) for r0 in range(o0, o1, unit_rows)]
+        else:
+            c = o1 - o0
+            groups, tiles = -(-c // item_tok), -(-c // 16)
+            per, extra = (tiles // groups, tiles % groups) if c else (0, 0)
+            bounds = []
+            for q in range(groups):
+                t0 = q * per + min(q, extra)
+                nt = per + (1 if q < extra else 0)
+                bounds.append((o0 + 16 * t0, min(o0 + 16 * (t0 + nt), o1)))
+        for r0, r1 in bounds:
             runs.append({int(s) // k for s in sorted_slots[r0:r1]})
     by_token = {}
     for i, toks in enumerate(runs):

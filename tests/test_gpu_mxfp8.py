@@ -4,7 +4,7 @@ matrix cores) against the CPU oracle run with the same MXFP8 rule.
 * the MXFP8 encoding of x (E4M3 codes and E8M0 scales) bit-exact: both
   sides start from the same bf16 values and the encoding is exact
   arithmetic on them
-* routing bit-exact (the prefill path groups 64 tokens per work item)
+* routing bit-exact (the prefill path groups up to 128 tokens per work item)
 * layer output: h is encoded from fp32 on the GPU and from fp64 in the
   oracle, so a code of h may differ where the value sits within fp32 error
   of a rounding boundary: the decision is taken in the kernel's precision.
@@ -13,7 +13,7 @@ matrix cores) against the CPU oracle run with the same MXFP8 rule.
   finished from the GPU's own h codes; against the plain fp64 oracle too,
   except the layers listed in MXFP8_PLAIN_OVER (twice the bar).
   Full-size layers compare a set of tokens that puts one compared token in
-  every 128-token prefill item (or 16-token tile) of every touched expert.
+  every prefill item (or 16-token tile) of every touched expert.
 """
 import numpy as np
 import pytest
@@ -152,18 +152,20 @@ def test_mxfp8_forward_small_edges(torch_dev, M, oracle_lib, T, k):
 
 
 def test_mxfp8_forward_one_hot_expert_ragged_items(torch_dev, M, oracle_lib):
-    """150 tokens all pick expert 3 first: its items hold 64, 64 and 22
-    tokens; the other experts get ragged small items."""
-    cfg = Config("hot8", "hot_t150_e8_h384_i256_k3", 150, 8, 384, 256, 3, "normal", "mxfp8", 13)
+    """300 tokens all pick expert 3 first: its items hold 112, 96 and 92
+    tokens (7, 6 and 6 tiles, the last one ragged); the other experts get
+    ragged smaller items."""
+    cfg = Config("hot8", "hot_t300_e8_h384_i256_k3", 300, 8, 384, 256, 3, "normal", "mxfp8", 13)
     logits = make_logits(cfg)
     logits[:, 3] += 100.0
     layer = get_layer(cfg, logits=logits)
     _parity(M, oracle_lib, cfg, layer, list(range(0, cfg.T, 7)) + [cfg.T - 1], logits=logits)
 
 
-def _covering(oracle_lib, cfg, unit_rows):
-    tokens, runs = covering_tokens(oracle_lib.route(make_logits(cfg), cfg.k), cfg.k, unit_rows)
-    say(f"{cfg.name}: {len(tokens)} tokens cover {runs} runs of {unit_rows} rows of the touched experts")
+def _covering(oracle_lib, cfg, unit_rows=16, item_tok=None):
+    tokens, runs = covering_tokens(oracle_lib.route(make_logits(cfg), cfg.k), cfg.k, unit_rows, item_tok)
+    what = f"items of up to {item_tok} tokens" if item_tok else f"runs of {unit_rows} rows"
+    say(f"{cfg.name}: {len(tokens)} tokens cover {runs} {what} of the touched experts")
     return tokens
 
 
@@ -175,9 +177,10 @@ def test_mxfp8_forward_batched_shape_every_tile(torch_dev, M, oracle_lib):
 
 
 def test_mxfp8_forward_prefill_every_item(torch_dev, M, oracle_lib):
-    """The prefill chunk: one compared token in each of its 128-token items."""
+    """The prefill chunk: one compared token in each of its items (up to 128
+    tokens of one expert each)."""
     cfg = get_config("c5")
-    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg, 128))
+    _parity(M, oracle_lib, cfg, get_layer(cfg), _covering(oracle_lib, cfg, item_tok=128))
 
 
 def test_mxfp8_forward_deterministic(torch_dev, M):
