@@ -229,9 +229,14 @@ int moe_mxfp4_init(int64_t max_tokens, int64_t num_experts, int64_t hidden,
 /* Release the workspaces of every device (after synchronising them). */
 void moe_mxfp4_finalize(void);
 
-/* The layer with bf16 activations, enqueued on `stream` (a hipStream_t;
- * NULL = the null stream).  x, router_logits and out hold num_tokens rows.
- * Returns without synchronising. */
+/* The layer with bf16 activations on row-major weights (the VALU GEMV
+ * path), enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ * x, router_logits and out hold num_tokens rows.  Returns without
+ * synchronising.  The matrix-core path, the faster one at every layer
+ * size, reads the weights in the MFMA tile layout: rearrange them once at
+ * weight load with moe_mxfp4_prepack (same bytes) and call
+ * moe_mxfp4_forward_ex with weight_layout = MOE_LAYOUT_TILES (or
+ * moe_mxfp4_forward_t). */
 int moe_mxfp4_forward(const void* x, const float* router_logits, int64_t num_tokens,
                       int32_t top_k, const uint8_t* W_gate_up, const uint8_t* W_down,
                       const moe_mxfp4_scales* scales, void* out, void* stream);

@@ -51,7 +51,8 @@ def oracle_shared(oracle, cfg: Config):
     return (gc, gs, dc, ds)
 
 
-def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, shared=None):
+def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, shared=None,
+        layout=None):
     """One forward through the C ABI on every token of the layer; returns
     the requested debug outputs (routing; with MXFP8 also the codes of x)
     as numpy arrays.  out is NaN-filled first, so every element it holds
@@ -60,7 +61,9 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, 
     keeps the current workspace (and whatever an earlier call left in it).
     router: a [E, H] bf16 device router weight -- the layer then computes its
     own logits (returned as "logits") and is given no router_logits.
-    shared: the four tile tensors of an MXFP8 shared expert, or None."""
+    shared: the four tile tensors of an MXFP8 shared expert, or None.
+    layout: MOE_LAYOUT_* of the weights (default: the tile layout when the
+    matrix cores are asked for explicitly or MXFP8 runs, else row-major)."""
     import torch
     c = layer.cfg
     if init:
@@ -86,10 +89,11 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, 
         extra["router_weight"] = router
     layer.out.fill_(float("nan"))
     torch.cuda.synchronize()
-    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path} act={act} "
+    if layout is None:  # the tile layout on an explicit matrix-core request, else row-major
+        mfma = path == M.MOE_PATH_MFMA or act == M.MOE_ACT_MXFP8
+        layout = M.MOE_LAYOUT_TILES if mfma else M.MOE_LAYOUT_ROWS
+    say(f"forward {c.name} T={c.T} E={c.E} H={c.H} I={c.I} k={c.k} path={path} layout={layout} act={act} "
         f"launch={launch} shared={shared is not None}")
-    mfma = path == M.MOE_PATH_MFMA or act == M.MOE_ACT_MXFP8
-    layout = M.MOE_LAYOUT_TILES if mfma else M.MOE_LAYOUT_ROWS
     wgu, wdn, scales = layer.weights(layout)
     M.moe_mxfp4_forward_ex(layer.x, None if router is not None else layer.logits, c.k, wgu, wdn,
                            scales, layer.out, gemm_path=path, weight_layout=layout,

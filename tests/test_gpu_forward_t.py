@@ -25,7 +25,7 @@ def test_forward_t_matches_forward_ex(M, key, layout):
     cfg = get_config(key)
     layer = get_layer(cfg)
     lay = M.MOE_LAYOUT_TILES if layout == "tiles" else M.MOE_LAYOUT_ROWS
-    run(M, layer, path=2 if layout == "tiles" else 1)
+    run(M, layer, path=0, layout=lay)  # forward_ex, AUTO path, the same layout
     ref = layer.out.clone()
     wgu, wdn, scales = layer.weights(lay)
     layer.out.fill_(float("nan"))
