@@ -112,11 +112,20 @@ def test_seed_sweep_vs_oracle(M, oracle_lib, seed, path):
     assert ratio <= TOL
 
 
-@pytest.mark.parametrize("path", ["gemv", "auto", "split", "fused"])
+# (seed, path) cases with the shared expert whose MXFP8 output is over the
+# bar against the plain fp64 oracle: seed 207, whose routed rows carry the
+# boundary flip of h's codes that the sweep without the shared expert checks
+# and names (MXFP8_PLAIN_OVER; the routed h is the same with or without it)
+SHARED_MXFP8_PLAIN_OVER = {(207, "mx8")}
+
+
+@pytest.mark.parametrize("path", ["gemv", "auto", "split", "fused", "mx8"])
 @pytest.mark.parametrize("seed", list(SHAPES))
 def test_seed_sweep_with_shared_expert(M, oracle_lib, seed, path):
-    """The same sweep with an MXFP8 shared expert beside the routed ones
-    (bf16 activations, so h involves no encoding decision)."""
+    """The same sweep with an MXFP8 shared expert beside the routed ones, on
+    the bf16 paths (h involves no encoding decision) and the MXFP8 path
+    (against the plain fp64 oracle with the same MXFP8 rule; named
+    exceptions in SHARED_MXFP8_PLAIN_OVER, held to twice the bar)."""
     from tests.gpu_common import get_shared, oracle_shared
     gemm, act, launch = PATHS[path]
     cfg = _cfg(seed, act)
@@ -131,7 +140,10 @@ def test_seed_sweep_with_shared_expert(M, oracle_lib, seed, path):
     r = oracle_lib.route(lg, cfg.k)
     ex = oracle_experts(oracle_lib, cfg, r["ids"].ravel())
     ref = oracle_lib.forward(make_x_bf16(cfg), lg, cfg.k, cfg.H, cfg.I, ex,
-                             shared=oracle_shared(oracle_lib, cfg))
+                             shared=oracle_shared(oracle_lib, cfg), act_mxfp8=bool(act))
     ratio = parity_ratio(full, ref)
     say(f"seed sweep + shared {cfg.name} {path}: max|d|/rms = {ratio:.3e}")
-    assert ratio <= TOL
+    if (seed, path) in SHARED_MXFP8_PLAIN_OVER:
+        assert TOL < ratio <= 2 * TOL, "listed as over the bar against the plain oracle"
+    else:
+        assert ratio <= TOL
