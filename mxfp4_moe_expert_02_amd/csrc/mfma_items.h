@@ -150,7 +150,7 @@ struct XQ3 {
 // the bytes)
 template <int NT, typename W, typename X>
 struct Cps {
-    static constexpr int value = W::kChunkBytes != 4096 || NT != 1 ? 1 : kChunksPerStep;
+    static constexpr int value = W::kChunkBytes != 4096 || NT != 1 || X::kScaled ? 1 : kChunksPerStep;
 };
 
 template <typename W, int CPS>
@@ -238,6 +238,34 @@ __device__ inline void mfma_quad(const uint8_t* tiles, const uint8_t* tscales, R
     int left = (c_end - c_begin + CPS - 1) / CPS;  // steps
     load_w(c, wa);
     rows_of(xrow);
+    if constexpr (X::kScaled) {
+        // h (three terms per chunk) one step ahead as well: a step waits
+        // only for loads issued a step earlier (its B operand's latency is
+        // the loop's floor otherwise; the weights alone come from HBM)
+        XStep<X, NT, CPS> xb;
+        load_x(c, xa);
+        while (left >= 3) {
+            load_w(c + CPS, wb);
+            load_x(c + CPS, xb);
+            compute(c, wa, xa);
+            c += CPS;
+            load_w(c + CPS, wa);
+            load_x(c + CPS, xa);
+            compute(c, wb, xb);
+            c += CPS;
+            left -= 2;
+        }
+        if (left == 2) {
+            load_w(c + CPS, wb);
+            load_x(c + CPS, xb);
+            compute(c, wa, xa);
+            c += CPS;
+            compute(c, wb, xb);
+        } else {
+            compute(c, wa, xa);
+        }
+        return;
+    }
     while (left >= 3) {  // two steps, each with a successor to prefetch
         load_x(c, xa);
         __builtin_amdgcn_sched_barrier(0);
