@@ -387,6 +387,9 @@ def main():
                 "write_flush_us_per_layer": round(float(np.median(wf)) * 1e3, 2)}
 
     probe_gbs = None if args.no_probe else probe_bandwidth(M, torch)
+    # calibrated HBM bytes of the roofline kernel, taken on the plain layer
+    # only: none apply with the router or shared-expert options
+    traffic = None
     # the gate_up kernel the library runs for this layer (the wide bf16
     # kernels when the experts average >= 4 tokens each; the self-routed one
     # for at most 16 tokens unless the split launch is asked for)
@@ -396,6 +399,8 @@ def main():
              "self_gate_up_kernel" if self_routed else
              ("wide_gate_up_kernel" if wide else "mfma_gate_up_kernel") if path == M.MOE_PATH_MFMA
              else "gemv_gate_up_kernel")
+    if shared is None and router is None:
+        traffic = measured_traffic(cfg.name, kname)
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -419,7 +424,7 @@ def main():
                 "achieved": round(gu_tf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tf / FP8_PEAK_TFLOPS, 4),
                 "frac_of_fp4_peak": round(gu_tf / FP4_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(cfg.name, kname),
+                "traffic": traffic,
                 "algorithmic_flops_per_launch": gu_flops,
                 "algorithmic_bytes_per_launch": int(gu_bytes)}
     else:
@@ -428,7 +433,7 @@ def main():
                                    " (fused gate+up MXFP4 GEMM + SiLU*up)"),
                 "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(cfg.name, kname),
+                "traffic": traffic,
                 "frac_of_probe": round(gu_gbs / probe_gbs, 4) if probe_gbs else None,
                 "algorithmic_bytes_per_launch": int(kbytes)}
     result = {
