@@ -100,9 +100,16 @@ def build_info() -> dict:
         if os.path.exists(f):
             rocm = open(f).read().strip()
             break
+    built = None  # the commit the in-tree library was built from (build.py)
+    info = os.path.join(ROOT, "mxfp4_moe_expert_02_amd", "_build_info.json")
+    if os.path.exists(info):
+        try:
+            built = json.load(open(info))
+        except (OSError, ValueError):
+            built = None
     import torch
-    return {"git_sha": sha, "kernel_sources_sha256": sources_sha256(), "rocm_version": rocm,
-            "hip_runtime": torch.version.hip, "torch": torch.__version__}
+    return {"git_sha": sha, "library_built_from": built, "kernel_sources_sha256": sources_sha256(),
+            "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__}
 
 
 def touched_bytes(counts: np.ndarray, H: int, I: int) -> tuple[int, int]:

@@ -56,9 +56,34 @@ def build(verbose: bool = False, out: str | None = None, defines: dict | None = 
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
+    if out is None:
+        write_build_info()
     if verbose:
         print(f"built {lib}")
     return lib
+
+
+BUILD_INFO = os.path.join(HERE, "_build_info.json")  # git-ignored, beside the library
+
+
+def write_build_info() -> None:
+    """Record the commit the in-tree library was built from (and whether
+    the tree had uncommitted changes), for reports made where the tree has
+    no .git."""
+    import json
+    info = {"git_sha": None, "dirty": None}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        if r.returncode == 0:
+            info["git_sha"] = r.stdout.strip()
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            info["dirty"] = bool(d.stdout.strip()) if d.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 # host-side sanitizers (each flag after -Xarch_host, so device code is not
