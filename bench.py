@@ -61,11 +61,13 @@ def parse():
     p.add_argument("--path", type=int, default=0,
                    help="1: VALU GEMV over row-major weights; 2 (default): bf16 MFMA over "
                         "the tile layout (weights prepacked once before timing)")
-    p.add_argument("--launch", choices=["auto", "split", "self", "fused"], default="auto",
+    p.add_argument("--launch", choices=["auto", "split", "self", "fused", "queue"], default="auto",
                    help="bf16 MFMA path: auto (the library's choice: self-routed for at most "
-                        "16 tokens), split (routing kernel, then the GEMMs), self (no routing "
+                        "16 tokens, queue for layers whose experts average 4 or more tokens), "
+                        "split (routing kernel, then the GEMMs), self (no routing "
                         "kernel: each GEMM workgroup ranks its own expert), fused (one "
-                        "persistent launch: the whole layer for at most 16 tokens)")
+                        "persistent launch: the whole layer for at most 16 tokens), queue "
+                        "(both GEMMs in one launch of one workgroup per dequeued unit)")
     p.add_argument("--router", action="store_true",
                    help="compute the router logits in the layer from a bf16 router weight [E, H] "
                         "(x . W_router^T on the matrix cores) instead of taking them as input")
@@ -79,6 +81,9 @@ def parse():
                    help="also time the layer replayed from a captured HIP graph")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run one probe copy of this many bytes (counter calibration)")
+    p.add_argument("--seed", type=int, default=None,
+                   help="base seed of the synthetic inputs (default: the workload's own); the "
+                        "profiled HBM traffic applies to the default seed only")
     p.add_argument("--weight-sets", type=int, default=3,
                    help="separately allocated copies of the expert weights; step i uses copy "
                         "i mod N (1: every step rereads the same weights)")
@@ -226,7 +231,7 @@ def main():
     from mxfp4_moe_expert_02_amd.layer import build_layer
     from workloads import get_config
 
-    cfg = get_config(args.config)
+    cfg = get_config(args.config) if args.seed is None else get_config(args.config, seed=args.seed)
     mx8 = cfg.act == "mxfp8"
     act = M.MOE_ACT_MXFP8 if mx8 else M.MOE_ACT_BF16
     if mx8 and args.path == M.MOE_PATH_GEMV:
@@ -250,7 +255,8 @@ def main():
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
 
     launch = {"auto": M.MOE_LAUNCH_AUTO, "split": M.MOE_LAUNCH_SPLIT,
-              "self": M.MOE_LAUNCH_SELF_ROUTED, "fused": M.MOE_LAUNCH_FUSED}[args.launch]
+              "self": M.MOE_LAUNCH_SELF_ROUTED, "fused": M.MOE_LAUNCH_FUSED,
+              "queue": M.MOE_LAUNCH_QUEUE}[args.launch]
     wide = cfg.T * cfg.k >= 4 * cfg.E  # the library's wide items (experts average >= 4 tokens)
     self_ok = (path == M.MOE_PATH_MFMA and not mx8 and cfg.T * cfg.k < 8 * cfg.E and cfg.T <= 16
                and cfg.T * cfg.E <= 4096)
@@ -258,6 +264,11 @@ def main():
     # one launch for the whole layer (the single-launch kernel's time is the
     # "gate_up" stage, and it moves every touched byte)
     fused = path == M.MOE_PATH_MFMA and not mx8 and launch == M.MOE_LAUNCH_FUSED
+    # both routed GEMMs in one launch of one workgroup per unit (AUTO's choice
+    # for wide layers without a shared expert; its time is the "gate_up"
+    # stage, and it moves every touched byte)
+    queue = (path == M.MOE_PATH_MFMA and not mx8 and not self_routed and
+             (launch == M.MOE_LAUNCH_QUEUE or (launch == M.MOE_LAUNCH_AUTO and wide and not args.shared)))
 
     router = None
     if args.router:
@@ -403,10 +414,11 @@ def main():
     kname = ("mx8_gate_up_kernel" if mx8 else
              ("self_fused_kernel" if self_ok else "wide_fused_kernel" if wide else "mfma_fused_kernel")
              if fused else
+             ("wide_queue_kernel" if wide else "mfma_queue_kernel") if queue else
              "self_gate_up_kernel" if self_routed else
              ("wide_gate_up_kernel" if wide else "mfma_gate_up_kernel") if path == M.MOE_PATH_MFMA
              else "gemv_gate_up_kernel")
-    if shared is None and router is None:
+    if shared is None and router is None and args.seed is None:
         traffic = measured_traffic(cfg.name, kname)
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
@@ -418,7 +430,7 @@ def main():
     us = ms_per_step * 1e3
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     gu_ms = stage_ms["gate_up"]
-    kbytes = total_bytes if fused else gu_bytes  # the single launch moves every byte
+    kbytes = total_bytes if fused or queue else gu_bytes  # one launch moves every byte
     gu_gbs = kbytes / (gu_ms * 1e-3) / 1e9
     S = cfg.T * cfg.k
     S_all = S + (cfg.T if shared is not None else 0)  # rows through the FFN
@@ -437,7 +449,8 @@ def main():
     else:
         roof = {"bound": "hbm",
                 "kernel": kname + (" (the whole layer in one launch)" if fused else
-                                   " (fused gate+up MXFP4 GEMM + SiLU*up)"),
+                                   " (gate_up + SiLU*up and down, one workgroup per unit)" if queue
+                                   else " (fused gate+up MXFP4 GEMM + SiLU*up)"),
                 "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -464,8 +477,8 @@ def main():
                        max_tokens_per_expert=int(counts_np.max()),
                        touched_weight_bytes=int(total_bytes),
                        gemm_path="mfma" if path == M.MOE_PATH_MFMA else "gemv",
-                       launch=("single_launch" if fused else "self_routed" if self_routed else
-                               "split"),
+                       launch=("single_launch" if fused else "queue" if queue else
+                               "self_routed" if self_routed else "split"),
                        router="computed in the layer from W_router [E,H] bf16" if router is not None
                        else "logits given",
                        weight_layout="tiles" if layout == M.MOE_LAYOUT_TILES else "rows",
@@ -482,8 +495,11 @@ def main():
                     "p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
                     "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2)},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-        "stage_GBps": {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
-                       "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
+        # with the GEMMs in one launch its stage ("gate_up") moves every byte
+        "stage_GBps": ({"gate_up_and_down": round(total_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1)}
+                       if fused or queue else
+                       {"gate_up": round(gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9, 1),
+                        "down_combine": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)}),
         "roofline": roof,
     }
     if graph_ms is not None:

@@ -112,6 +112,19 @@ extern "C" {
                                 AUTO takes it wherever it applies.  Same output
                                 bits as SPLIT.  With NaN router logits the
                                 result for that token is unspecified. */
+#define MOE_LAUNCH_QUEUE 4   /* routed layers: after the route, the two GEMMs as
+                                one launch of one workgroup per unit, each
+                                dequeuing its unit from a counter (gate_up units,
+                                then down units; a down unit waits, bounded, for
+                                its item's gate_up units), then the combine.
+                                Down units of finished items run beside the last
+                                gate_up units, which the split launch's kernel
+                                boundary leaves alone on a partly idle GPU.  Same
+                                output bits as SPLIT.  AUTO takes it for layers
+                                whose experts average at least 4 tokens
+                                (T*top_k >= 4*E) and that have no shared expert;
+                                with one, the shared expert's GEMMs run as kernels
+                                of their own. */
 
 /* Weight layouts (moe_mxfp4_options.weight_layout) */
 #define MOE_LAYOUT_ROWS 0    /* row-major packed codes + scales, as described above */
@@ -168,13 +181,13 @@ typedef struct moe_mxfp4_options {
      * W_gate_up, W_down and the scales.  ROWS runs the GEMV path, TILES the
      * MFMA path; asking for the other path returns MOE_E_OPTION. */
     int32_t weight_layout;
-    /* MOE_LAUNCH_AUTO, MOE_LAUNCH_SPLIT or MOE_LAUNCH_FUSED (see above) */
+    /* MOE_LAUNCH_AUTO, _SPLIT, _FUSED, _SELF_ROUTED or _QUEUE (see above) */
     int32_t launch;
-    /* Optional [1] int32 device output: nonzero if, in the fused launch, a
-     * down unit gave up waiting for its gate_up units (it then went on, and
-     * out is not to be trusted).  The waits are bounded at about four
-     * million polls; a correct launch never reaches that.  0 in split
-     * launches. */
+    /* Optional [1] int32 device output: nonzero if, in the fused or queue
+     * launch, a down unit gave up waiting for its gate_up units (it then
+     * went on, and out is not to be trusted).  The waits are bounded at
+     * about four million polls; a correct launch never reaches that.  0 in
+     * split launches. */
     int32_t* wait_error;
     /* Optional [E, H] bf16 router weight (device, row-major, 16-byte
      * aligned).  When set, the layer computes its router logits itself,

@@ -9,7 +9,8 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_MXFP8, MOE_DT_BF16, MOE_DT_F32, MOE_DT_
                    MOE_E_ALIGN, MOE_E_DTYPE, MOE_E_HIP, MOE_E_LIMIT,
                    MOE_E_NOT_INIT, MOE_E_NULL, MOE_E_OPTION, MOE_E_SHAPE, MOE_E_TOKENS, MOE_E_TOPK,
                    MOE_OK,
-                   MOE_LAUNCH_AUTO, MOE_LAUNCH_FUSED, MOE_LAUNCH_SELF_ROUTED, MOE_LAUNCH_SPLIT,
+                   MOE_LAUNCH_AUTO, MOE_LAUNCH_FUSED, MOE_LAUNCH_QUEUE, MOE_LAUNCH_SELF_ROUTED,
+                   MOE_LAUNCH_SPLIT,
                    MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES, MOE_PATH_AUTO, MOE_PATH_GEMV,
                    MOE_PATH_MFMA, MoeError, lib, moe_mxfp4_prepack,
                    moe_mxfp4_finalize, moe_mxfp4_forward, moe_mxfp4_forward_ex,

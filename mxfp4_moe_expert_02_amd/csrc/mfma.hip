@@ -275,6 +275,47 @@ mfma_fused_kernel(GemmArgs a) {
     grid_combine(a, n_run, n_all, &a.queue[kQueueDone], &a.queue[kQueueGo], &a.queue[kQueueError]);
 }
 
+// The same units as one launch of one workgroup per unit (see
+// wide_queue_kernel in mfma_wide.hip): each workgroup dequeues one unit --
+// gate_up (item, quad), then down (item, quad pair) -- runs it and exits; a
+// down unit first waits (bounded) for the I/32 gate_up units of its item,
+// dequeued earlier by running workgroups that never wait.  The combine is a
+// launch of its own; arithmetic and order are the split launch's.
+__global__ void __launch_bounds__(kMfmaThreads)
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu)))
+mfma_queue_kernel(GemmArgs a) {
+    __shared__ f32x4_t red[kRedGateUp];
+    __shared__ int s_unit;
+    const int n_items = uniform(a.meta[kMetaNumMfmaItems]);
+    const int gu_units = a.I / 32, dn_units = (a.H / 64 + 1) / 2;
+    const int n_gu = n_items * gu_units, n_all = n_gu + n_items * dn_units;
+    if (threadIdx.x == 0) s_unit = atomicAdd(&a.queue[kQueueNext], 1);
+    __syncthreads();
+    const int u = uniform(s_unit);
+    if (u >= n_all) return;
+    if (u < n_gu) {
+        const int item = u / gu_units;
+        const int4 it = a.items[item];
+        const int64_t e = uniform(it.x);
+        gate_up_item<1, W4, XB, true>(a, u % gu_units, a.wgu + e * gu_units * (a.H / 128) * 4096,
+                                      a.sgu + e * gu_units * (a.H / 128) * 256,
+                                      SortedRows{uniform(it.y), uniform(it.z)}, red);
+        if (threadIdx.x < kWave) {  // wave 0 stored the h rows
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): they are complete
+            if (threadIdx.x == 0) atomicAdd(&a.gu_done[(int64_t)item * kLineInts], 1);
+        }
+    } else {
+        const int v = u - n_gu, item = v / dn_units;
+        const int4 it = a.items[item];
+        if (threadIdx.x == 0) wait_count(&a.gu_done[(int64_t)item * kLineInts], gu_units, &a.queue[kQueueError]);
+        __syncthreads();
+        const int64_t e = uniform(it.x);
+        down_item<1, false, W4>(a, v % dn_units, a.wdn + e * (a.H / 64) * (a.I / 128) * 4096,
+                                a.sdn + e * (a.H / 64) * (a.I / 128) * 256,
+                                SortedRows{uniform(it.y), uniform(it.z)}, red);
+    }
+}
+
 constexpr int kSharedWideTok = 64;
 
 // ---- the self-routed layer in one launch.  The pages run a model as one
@@ -472,6 +513,11 @@ hipError_t launch_self_fused(const GemmArgs& a, int32_t* flags, hipStream_t stre
     hipError_t err = resident_grid(reinterpret_cast<const void*>(self_fused_kernel), kMfmaThreads, &grid);
     if (err != hipSuccess) return err;
     self_fused_kernel<<<(int)(units < grid ? units : grid), kMfmaThreads, 0, stream>>>(a, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_queue(const GemmArgs& a, int max_items, hipStream_t stream) {
+    mfma_queue_kernel<<<max_items * (a.I / 32 + (a.H / 64 + 1) / 2), kMfmaThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

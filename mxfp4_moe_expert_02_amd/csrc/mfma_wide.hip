@@ -392,6 +392,50 @@ __global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_fused_kernel(
     grid_combine(a, n_run, n_all, &a.queue[kQueueDone], &a.queue[kQueueGo], &a.queue[kQueueError]);
 }
 
+// The wide kernels as one launch of one workgroup per unit: each
+// workgroup dequeues its unit from a counter -- the gate_up units (item,
+// quad block) first, then the down units (item, quad block) -- runs it and
+// exits; the combine is a launch of its own.  A down unit first waits
+// (bounded, raising queue[kQueueError] if it gives up) until all I/128
+// gate_up units of its item are done; those were dequeued earlier, by
+// workgroups that are running and never wait, so no wait can deadlock
+// whatever the hardware's dispatch order.  The down units of finished items
+// thus run while the last gate_up units do: with the split launch the end
+// of gate_up's last round of workgroups, often a fraction of the CUs,
+// leaves the rest of the GPU idle.  Unit bodies, arithmetic and order are
+// the split launch's (h stores agent-coherent: other XCDs read them in
+// this launch), so the output bits are too.
+__global__ void __launch_bounds__(kWThreads, kWideWavesPerEu) wide_queue_kernel(GemmArgs a) {
+    __shared__ union {
+        WSmem x;
+        WQSmem q;
+    } sm;
+    __shared__ int s_unit;
+    const int n_items = uniform(a.meta[kMetaNumMfmaItems]);
+    const int gu_units = a.I / 128, dn_units = (a.H / 64 + kWQuads - 1) / kWQuads;
+    const int n_gu = n_items * gu_units, n_all = n_gu + n_items * dn_units;
+    if (threadIdx.x == 0) s_unit = atomicAdd(&a.queue[kQueueNext], 1);
+    __syncthreads();
+    const int u = uniform(s_unit);
+    if (u >= n_all) return;
+    if (u < n_gu) {
+        const int item = u / gu_units, qb = u % gu_units;
+        const int4 it = a.items[item];
+        const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+        by_tiles(m, [&](auto nt) { wide_gate_up<decltype(nt)::value, true>(a, qb, e, row0, m, sm.x); });
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's h stores completed
+        __syncthreads();
+        if (threadIdx.x == 0) atomicAdd(&a.gu_done[(int64_t)item * kLineInts], 1);
+    } else {
+        const int v = u - n_gu, item = v / dn_units, qb = v % dn_units;
+        const int4 it = a.items[item];
+        const int e = uniform(it.x), row0 = uniform(it.y), m = uniform(it.z);
+        if (threadIdx.x == 0) wait_count(&a.gu_done[(int64_t)item * kLineInts], gu_units, &a.queue[kQueueError]);
+        __syncthreads();
+        by_tiles(m, [&](auto nt) { wide_down<decltype(nt)::value, false>(a, qb, e, SortedRows{row0, m}, sm.q); });
+    }
+}
+
 }  // namespace
 
 hipError_t launch_wide_gate_up(const GemmArgs& a, int max_items, hipStream_t stream) {
@@ -404,6 +448,12 @@ hipError_t launch_wide_down(const GemmArgs& a, int max_items, hipStream_t stream
     const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
     const int sh = a.sh_wdn ? shared_blocks((a.H / 64 + 1) / 2, (a.T + 15) / 16) : 0;
     wide_down_kernel<<<sh + max_items * qblocks, kWThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_queue(const GemmArgs& a, int max_items, hipStream_t stream) {
+    const int qblocks = (a.H / 64 + kWQuads - 1) / kWQuads;
+    wide_queue_kernel<<<max_items * (a.I / 128 + qblocks), kWThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -303,8 +303,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
         return MOE_E_OPTION;
     if (o.num_events < 0 || o.num_events > 4 || (o.num_events > 0 && !o.events))
         return MOE_E_OPTION;
-    if (o.launch != MOE_LAUNCH_AUTO && o.launch != MOE_LAUNCH_SPLIT &&
-        o.launch != MOE_LAUNCH_FUSED && o.launch != MOE_LAUNCH_SELF_ROUTED)
+    if (o.launch != MOE_LAUNCH_AUTO && o.launch != MOE_LAUNCH_SPLIT && o.launch != MOE_LAUNCH_FUSED &&
+        o.launch != MOE_LAUNCH_SELF_ROUTED && o.launch != MOE_LAUNCH_QUEUE)
         return MOE_E_OPTION;
     if (num_tokens == 0) return MOE_OK;
     if (o.router_weight) router_logits = nullptr;  // ignored: the layer computes the logits
@@ -363,6 +363,14 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     const bool self_fused = self_ok && o.launch == MOE_LAUNCH_FUSED;
     const bool self = self_ok && (o.launch == MOE_LAUNCH_SELF_ROUTED || o.launch == MOE_LAUNCH_AUTO ||
                                   self_fused);
+    // The routed bf16 matrix-core GEMMs as one launch of one workgroup per
+    // unit; AUTO takes it for wide layers without a shared expert (whose
+    // blocks the split kernels run beside the routed ones).  On such layers
+    // a split gate_up workgroup streams a whole 256-row block over K, and
+    // the last, partly filled round of them leaves most of the GPU idle,
+    // which down units of finished items fill here.
+    const bool queue = !mx8 && !self && path == MOE_PATH_MFMA &&
+                       (o.launch == MOE_LAUNCH_QUEUE || (o.launch == MOE_LAUNCH_AUTO && wide && !shared));
 
     if ((err = mark(0)) != hipSuccess) return hip_fail(err, "hipEventRecord");
     if (o.router_weight) {  // the router linear layer, ahead of the routing
@@ -440,7 +448,8 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
     // stages of the routed ones.  The matrix-core GEMM kernels of the split
     // launch run its workgroups themselves, ahead of the routed ones; the
     // VALU path and the single-launch layer launch them on their own.
-    const bool shared_inside = path == MOE_PATH_MFMA && (mx8 || o.launch != MOE_LAUNCH_FUSED || self_fused);
+    const bool shared_inside =
+        path == MOE_PATH_MFMA && (mx8 || (o.launch != MOE_LAUNCH_FUSED && !queue) || self_fused);
     auto shared_gate_up = [&]() -> hipError_t {
         return shared && !shared_inside ? moe::launch_shared_gate_up(a, st) : hipSuccess;
     };
@@ -491,6 +500,14 @@ int moe_mxfp4_forward_ex(const void* x, const float* router_logits, int64_t num_
                        : moe::launch_mfma_fused(a, max_items, st);
             if (err != hipSuccess) return hip_fail(err, "fused expert layer");
             if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        } else if (queue) {
+            // one kernel for both GEMMs: event [2] marks its end
+            err = wide ? moe::launch_wide_queue(a, max_items, st) : moe::launch_mfma_queue(a, max_items, st);
+            if (err != hipSuccess) return hip_fail(err, "expert GEMMs");
+            if ((err = mark(2)) != hipSuccess) return hip_fail(err, "hipEventRecord");
+            if ((err = shared_down()) != hipSuccess) return hip_fail(err, "shared down");
+            err = moe::launch_combine(a, st);
+            if (err != hipSuccess) return hip_fail(err, "combine");
         } else {
             err = wide ? moe::launch_wide_gate_up(a, max_items, st)
                        : moe::launch_mfma_gate_up(a, max_items, st);

@@ -266,6 +266,12 @@ hipError_t launch_mfma_fused(const GemmArgs& a, int max_items, hipStream_t strea
 // workspace.
 hipError_t launch_self_fused(const GemmArgs& a, int32_t* flags, hipStream_t stream);
 hipError_t launch_wide_fused(const GemmArgs& a, int max_items, hipStream_t stream);
+// The two GEMMs as one launch of one workgroup per unit (gate_up units,
+// then down units that wait, bounded, for their item's gate_up units),
+// each dequeued from queue[kQueueNext]; launch_combine forms out after it.
+// Needs the queue words and gu_done zeroed (the route does it).
+hipError_t launch_mfma_queue(const GemmArgs& a, int max_items, hipStream_t stream);
+hipError_t launch_wide_queue(const GemmArgs& a, int max_items, hipStream_t stream);
 // MXFP8 (prefill) path: encode x per token along H, then the scaled
 // FP4 x FP8 matrix-core GEMMs (gate_up encodes h to MXFP8 in its epilogue;
 // down writes y, launch_combine forms out).

@@ -57,7 +57,7 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, 
     the requested debug outputs (routing; with MXFP8 also the codes of x)
     as numpy arrays.  out is NaN-filled first, so every element it holds
     afterwards was written by this call.  launch: MOE_LAUNCH_* (the fused
-    launch also returns its wait-error flag as "wait_error"); init=False
+    and queue launches also return their wait-error flag as "wait_error"); init=False
     keeps the current workspace (and whatever an earlier call left in it).
     router: a [E, H] bf16 device router weight -- the layer then computes its
     own logits (returned as "logits") and is given no router_logits.
@@ -81,7 +81,7 @@ def run(M, layer, path=0, debug=False, act=0, launch=0, init=True, router=None, 
             dbg["x_scales"] = torch.empty((c.T, c.H // 32), dtype=torch.uint8, device="cuda")
             dbg["h_codes"] = torch.empty((S, c.I), dtype=torch.uint8, device="cuda")
             dbg["h_scales"] = torch.empty((S, c.I // 32), dtype=torch.uint8, device="cuda")
-    if launch == M.MOE_LAUNCH_FUSED:
+    if launch in (M.MOE_LAUNCH_FUSED, M.MOE_LAUNCH_QUEUE):
         dbg["wait_error"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     extra = {}
     if router is not None:

@@ -112,9 +112,9 @@ def test_forward_validation_without_gpu(L):
     bad_layout.weight_layout = 5
     assert _fwd(L, opt=bad_layout) == L.MOE_E_OPTION
     bad_launch = L.moe_mxfp4_options(0, 0)
-    bad_launch.launch = 4
+    bad_launch.launch = 5
     assert _fwd(L, opt=bad_launch) == L.MOE_E_OPTION
-    for launch in (L.MOE_LAUNCH_FUSED, L.MOE_LAUNCH_SELF_ROUTED):
+    for launch in (L.MOE_LAUNCH_FUSED, L.MOE_LAUNCH_SELF_ROUTED, L.MOE_LAUNCH_QUEUE):
         req = L.moe_mxfp4_options(0, L.MOE_PATH_MFMA)
         req.weight_layout = L.MOE_LAYOUT_TILES
         req.launch = launch

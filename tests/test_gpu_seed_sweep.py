@@ -47,6 +47,7 @@ PATHS = {  # name: (gemm path, activation format, launch)
     "auto": (2, 0, 0),
     "split": (2, 0, 1),
     "fused": (2, 0, 2),
+    "queue": (2, 0, 4),
     "mx8": (0, 1, 0),
 }
 
@@ -77,7 +78,7 @@ def test_seed_sweep_vs_oracle(M, oracle_lib, seed, path):
     cfg = _cfg(seed, act)
     layer = get_layer(cfg)
     dbg = run(M, layer, path=gemm, act=act, launch=launch, debug=True)
-    if launch == M.MOE_LAUNCH_FUSED:
+    if launch in (M.MOE_LAUNCH_FUSED, M.MOE_LAUNCH_QUEUE):
         assert int(dbg["wait_error"][0]) == 0
     lg = make_logits(cfg)
     r = oracle_lib.route(lg, cfg.k)
@@ -119,7 +120,7 @@ def test_seed_sweep_vs_oracle(M, oracle_lib, seed, path):
 SHARED_MXFP8_PLAIN_OVER = {(207, "mx8")}
 
 
-@pytest.mark.parametrize("path", ["gemv", "auto", "split", "fused", "mx8"])
+@pytest.mark.parametrize("path", ["gemv", "auto", "split", "fused", "queue", "mx8"])
 @pytest.mark.parametrize("seed", list(SHAPES))
 def test_seed_sweep_with_shared_expert(M, oracle_lib, seed, path):
     """The same sweep with an MXFP8 shared expert beside the routed ones, on
@@ -132,7 +133,7 @@ def test_seed_sweep_with_shared_expert(M, oracle_lib, seed, path):
     layer = get_layer(cfg)
     sh = get_shared(cfg)
     dbg = run(M, layer, path=gemm, act=act, launch=launch, shared=sh.tiles)
-    if launch == M.MOE_LAUNCH_FUSED:
+    if launch in (M.MOE_LAUNCH_FUSED, M.MOE_LAUNCH_QUEUE):
         assert int(dbg["wait_error"][0]) == 0
     full = bf16_tensor_to_f64(layer.out)
     assert np.isfinite(full).all()
