@@ -222,8 +222,8 @@ def cpu_baseline(cfg, gbytes_total: float, shared: bool = False) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the layer's multi-GPU expert-parallel design is described but not built.",
+        print(f"bench.py: the layer runs on one GPU only (asked for --gpus {args.gpus}); "
+              "its multi-GPU expert-parallel form is a design, not code.",
               file=sys.stderr)
         sys.exit(2)
     import torch
